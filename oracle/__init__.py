@@ -1,0 +1,16 @@
+"""fp64 CPU oracle for the FlashAttention-2 forward pass.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
+benchmark's CPU-baseline leg, never by the library.  It shares no code with
+the HIP path and never imports it.
+"""
+from .attention import attention_fp64, attention_rows_fp64, scaled_logits_fp64
+from .tiled import causal_block_end, fa2_forward_tiled_fp64
+
+__all__ = [
+    "attention_fp64",
+    "attention_rows_fp64",
+    "scaled_logits_fp64",
+    "fa2_forward_tiled_fp64",
+    "causal_block_end",
+]
