@@ -1,0 +1,72 @@
+"""Build libfa2.so (the gfx950 kernels plus the C-ABI host code) in-tree with hipcc.
+
+    python -m exact_attention_62_amd.build          # writes exact_attention_62_amd/libfa2.so
+
+hipcc cross-compiles for gfx950 without a GPU present.  Packed fp32 VALU
+instructions are disabled for device code (``-packed-fp32-ops``); the host
+pass warns that it does not know that feature, which is harmless.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libfa2.so")
+
+SOURCES = ["fa2_api.cpp", "fa2_fwd_bf16.hip", "fa2_fwd_f32.hip"]
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    path = os.path.join(rocm, "bin", "hipcc")
+    if not os.path.exists(path):
+        path = shutil.which("hipcc") or path
+    return path
+
+
+def common_flags(extra=()):
+    return ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}", *extra]
+
+
+def build(verbose: bool = False, extra_flags=()) -> str:
+    """Compile every source and link libfa2.so; returns its path.  Raises on failure."""
+    cc = hipcc()
+    with tempfile.TemporaryDirectory(prefix="fa2_build_") as tmp:
+        objs = []
+        for src in SOURCES:
+            obj = os.path.join(tmp, os.path.splitext(src)[0] + ".o")
+            lang = ["-x", "hip"] if src.endswith(".hip") else []
+            cmd = [cc, *common_flags(extra_flags), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+            _run(cmd, verbose)
+            objs.append(obj)
+        tmp_lib = os.path.join(tmp, "libfa2.so")
+        _run([cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp_lib], verbose)
+        shutil.copyfile(tmp_lib, LIB + ".tmp")
+        os.replace(LIB + ".tmp", LIB)
+    return LIB
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    out = "\n".join(line for line in r.stdout.splitlines()
+                    if "packed-fp32-ops" not in line)  # the host pass's harmless warning
+    if r.returncode != 0:
+        raise RuntimeError(f"command failed ({r.returncode}): {' '.join(cmd)}\n{out}")
+    if verbose and out.strip():
+        print(out, flush=True)
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv[1:]))

@@ -1,0 +1,141 @@
+"""Python binding of libfa2.so: argument marshalling only.
+
+Every step of the forward pass runs in the library's HIP kernels; this module
+checks tensor properties, passes raw device pointers, sizes and the current
+HIP stream through ctypes, and turns status codes into exceptions.  PyTorch
+supplies device memory and streams and nothing else.  There is no fallback:
+if the library has not been built, or the tensors are not on a GPU, the call
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+
+import torch
+
+__all__ = ["FA2Error", "fa2_fwd", "fa2_launch_shape", "fa2_strerror", "fa2_last_error",
+           "attention", "library_path", "load_library"]
+
+FA2_OK, FA2_EINVAL, FA2_ENOTSUP, FA2_EHIP = 0, -1, -2, -3
+FA2_BF16, FA2_FP32 = 0, 1
+_DTYPES = {torch.bfloat16: FA2_BF16, torch.float32: FA2_FP32}
+
+_lib = None
+_lock = threading.Lock()
+
+
+class FA2Error(RuntimeError):
+    """A non-zero status from libfa2.so; ``status`` holds the code."""
+
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        super().__init__(f"{fa2_strerror(status)} ({status}): {detail}")
+
+
+def library_path() -> str:
+    return os.environ.get("FA2_LIBRARY",
+                          os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa2.so"))
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libfa2.so once; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        path = library_path()
+        if not os.path.exists(path):
+            raise RuntimeError(
+                f"{path} is missing: build it first (python -m exact_attention_62_amd.build)")
+        lib = ctypes.CDLL(path)
+        i64, vp = ctypes.c_int64, ctypes.c_void_p
+        lib.fa2_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int,
+                                ctypes.c_float, ctypes.c_int, vp]
+        lib.fa2_fwd.restype = ctypes.c_int
+        lib.fa2_launch_shape.argtypes = [i64, i64, i64, i64, ctypes.c_int,
+                                         ctypes.POINTER(i64), ctypes.POINTER(i64),
+                                         ctypes.POINTER(i64)]
+        lib.fa2_launch_shape.restype = ctypes.c_int
+        lib.fa2_strerror.argtypes = [ctypes.c_int]
+        lib.fa2_strerror.restype = ctypes.c_char_p
+        lib.fa2_last_error.argtypes = []
+        lib.fa2_last_error.restype = ctypes.c_char_p
+        _lib = lib
+    return _lib
+
+
+def fa2_strerror(status: int) -> str:
+    return load_library().fa2_strerror(int(status)).decode()
+
+
+def fa2_last_error() -> str:
+    return load_library().fa2_last_error().decode()
+
+
+def _check(status: int) -> None:
+    if status != FA2_OK:
+        raise FA2Error(status, fa2_last_error())
+
+
+def fa2_launch_shape(B: int, H: int, N: int, d: int, dtype: torch.dtype = torch.bfloat16):
+    """(kBlockM, num_m_block, blocks) of the grid fa2_fwd launches for this problem."""
+    lib = load_library()
+    out = [ctypes.c_int64(0) for _ in range(3)]
+    _check(lib.fa2_launch_shape(B, H, N, d, _DTYPES.get(dtype, -1), *(ctypes.byref(o) for o in out)))
+    return tuple(o.value for o in out)
+
+
+def fa2_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+            lse: torch.Tensor, causal: bool = False, scale: float | None = None,
+            stream: torch.cuda.Stream | None = None) -> None:
+    """Enqueue the forward pass on ``stream`` (default: the current stream).
+
+    q, k, v, o: contiguous [B, H, N, d] tensors of one dtype (bfloat16 or
+    float32) on the current GPU; lse: contiguous float32 [B, H, N].  Writes
+    o and lse in place.
+    """
+    if q.dim() != 4:
+        raise ValueError(f"q must be [B, H, N, d], got shape {tuple(q.shape)}")
+    B, H, N, d = q.shape
+    for name, t in (("k", k), ("v", v), ("o", o)):
+        if t.shape != q.shape:
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(q.shape)}")
+        if t.dtype != q.dtype:
+            raise ValueError(f"{name} has dtype {t.dtype}, expected {q.dtype}")
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32:
+        raise ValueError(f"lse must be float32 [{B}, {H}, {N}], got {lse.dtype} {tuple(lse.shape)}")
+    if q.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    tensors = (q, k, v, o, lse)
+    for t in tensors:
+        if not t.is_cuda:
+            raise ValueError("every tensor must be on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("every tensor must be contiguous")
+    dev = q.device
+    if any(t.device != dev for t in tensors):
+        raise ValueError("every tensor must be on the same device")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    lib = load_library()
+    with torch.cuda.device(dev):
+        st = lib.fa2_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                         B, H, N, d, 1 if causal else 0, float(scale), _DTYPES[q.dtype],
+                         ctypes.c_void_p(stream.cuda_stream))
+    _check(st)
+
+
+def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+              scale: float | None = None):
+    """Allocate O and L and run the forward pass.  Returns (o, lse)."""
+    o = torch.empty_like(q, memory_format=torch.contiguous_format)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    fa2_fwd(q, k, v, o, lse, causal=causal, scale=scale)
+    return o, lse

@@ -1,0 +1,150 @@
+"""The C ABI of libfa2.so on the CPU: exports, work decomposition and every error path.
+
+Nothing here launches a kernel.  Invalid arguments are rejected before any HIP
+call; the HIP-error path is exercised only where no GPU is visible.
+"""
+from __future__ import annotations
+
+import ctypes
+import json
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+from exact_attention_62_amd import fa2 as F
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa2.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(F.library_path()),
+                                reason="libfa2.so not built (python -m exact_attention_62_amd.build)")
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: every call below fails before a launch
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa2_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    assert _declared_functions() == ["fa2_fwd", "fa2_last_error", "fa2_launch_shape", "fa2_strerror"]
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", F.library_path()], check=True,
+                         capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (fa2_\w+)", out))
+    for name in _declared_functions():
+        assert name in exported, name
+        assert hasattr(F.load_library(), name)
+
+
+def _fwd(q=FAKE, k=FAKE + 0x100000, v=FAKE + 0x200000, o=FAKE + 0x300000, L=FAKE + 0x400000,
+         B=1, H=1, N=16, d=64, causal=0, scale=0.125, dtype=F.FA2_BF16):
+    lib = F.load_library()
+    return lib.fa2_fwd(q, k, v, o, L, B, H, N, d, causal, scale, dtype, None)
+
+
+@pytest.mark.parametrize("kw,needle", [
+    (dict(q=None), "Q is NULL"),
+    (dict(L=None), "L is NULL"),
+    (dict(v=FAKE + 8), "V="),
+    (dict(L=FAKE + 0x400002), "4-byte aligned"),
+    (dict(B=-1), "sizes must be >= 0"),
+    (dict(N=-5), "sizes must be >= 0"),
+    (dict(causal=2), "causal=2"),
+    (dict(scale=float("nan")), "finite"),
+    (dict(scale=float("inf")), "finite"),
+    (dict(o=FAKE), "overlaps"),
+    (dict(L=FAKE + 0x300000 + 64), "overlaps"),
+    (dict(N=(1 << 31) // 256 + 1), "maximum"),
+    (dict(B=1 << 20, H=1 << 12), "exceeds"),
+])
+def test_invalid_arguments_are_rejected_before_any_hip_call(kw, needle):
+    assert _fwd(**kw) == F.FA2_EINVAL
+    assert needle in F.fa2_last_error()
+
+
+@pytest.mark.parametrize("kw", [dict(d=96), dict(d=32), dict(d=512), dict(dtype=7)])
+def test_unsupported_requests(kw):
+    assert _fwd(**kw) == F.FA2_ENOTSUP
+    assert F.fa2_last_error()
+
+
+def test_empty_problem_is_a_no_op():
+    for kw in (dict(B=0), dict(H=0), dict(N=0)):
+        assert _fwd(q=None, k=None, v=None, o=None, L=None, **kw) == F.FA2_OK
+        assert F.fa2_last_error() == ""
+
+
+def test_strerror_covers_every_status():
+    assert F.fa2_strerror(0) == "success"
+    for s in (F.FA2_EINVAL, F.FA2_ENOTSUP, F.FA2_EHIP):
+        assert F.fa2_strerror(s) not in ("", "unknown status")
+    assert F.fa2_strerror(42) == "unknown status"
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="needs a host without a visible GPU")
+def test_valid_call_without_a_device_reports_the_hip_error():
+    assert _fwd() == F.FA2_EHIP
+    assert "hip" in F.fa2_last_error().lower()
+
+
+def test_grid_matches_the_pages_worked_example():
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "grid_example.json")))
+    kBlockM, _, _ = F.fa2_launch_shape(1, 1, 1, 128)
+    N = g["num_m_block"] * kBlockM
+    km, nmb, blocks = F.fa2_launch_shape(g["batch_size"], g["num_heads"], N, 128)
+    assert (km, nmb, blocks) == (kBlockM, g["num_m_block"], g["blocks"])
+    # A ragged length rounds the row blocks up.
+    assert F.fa2_launch_shape(1, 2, N - 1, 128)[1:] == (4, 8)
+    assert F.fa2_launch_shape(1, 2, N + 1, 128)[1:] == (5, 10)
+
+
+def test_grid_of_the_named_workloads():
+    # (query blocks, batch, head) for the five workloads at kBlockM = 128 (bf16).
+    assert F.fa2_launch_shape(2, 4, 1024, 64) == (128, 8, 64)
+    assert F.fa2_launch_shape(16, 16, 2048, 128) == (128, 16, 4096)
+    assert F.fa2_launch_shape(1, 16, 16384, 128) == (128, 128, 2048)
+    assert F.fa2_launch_shape(2, 16, 8191, 256) == (128, 64, 2048)
+    assert F.fa2_launch_shape(1, 1, 128, 64, torch.float32) == (4, 32, 32)
+
+
+def test_launch_shape_rejects_what_fwd_rejects():
+    with pytest.raises(F.FA2Error) as e:
+        F.fa2_launch_shape(1, 1, 16, 100)
+    assert e.value.status == F.FA2_ENOTSUP
+    with pytest.raises(F.FA2Error) as e:
+        F.fa2_launch_shape(-1, 1, 16, 64)
+    assert e.value.status == F.FA2_EINVAL
+
+
+def test_binding_rejects_cpu_tensors():
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        F.fa2_fwd(q, q.clone(), q.clone(), q.clone(), torch.zeros(1, 1, 8))
+    with pytest.raises(ValueError, match="shape"):
+        F.fa2_fwd(q, q[:, :, :4].clone(), q.clone(), q.clone(), torch.zeros(1, 1, 8))
+    with pytest.raises(ValueError, match="lse"):
+        F.fa2_fwd(q, q.clone(), q.clone(), q.clone(), torch.zeros(1, 1, 8, dtype=torch.float64))
+
+
+def test_last_error_is_thread_local():
+    import threading
+    assert _fwd(causal=5) == F.FA2_EINVAL
+    seen = {}
+
+    def other():
+        seen["msg"] = F.fa2_last_error()
+        _fwd(d=96)
+
+    t = threading.Thread(target=other)
+    t.start()
+    t.join()
+    assert seen["msg"] == ""
+    assert "causal=5" in F.fa2_last_error()

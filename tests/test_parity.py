@@ -1,0 +1,245 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle.
+
+Tolerances: bf16 O max-abs 2e-2 and L max-abs 1e-3; float32 exact mode 1e-5 on
+both.  Small problems are compared element by element against the whole
+oracle; the full-size workloads, run in the launch configuration the
+benchmark times, are compared on sampled rows that the oracle computes one by
+one (first and last rows, rows around every 128-row block edge, the ragged
+tail, and random rows), across several heads.
+"""
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from exact_attention_62_amd import attention, fa2_fwd
+from exact_attention_62_amd.inputs import WORKLOADS, make, make_random
+from oracle import attention_fp64, attention_rows_fp64
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": (2e-2, 1e-3), "fp32": (1e-5, 1e-5)}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+
+
+def _say(msg):
+    print(f"\n[parity] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def _run(q, k, v, causal, scale=None):
+    qd, kd, vd = (t.cuda() for t in (q, k, v))
+    o, lse = attention(qd, kd, vd, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def _cmp(o, lse, O_ref, L_ref, dtype, what):
+    otol, ltol = TOL[dtype]
+    o64 = o.double().cpu().numpy()
+    l64 = lse.double().cpu().numpy()
+    assert np.all(np.isfinite(o64)) and np.all(np.isfinite(l64)), f"{what}: non-finite output"
+    eo = np.abs(o64 - O_ref).max() if O_ref.size else 0.0
+    el = np.abs(l64 - L_ref).max() if L_ref.size else 0.0
+    assert eo <= otol, f"{what}: max |O - O_ref| = {eo:.3e} > {otol}"
+    assert el <= ltol, f"{what}: max |L - L_ref| = {el:.3e} > {ltol}"
+    return eo, el
+
+
+# ----------------------------------------------------------------- small, whole oracle
+
+SMALL = [
+    # (B, H, N, d): single rows, one partial block, exact blocks, ragged tails,
+    # several blocks, and more (query block, head) pairs than a multiple of 8
+    (1, 1, 1, 64), (1, 1, 7, 128), (1, 2, 64, 64), (2, 1, 127, 128), (1, 1, 128, 256),
+    (1, 3, 129, 64), (1, 1, 200, 256), (2, 3, 300, 128), (1, 1, 513, 64), (3, 1, 257, 256),
+    (1, 5, 640, 128),
+]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: "x".join(map(str, s)))
+def test_small_bf16(shape, causal):
+    B, H, N, d = shape
+    _say(f"bf16 B={B} H={H} N={N} d={d} causal={causal}")
+    q, k, v = make_random(B, H, N, d, seed=N * 7 + d + causal)
+    O, L = attention_fp64(q, k, v, causal=causal)
+    o, lse = _run(q, k, v, causal)
+    _cmp(o, lse, O, L, "bf16", f"{shape} causal={causal}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", [(1, 1, 128, 64), (1, 2, 77, 128), (2, 1, 130, 256),
+                                   (1, 1, 1, 64)], ids=lambda s: "x".join(map(str, s)))
+def test_small_fp32(shape, causal):
+    B, H, N, d = shape
+    _say(f"fp32 B={B} H={H} N={N} d={d} causal={causal}")
+    q, k, v = make_random(B, H, N, d, seed=N + d + causal, dtype="fp32")
+    O, L = attention_fp64(q, k, v, causal=causal)
+    o, lse = _run(q, k, v, causal)
+    _cmp(o, lse, O, L, "fp32", f"fp32 {shape} causal={causal}")
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_tiny_fp32_workload(seed):
+    w = WORKLOADS["tiny"]
+    _say(f"workload tiny seed={seed}")
+    q, k, v = make(w, seed)
+    O, L = attention_fp64(q, k, v, causal=False, scale=w.scale)
+    o, lse = _run(q, k, v, False, w.scale)
+    _cmp(o, lse, O, L, "fp32", f"tiny seed={seed}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_small_workload(seed, causal):
+    w = WORKLOADS["small"]
+    _say(f"workload small seed={seed} causal={causal}")
+    q, k, v = make(w, seed)
+    O, L = attention_fp64(q, k, v, causal=causal, scale=w.scale)
+    o, lse = _run(q, k, v, causal, w.scale)
+    _cmp(o, lse, O, L, "bf16", f"small seed={seed} causal={causal}")
+
+
+# ------------------------------------------------- full-size workloads, sampled rows
+
+def _sample_rows(N, rng, n_random=48):
+    edges = [r for b in range(128, N, 128) for r in (b - 1, b)]
+    rows = set(range(min(N, 8))) | set(range(max(0, N - 8), N)) | set(edges[::3])
+    rows |= set(rng.integers(0, N, n_random).tolist())
+    return sorted(rows)
+
+
+@pytest.mark.parametrize("name,causal,seed", [
+    ("train", True, 0), ("train", True, 1), ("train", True, 2),
+    ("long", True, 0), ("long", False, 0), ("long", True, 1),
+    ("ragged", True, 0), ("ragged", True, 1), ("ragged", True, 2),
+])
+def test_full_size_workload_sampled(name, causal, seed):
+    w = WORKLOADS[name]
+    _say(f"workload {name} B={w.B} H={w.H} N={w.N} d={w.d} causal={causal} seed={seed}")
+    q, k, v = make(w, seed)
+    o, lse = _run(q, k, v, causal, w.scale)
+    o, lse = o.cpu(), lse.cpu()
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+    rng = np.random.default_rng(seed + 17)
+    heads = {(0, 0), (w.B - 1, w.H - 1)} | {(int(rng.integers(w.B)), int(rng.integers(w.H)))
+                                             for _ in range(2)}
+    worst_o = worst_l = 0.0
+    for b, h in sorted(heads):
+        rows = _sample_rows(w.N, rng)
+        O, L = attention_rows_fp64(q, k, v, b, h, rows, causal=causal, scale=w.scale)
+        eo, el = _cmp(o[b, h, rows], lse[b, h, rows], O, L, "bf16", f"{name} head ({b},{h})")
+        worst_o, worst_l = max(worst_o, eo), max(worst_l, el)
+    _say(f"{name}: max |dO| = {worst_o:.3e}, max |dL| = {worst_l:.3e}")
+
+
+def test_ragged_sigma2_reading():
+    # "N(0,4)" read as variance 4 (sigma 2): logits reach ~25 instead of ~100.
+    w = WORKLOADS["ragged"]
+    _say("workload ragged, sigma=2")
+    q, k, v = make(w, 0, qk_sigma=2.0, B=1, H=4)
+    o, lse = _run(q, k, v, True, w.scale)
+    rng = np.random.default_rng(5)
+    for h in range(4):
+        rows = _sample_rows(w.N, rng, 32)
+        O, L = attention_rows_fp64(q, k, v, 0, h, rows, causal=True, scale=w.scale)
+        _cmp(o[0, h, rows].cpu(), lse[0, h, rows].cpu(), O, L, "bf16", f"sigma2 head {h}")
+
+
+# ------------------------------------------------------------ closed forms on the GPU
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_closed_forms_on_gpu(d):
+    _say(f"closed forms d={d}")
+    B, H, N = 1, 2, 300
+    q, k, v = make_random(B, H, N, d, seed=d)
+    scale = 1.0 / math.sqrt(d)
+    # Causal row 0 sees only key 0: O_0 = V_0 exactly, L_0 = scale * q_0 . k_0.
+    o, lse = _run(q, k, v, True)
+    assert torch.equal(o[:, :, 0].cpu(), v[:, :, 0])
+    l0 = scale * (q[:, :, 0].double() * k[:, :, 0].double()).sum(-1)
+    assert (lse[:, :, 0].cpu().double() - l0).abs().max() < 1e-4
+    # Identical keys: O_i is the mean of the visible V rows, L_i = s_i + ln(n_i).
+    kk = k[:, :, :1].expand(B, H, N, d).contiguous()
+    for causal in (False, True):
+        o, lse = _run(q, kk, v, causal)
+        n = torch.arange(1, N + 1, dtype=torch.float64) if causal else torch.full((N,), float(N))
+        mean = (v.double().cumsum(2) / n[:, None]) if causal else v.double().mean(2, keepdim=True)
+        assert (o.cpu().double() - mean).abs().max() < 2e-2
+        s = scale * (q.double() * kk.double()).sum(-1)
+        assert (lse.cpu().double() - (s + n.log())).abs().max() < 1e-3
+    # Constant V: O = c (P~ is rounded to bf16 for the MFMA while l sums it in
+    # fp32, so O is c up to that rounding, well inside the bf16 tolerance).
+    vc = torch.full_like(v, -1.5)
+    o, _ = _run(q, k, vc, True)
+    assert (o.cpu().double() + 1.5).abs().max() < 2e-2
+    # Zero scale: uniform weights, L = ln(n).
+    o, lse = _run(q, k, v, True, 0.0)
+    n = torch.arange(1, N + 1, dtype=torch.float64)
+    assert (lse.cpu().double() - n.log()).abs().max() < 1e-5
+    assert (o.cpu().double() - v.double().cumsum(2) / n[:, None]).abs().max() < 2e-2
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_negative_scale(dtype):
+    _say(f"negative scale {dtype}")
+    q, k, v = make_random(1, 2, 200, 128, seed=3, dtype=dtype)
+    for causal in (False, True):
+        O, L = attention_fp64(q, k, v, causal=causal, scale=-0.09)
+        o, lse = _run(q, k, v, causal, -0.09)
+        _cmp(o, lse, O, L, dtype, f"scale<0 causal={causal}")
+
+
+# ------------------------------------------------------ determinism and completeness
+
+def test_poisoned_outputs_are_fully_overwritten_and_runs_repeat_bitwise():
+    _say("poison + determinism")
+    for N, d, causal in [(1000, 128, True), (8191 // 8, 256, True), (333, 64, False)]:
+        q, k, v = (t.cuda() for t in make_random(2, 3, N, d, seed=N))
+        o1 = torch.full_like(q, float("nan"))
+        l1 = torch.full(q.shape[:3], float("nan"), device="cuda")
+        fa2_fwd(q, k, v, o1, l1, causal=causal)
+        o2 = torch.full_like(q, float("inf"))
+        l2 = torch.full(q.shape[:3], float("inf"), device="cuda")
+        fa2_fwd(q, k, v, o2, l2, causal=causal)
+        torch.cuda.synchronize()
+        assert torch.isfinite(o1.float()).all() and torch.isfinite(l1).all()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_slice_alone_equals_slice_in_batch():
+    _say("slice independence")
+    q, k, v = (t.cuda() for t in make_random(3, 4, 700, 128, seed=11))
+    o, lse = attention(q, k, v, causal=True)
+    b, h = 2, 1
+    o1, l1 = attention(q[b:b + 1, h:h + 1].contiguous(), k[b:b + 1, h:h + 1].contiguous(),
+                       v[b:b + 1, h:h + 1].contiguous(), causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1[0, 0], o[b, h]) and torch.equal(l1[0, 0], lse[b, h])
+
+
+def test_empty_problem_and_explicit_stream():
+    _say("empty + stream")
+    q = torch.empty(2, 3, 0, 64, dtype=torch.bfloat16, device="cuda")
+    o, lse = attention(q, q, q, causal=True)
+    assert o.shape == q.shape and lse.shape == (2, 3, 0)
+    s = torch.cuda.Stream()
+    qq, kk, vv = (t.cuda() for t in make_random(1, 1, 256, 64, seed=1))
+    o = torch.empty_like(qq)
+    lse = torch.empty(1, 1, 256, device="cuda")
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fa2_fwd(qq, kk, vv, o, lse, causal=True)
+    s.synchronize()
+    O, L = attention_fp64(qq.cpu(), kk.cpu(), vv.cpu(), causal=True)
+    _cmp(o, lse, O, L, "bf16", "side stream")
