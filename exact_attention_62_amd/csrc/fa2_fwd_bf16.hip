@@ -19,18 +19,39 @@
 // MFMA orientation.  v_mfma_f32_32x32x16_bf16 produces a 32x32 fp32 tile
 // where lane l holds column (l % 32) and rows 8*(r/4) + 4*(l/32) + (r%4),
 // r = 0..15.  The kernel computes S^T = K Q^T, so that a lane holds 16 keys of
-// ONE query row: the row max and row sum are in-lane, plus one
-// v_permlane32_swap to combine the two lane halves.  The output is likewise
-// accumulated transposed, O^T += V^T P^T, so each lane's accumulators all
-// belong to its one query row (the rescale by alpha and the final 1/l are
-// per-lane scalars).  The P^T operand comes straight from the S^T registers:
-// the contraction index may be permuted freely as long as both operands use
-// the same order, so V^T is stored in LDS with its keys permuted (bits 2 and
-// 3 of the key index swapped within each group of 16) to match the order in
-// which S^T's accumulator rows sit in a lane.
+// ONE query row: the row max and row sum are in-lane, plus one exchange with
+// the lane 32 positions away.  The output is accumulated transposed too,
+// O^T += V^T P^T, so each lane's accumulators all belong to its one query row
+// (the rescale and the final 1/l are per-lane scalars).  The P^T operand comes
+// straight from the S^T registers: the contraction index may be permuted
+// freely as long as both operands use the same order, and the V^T operand is
+// read in exactly the order in which S^T's accumulator rows sit in a lane.
+//
+// Memory pipeline.  K and V blocks go from HBM straight into LDS
+// (global_load_lds_dwordx4, no register staging), double-buffered: while
+// block j is consumed, blocks j+1 (V) and j+2 (K) are in flight, with one
+// workgroup barrier per block.  Each direct load writes 1 KB of LDS (whole key
+// rows); those 1 KB pieces sit 1040 bytes apart, and which rows share a piece
+// is chosen so that both the K fragment reads (16 rows x 16 bytes per pass)
+// and the transposing V reads (ds_read_b64_tr_b16: 4 rows x 64 bytes per
+// pass) touch every LDS bank once, while every fragment address stays one
+// per-lane base plus a compile-time offset.
+//
+// Overlap.  The MFMAs of block j+1's S = K Q^T are issued in the same basic
+// block as block j's softmax (vector ALU: exp2, row max/sum, bf16 packing), so
+// the matrix cores and the vector ALUs work concurrently; the PV MFMAs of
+// block j follow.
+//
+// Rescaling.  The running reference max m only moves when a block's row max
+// exceeds it by more than kTau (in log2 units); otherwise O and l keep their
+// scale and P~ = exp2(c s - c m) stays <= 2^kTau.  O / l and L = m + ln(l) are
+// unchanged by the choice of reference, so this is the same online softmax
+// with fewer rescales of O.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "fa2_internal.h"
 
@@ -38,55 +59,85 @@ namespace fa2 {
 namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
-typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
+typedef __attribute__((ext_vector_type(4))) short s16x4_t;
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((address_space(3))) s16x4_t* lds_s16x4_ptr_t;
+typedef __attribute__((address_space(1))) const void* global_ptr_t;
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBM = 32 * kWaves;  // query rows per workgroup
 static_assert(kBM == kBlockM_bf16, "kBlockM mismatch");
 
-// Keys per K/V block for each head dimension.  Each thread stages four
-// consecutive keys x 8 dims of K and of V per block: BN * D = 4 * 8 * 256.
-template <int D> struct KvBlock;
-template <> struct KvBlock<64> { static constexpr int BN = 128, kWavesPerSimd = 2; };
-template <> struct KvBlock<128> { static constexpr int BN = 64, kWavesPerSimd = 2; };
-template <> struct KvBlock<256> { static constexpr int BN = 32, kWavesPerSimd = 1; };
-
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_inff();
+constexpr float kTau = 8.0f;  // lazy-rescale threshold, log2 units
 
-// Position of key k (within a block) in the V^T rows in LDS: bits 2 and 3 swapped.
-__device__ __forceinline__ int vt_pos(int k) {
-  return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
+// Keys per K/V block and wavefronts per SIMD for each head dimension.
+template <int D> struct Cfg;
+template <> struct Cfg<64> { static constexpr int BN = 64, kWavesPerSimd = 2; };
+template <> struct Cfg<128> { static constexpr int BN = 64, kWavesPerSimd = 2; };
+template <> struct Cfg<256> { static constexpr int BN = 32, kWavesPerSimd = 1; };
+
+// LDS layout of a K or V block: key row r lives in 1 KB piece blk(r) at row
+// slot slot(r); pieces are kPiece bytes apart.  Rows 0..15 of any aligned group
+// fall in 16 different pieces (16 different bank offsets, for the K reads),
+// and the 4 rows of an aligned group of 4 fall in pieces 4 apart (64-byte bank
+// offsets apart, for the transposing V reads).
+constexpr int kPiece = 1024 + 16;
+template <int D>
+__host__ __device__ constexpr int blk(int r) {
+  if constexpr (D == 64) return ((r >> 2) & 3) + 4 * (r & 1);
+  else return 4 * (r & 3) + ((r >> 2) & 3);
 }
+template <int D>
+__host__ __device__ constexpr int slot(int r) {
+  if constexpr (D == 64) return 2 * (r >> 4) + ((r >> 1) & 1);
+  else return r >> 4;
+}
+template <int D>
+__host__ __device__ constexpr int lds_off(int r) { return blk<D>(r) * kPiece + slot<D>(r) * 2 * D; }
 
-// Combine a per-lane value with the one held 32 lanes away (the two lane halves
-// of a 32x32 MFMA tile hold different keys of the same query row).
-// (__builtin_amdgcn_permlane32_swap is not used here: with both of its results
-// feeding one commutative operation, hipcc 7.2 keeps only the first result.)
+// Value of x combined with the one held 32 lanes away (the two lane halves of
+// a 32x32 MFMA tile hold different keys of the same query row).
 __device__ __forceinline__ float halves_max(float x) { return fmaxf(x, __shfl_xor(x, 32, 64)); }
 __device__ __forceinline__ float halves_sum(float x) { return x + __shfl_xor(x, 32, 64); }
 
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(kThreads, KvBlock<D>::kWavesPerSimd)
+__global__ void __launch_bounds__(kThreads, Cfg<D>::kWavesPerSimd)
 fa2_fwd_bf16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
                     const uint16_t* __restrict__ Vg, uint16_t* __restrict__ Og,
                     float* __restrict__ Lg, int N, int num_m_block, int total_blocks,
-                    float c, float scale_abs, uint32_t qsign) {
-  constexpr int BN = KvBlock<D>::BN;
-  constexpr int KST = D + 8;   // K row stride in LDS (elements): +16 bytes against bank conflicts
-  constexpr int VST = BN + 8;  // V^T row stride in LDS (elements)
-  constexpr int KS = D / 16;   // MFMA k-steps over the head dimension
-  constexpr int DT = D / 32;   // 32-wide tiles of the head dimension
-  constexpr int KT = BN / 32;  // 32-key sub-blocks per K/V block
-  constexpr int CH = D / 8;    // 16-byte chunks per row
-  static_assert(BN * D == 4 * 8 * kThreads, "each thread stages 4 rows x 8 elements");
+                    float c, float scale_abs, uint32_t qsign, uint32_t qkeep) {
+  constexpr int BN = Cfg<D>::BN;
+  constexpr int CH = D / 8;                  // 16-byte chunks per key row
+  constexpr int KT = BN / 32;                // 32-key sub-blocks per block
+  constexpr int KS = D / 16;                 // MFMA k-steps over the head dimension
+  constexpr int DT = D / 32;                 // 32-wide tiles of the head dimension
+  constexpr int U = BN / 16;                 // 16-key MFMA k-steps of the PV product
+  constexpr int ROWB = D * 2;                // bytes per key row
+  constexpr int RPP = 1024 / ROWB;           // key rows per 1 KB piece
+  constexpr int PIECES = BN / RPP;           // pieces per K or V block
+  constexpr int LOADS = PIECES / kWaves;     // direct loads per thread per block
+  constexpr int TB = PIECES * kPiece;        // bytes per K or V block buffer
+  constexpr int USTEP = lds_off<D>(16) - lds_off<D>(0);  // 16 keys further in a block
+  constexpr int KTSTEP = lds_off<D>(32) - lds_off<D>(0); // 32 keys further in a block
+  static_assert(LOADS >= 1 && PIECES % kWaves == 0, "block must split evenly over wavefronts");
+  static_assert(3 * TB + 2 * kPiece + USTEP * (U - 1) + 64 * DT + 1024 < 65536,
+                "LDS offsets fit the 16-bit instruction offset");
 
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[BN * KST];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[D * VST];
+  __shared__ __attribute__((aligned(1024))) char smem[4 * TB];  // K0 K1 V0 V1
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -120,20 +171,64 @@ fa2_fwd_bf16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict_
   const int q0 = m * kBM + wave * 32;  // first query row of this wavefront
   const int qrow = q0 + col;
 
-  // Q fragments (the B operand of S^T = K Q^T), kept in registers for the whole loop.
+  // Q fragments (the B operand of S^T = K Q^T), kept in registers for the whole
+  // loop.  A negative scale flips Q's sign (exact); a zero scale zeroes Q, which
+  // gives the same all-zero logits.
   bf16x8_t qf[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     u32x4_t t = {0u, 0u, 0u, 0u};
     if (qrow < N) t = *(const u32x4_t*)(Qh + (size_t)qrow * D + ks * 16 + 8 * half);
-    t ^= qsign;  // exact sign flip when the scale is negative
+    t = (t & qkeep) ^ qsign;
     qf[ks] = __builtin_bit_cast(bf16x8_t, t);
   }
+
+  // ---- global -> LDS staging map: load i of this thread fills piece
+  // b = wave*LOADS + i, whose lane L writes bytes 16L.. of the piece: row slot
+  // L / CH, 16-byte chunk L % CH of the key row r with blk(r) = b and
+  // slot(r) = L / CH.  That row splits into a per-lane part and a per-piece
+  // (wave-uniform) part 4*(b&3) + (b>>2).
+  int lane_row, lane_col;
+  {
+    const int sl = lane / CH;
+    lane_row = D == 64 ? 16 * (sl >> 1) + 2 * (sl & 1) : 16 * sl;
+    lane_col = (lane % CH) * 8;
+  }
+  auto issue_block = [&](const uint16_t* head, int k0, char* buf) {
+    const bool tail = k0 + BN > N;  // rows past N are clamped to row N-1 (their keys are masked)
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int b = wave * LOADS + i;
+      const int prow = k0 + 4 * (b & 3) + (b >> 2);
+      int r = prow + lane_row;
+      if (tail) r = min(r, N - 1);
+      __builtin_amdgcn_global_load_lds((global_ptr_t)(head + (size_t)r * D + lane_col),
+                                       (lds_ptr_t)(buf + b * kPiece), 16, 0, 0);
+    }
+  };
+
+  // ---- LDS fragment addresses (bytes within a block buffer).
+  // K (A operand of S^T): key row kt*32 + col, dims 16*ks + 8*half ..+8.
+  const uint32_t kaddr = lds_off<D>(col) + 16 * half;
+  // V^T (A operand of O^T += V^T P^T) through ds_read_b64_tr_b16: within each
+  // group of 16 lanes, lane 4*r + c supplies the address of 4 consecutive dims
+  // (d0 + 4c ..) of key row (kbase + r); the hardware hands lane t of the
+  // group the 4 keys kbase..kbase+3 of dim d0 + t.  kbase = 16u + 4*half (the
+  // first 4 slots of the operand) or 16u + 8 + 4*half (the last 4), matching
+  // the keys 8*(r/4) + 4*half + r%4 that a lane's S^T accumulators hold.
+  uint32_t vaddr;
+  {
+    const int g = lane >> 4, i16 = lane & 15;
+    const int r = 4 * (g >> 1) + (i16 >> 2);
+    const int d = 16 * (g & 1) + 4 * (i16 & 3);
+    vaddr = lds_off<D>(r) + 2 * d;
+  }
+  static_assert(lds_off<D>(8) - lds_off<D>(0) == 2 * kPiece, "rows 8 apart are 2 pieces apart");
 
   f32x16_t o[DT];
 #pragma unroll
   for (int t = 0; t < DT; ++t) o[t] = f32x16_t{};
-  float m_run = kNegInf;  // running max of the unscaled logits (sign-adjusted)
+  float m_ref = kNegInf;  // reference max of the (sign-adjusted) raw logits
   float l_part = 0.f;     // running sum over this lane's half of the keys
 
   const int n_blocks = (N + BN - 1) / BN;
@@ -143,117 +238,129 @@ fa2_fwd_bf16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict_
     j_end = last / BN + 1;
   }
 
-  // Staging map: thread -> 16-byte column chunk cc of rows 4*rg .. 4*rg+3.
-  const int cc = tid % CH;
-  const int rg = tid / CH;
-  u32x4_t kr[4], vr[4];
-  auto load_block = [&](int j) {
+  char* const Kb0 = smem;
+  char* const Vb0 = smem + 2 * TB;
+
+  auto compute_S = [&](const char* kb, f32x16_t (&S)[KT]) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = j * BN + rg * 4 + r;
-      if (row < N) {
-        kr[r] = *(const u32x4_t*)(Kh + (size_t)row * D + cc * 8);
-        vr[r] = *(const u32x4_t*)(Vh + (size_t)row * D + cc * 8);
-      } else {
-        kr[r] = u32x4_t{0u, 0u, 0u, 0u};
-        vr[r] = u32x4_t{0u, 0u, 0u, 0u};
+    for (int kt = 0; kt < KT; ++kt) {
+      S[kt] = f32x16_t{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8_t a = *(const bf16x8_t*)(kb + kaddr + kt * KTSTEP + ks * 32);
+        S[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], S[kt], 0, 0, 0);
       }
     }
   };
 
-  load_block(0);
-  for (int j = 0; j < j_end; ++j) {
-    __syncthreads();  // every wavefront has finished reading the previous block
-#pragma unroll
-    for (int r = 0; r < 4; ++r) *(u32x4_t*)(Ks + (rg * 4 + r) * KST + cc * 8) = kr[r];
-    {
-      // V^T: for each of the thread's 8 dims, its 4 keys form 8 contiguous bytes.
-      const int pos = vt_pos(rg * 4);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        u32x2_t ev, od;
-        ev[0] = __builtin_amdgcn_perm(vr[1][w], vr[0][w], 0x05040100u);
-        ev[1] = __builtin_amdgcn_perm(vr[3][w], vr[2][w], 0x05040100u);
-        od[0] = __builtin_amdgcn_perm(vr[1][w], vr[0][w], 0x07060302u);
-        od[1] = __builtin_amdgcn_perm(vr[3][w], vr[2][w], 0x07060302u);
-        *(u32x2_t*)(Vs + (cc * 8 + 2 * w) * VST + pos) = ev;
-        *(u32x2_t*)(Vs + (cc * 8 + 2 * w + 1) * VST + pos) = od;
-      }
-    }
-    __syncthreads();
-    if (j + 1 < j_end) load_block(j + 1);  // in flight while this block is computed
-
+  // Softmax of block j (pseudo-code line 9) and the O update (line 10);
+  // `during` issues independent MFMA work (the next block's S) alongside.
+  auto consume = [&](auto masked_tag, int j, f32x16_t(&S)[KT], auto&& during) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
     const int k0 = j * BN;
-    if (CAUSAL && k0 > q0 + 31) continue;  // block entirely masked for this wavefront
-
-    // S^T = K_j Q_i^T (line 8 of the pseudo-code), fp32 accumulation.
-    f32x16_t sacc[KT];
-#pragma unroll
-    for (int kt = 0; kt < KT; ++kt) {
-      sacc[kt] = f32x16_t{};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8_t a = *(const bf16x8_t*)(Ks + (kt * 32 + col) * KST + ks * 16 + 8 * half);
-        sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sacc[kt], 0, 0, 0);
-      }
-    }
-
-    const bool masked = (CAUSAL && k0 + BN - 1 > q0) || (k0 + BN > N);
-    if (masked) {
+    if constexpr (MASKED) {
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = k0 + kt * 32 + 8 * (r / 4) + 4 * half + (r % 4);
           const bool hide = (CAUSAL && key > qrow) || key >= N;
-          sacc[kt][r] = hide ? kNegInf : sacc[kt][r];
+          S[kt][r] = hide ? kNegInf : S[kt][r];
         }
     }
-
-    // Online softmax (line 9): new running max, rescale factor, P~ and row sum.
+    during();
     float mx = kNegInf;
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kt][r]);
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[kt][r]);
     mx = halves_max(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const float mc = m_new == kNegInf ? 0.f : c * m_new;
-    const float alpha = m_run == kNegInf ? 0.f : __builtin_amdgcn_exp2f(c * m_run - mc);
-    m_run = m_new;
-
+    float alpha = 1.f;
+    if (m_ref == kNegInf) {  // first block with a visible key: O and l are still zero
+      m_ref = mx;
+      alpha = 0.f;
+    } else if (c * (mx - m_ref) > kTau) {
+      alpha = __builtin_amdgcn_exp2f(c * (m_ref - mx));
+      m_ref = mx;
+    }
+    const float mc = m_ref == kNegInf ? 0.f : c * m_ref;
     float ls = 0.f;
+    bf16x8_t pb[U];
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][r], c, -mc));
-        if (masked) p = sacc[kt][r] == kNegInf ? 0.f : p;
-        sacc[kt][r] = p;
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kt][r], c, -mc));
         ls += p;
+        pb[kt * 2 + r / 8][r % 8] = (__bf16)p;
       }
     l_part = alpha * l_part + ls;
-
-    // O^T = diag(alpha) O^T + V_j^T P~^T (line 10), no division by l.
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
 #pragma unroll
-    for (int t = 0; t < DT; ++t) o[t] *= alpha;
+      for (int t = 0; t < DT; ++t) o[t] *= alpha;
+    }
+    const char* vb = Vb0 + (j & 1) * TB + vaddr;
 #pragma unroll
-    for (int kt = 0; kt < KT; ++kt)
+    for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int hk = 0; hk < 2; ++hk) {
-        bf16x8_t pb;
-#pragma unroll
-        for (int s = 0; s < 8; ++s) pb[s] = (__bf16)sacc[kt][hk * 8 + s];
-        const int u = kt * 2 + hk;  // 16-key step
-#pragma unroll
-        for (int t = 0; t < DT; ++t) {
-          const bf16x8_t a = *(const bf16x8_t*)(Vs + (t * 32 + col) * VST + u * 16 + 8 * half);
-          o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, o[t], 0, 0, 0);
-        }
+      for (int t = 0; t < DT; ++t) {
+        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4_ptr_t)(vb + u * USTEP + t * 64));
+        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4_ptr_t)(vb + 2 * kPiece + u * USTEP + t * 64));
+        const bf16x8_t a = __builtin_bit_cast(
+            bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[u], o[t], 0, 0, 0);
       }
-  }
+  };
 
-  // Epilogue (lines 12-13): O = O / l once, L = m + ln(l).
+  // ---- prologue: K0, V0 and K1 in flight; S for block 0.
+  issue_block(Kh, 0, Kb0);
+  issue_block(Vh, 0, Vb0);
+  if (j_end > 1) {
+    issue_block(Kh, BN, Kb0 + TB);
+    wait_vmcnt<2 * LOADS>();
+  } else {
+    wait_vmcnt<LOADS>();
+  }
+  __syncthreads();
+  f32x16_t S_cur[KT];
+  compute_S(Kb0, S_cur);
+
+  // One barrier per block: block j's V and block j+1's K have landed in LDS,
+  // and every wavefront is done with the buffers of block j-1, which the loads
+  // for blocks j+2 (K) and j+1 (V) issued right after reuse.
+  auto advance = [&](int j) {
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (j + 2 < j_end) issue_block(Kh, (j + 2) * BN, Kb0 + (j & 1) * TB);
+    if (j + 1 < j_end) issue_block(Vh, (j + 1) * BN, Vb0 + ((j + 1) & 1) * TB);
+  };
+  // Blocks before j_mask need no mask for this wavefront (all keys visible to
+  // all of its rows); the loop runs in three stretches so that each loop body
+  // holds a single variant: unmasked, masked (causal diagonal, ragged tail),
+  // and the last block, which has no successor to overlap with.
+  const int j_mask = CAUSAL ? min((q0 + 1) / BN, N / BN) : N / BN;
+  int j = 0;
+  for (; j < j_mask && j + 1 < j_end; ++j) {
+    advance(j);
+    f32x16_t S_next[KT];
+    consume(std::false_type{}, j, S_cur, [&]() { compute_S(Kb0 + ((j + 1) & 1) * TB, S_next); });
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) S_cur[kt] = S_next[kt];
+  }
+  for (; j + 1 < j_end; ++j) {
+    advance(j);
+    f32x16_t S_next[KT];
+    consume(std::true_type{}, j, S_cur, [&]() { compute_S(Kb0 + ((j + 1) & 1) * TB, S_next); });
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) S_cur[kt] = S_next[kt];
+  }
+  advance(j);
+  if (j < j_mask) consume(std::false_type{}, j, S_cur, [] {});
+  else consume(std::true_type{}, j, S_cur, [] {});
+
+  // ---- epilogue (lines 12-13): O = O / l once, L = m + ln(l).
   const float l_tot = halves_sum(l_part);
   const float inv = 1.f / l_tot;
   if (qrow < N) {
@@ -262,24 +369,29 @@ fa2_fwd_bf16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict_
     for (int t = 0; t < DT; ++t)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
         bf16x4_t w;
 #pragma unroll
         for (int r = 0; r < 4; ++r) w[r] = (__bf16)(o[t][g * 4 + r] * inv);
         *(bf16x4_t*)(orow + t * 32 + 8 * g + 4 * half) = w;
       }
-    if (half == 0) Lh[qrow] = __builtin_fmaf(__builtin_amdgcn_logf(l_tot), kLn2, scale_abs * m_run);
+    if (half == 0)
+      Lh[qrow] = __builtin_fmaf(__builtin_amdgcn_logf(l_tot), kLn2, scale_abs * m_ref);
   }
 }
 
 template <int D, bool CAUSAL>
 hipError_t launch(const FwdArgs& a) {
   const int total = a.num_m_block * a.BH;
-  const float sa = a.scale < 0.f ? -a.scale : a.scale;
+  // The kernel works with c = |scale| * log2(e) > 0: a negative scale flips the
+  // sign of Q and a zero scale zeroes Q (both exact), with |scale| = 1 then.
+  const bool zero = a.scale == 0.f;
+  const float sa = zero ? 1.f : (a.scale < 0.f ? -a.scale : a.scale);
   const uint32_t qsign = a.scale < 0.f ? 0x80008000u : 0u;
+  const uint32_t qkeep = zero ? 0u : 0xFFFFFFFFu;
   hipLaunchKernelGGL((fa2_fwd_bf16_kernel<D, CAUSAL>), dim3(total), dim3(kThreads), 0, a.stream,
                      (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V,
-                     (uint16_t*)a.O, a.L, a.N, a.num_m_block, total, sa * kLog2e, sa, qsign);
+                     (uint16_t*)a.O, a.L, a.N, a.num_m_block, total, sa * kLog2e, sa, qsign,
+                     qkeep);
   return hipGetLastError();
 }
 
