@@ -47,7 +47,25 @@ def parse_args(argv=None):
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target duration of the CPU-oracle baseline sample (0 disables it)")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="instead of the benchmark, run a plain device-to-device copy of MIB MiB "
+                        "(--steps times): the reference for scaling FETCH_SIZE / WRITE_SIZE")
     return p.parse_args(argv)
+
+
+def copy_calibration(mib: int, steps: int) -> int:
+    """A plain copy kernel of known size, for calibrating the HBM byte counters."""
+    import torch
+
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n * 4, "copy_calibration_bytes_written": n * 4,
+                      "steps": steps}), flush=True)
+    return 0
 
 
 def kernel_source_hash(dtype: str) -> str:
@@ -116,6 +134,9 @@ def main(argv=None) -> int:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
               f"(asked for --gpus {args.gpus}, WORLD_SIZE={world}).", file=sys.stderr)
         return 2
+
+    if args.copy_calibration:
+        return copy_calibration(args.copy_calibration, args.steps)
 
     import torch
 

@@ -141,7 +141,7 @@ fa2_fwd_bf16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict_
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps LDS bases scalar
   const int col = lane & 31;  // this lane's query row within the wavefront's 32
   const int half = lane >> 5;
 
@@ -194,16 +194,26 @@ fa2_fwd_bf16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict_
     lane_row = D == 64 ? 16 * (sl >> 1) + 2 * (sl & 1) : 16 * sl;
     lane_col = (lane % CH) * 8;
   }
+  const uint32_t lane_bytes = (uint32_t)(lane_row * D + lane_col) * 2;
   auto issue_block = [&](const uint16_t* head, int k0, char* buf) {
-    const bool tail = k0 + BN > N;  // rows past N are clamped to row N-1 (their keys are masked)
+    if (k0 + BN <= N) {
+      // Scalar base (the piece's first row) plus a constant 32-bit per-lane offset.
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int b = wave * LOADS + i;
-      const int prow = k0 + 4 * (b & 3) + (b >> 2);
-      int r = prow + lane_row;
-      if (tail) r = min(r, N - 1);
-      __builtin_amdgcn_global_load_lds((global_ptr_t)(head + (size_t)r * D + lane_col),
-                                       (lds_ptr_t)(buf + b * kPiece), 16, 0, 0);
+      for (int i = 0; i < LOADS; ++i) {
+        const int b = wave * LOADS + i;
+        const char* base = (const char*)(head + (size_t)(k0 + 4 * (b & 3) + (b >> 2)) * D);
+        __builtin_amdgcn_global_load_lds((global_ptr_t)(base + lane_bytes),
+                                         (lds_ptr_t)(buf + b * kPiece), 16, 0, 0);
+      }
+    } else {
+      // Ragged last block: rows past N are clamped to row N-1 (their keys are masked).
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        const int b = wave * LOADS + i;
+        const int r = min(k0 + 4 * (b & 3) + (b >> 2) + lane_row, N - 1);
+        __builtin_amdgcn_global_load_lds((global_ptr_t)(head + (size_t)r * D + lane_col),
+                                         (lds_ptr_t)(buf + b * kPiece), 16, 0, 0);
+      }
     }
   };
 
@@ -341,20 +351,36 @@ fa2_fwd_bf16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict_
   // holds a single variant: unmasked, masked (causal diagonal, ragged tail),
   // and the last block, which has no successor to overlap with.
   const int j_mask = CAUSAL ? min((q0 + 1) / BN, N / BN) : N / BN;
+  const int j_unmasked = min(j_mask, j_end - 1);  // unmasked blocks that have a successor
+  f32x16_t SB[KT];
   int j = 0;
-  for (; j < j_mask && j + 1 < j_end; ++j) {
+  // Unrolled by two so that the S registers alternate between S_cur and SB
+  // instead of being copied every block.
+  for (; j + 2 <= j_unmasked; j += 2) {
     advance(j);
-    f32x16_t S_next[KT];
-    consume(std::false_type{}, j, S_cur, [&]() { compute_S(Kb0 + ((j + 1) & 1) * TB, S_next); });
-#pragma unroll
-    for (int kt = 0; kt < KT; ++kt) S_cur[kt] = S_next[kt];
+    consume(std::false_type{}, j, S_cur, [&]() { compute_S(Kb0 + ((j + 1) & 1) * TB, SB); });
+    advance(j + 1);
+    consume(std::false_type{}, j + 1, SB, [&]() { compute_S(Kb0 + (j & 1) * TB, S_cur); });
   }
-  for (; j + 1 < j_end; ++j) {
+  if (j < j_unmasked) {
     advance(j);
-    f32x16_t S_next[KT];
-    consume(std::true_type{}, j, S_cur, [&]() { compute_S(Kb0 + ((j + 1) & 1) * TB, S_next); });
+    consume(std::false_type{}, j, S_cur, [&]() { compute_S(Kb0 + ((j + 1) & 1) * TB, SB); });
 #pragma unroll
-    for (int kt = 0; kt < KT; ++kt) S_cur[kt] = S_next[kt];
+    for (int kt = 0; kt < KT; ++kt) S_cur[kt] = SB[kt];
+    ++j;
+  }
+  for (; j + 2 < j_end; j += 2) {
+    advance(j);
+    consume(std::true_type{}, j, S_cur, [&]() { compute_S(Kb0 + ((j + 1) & 1) * TB, SB); });
+    advance(j + 1);
+    consume(std::true_type{}, j + 1, SB, [&]() { compute_S(Kb0 + (j & 1) * TB, S_cur); });
+  }
+  if (j + 1 < j_end) {
+    advance(j);
+    consume(std::true_type{}, j, S_cur, [&]() { compute_S(Kb0 + ((j + 1) & 1) * TB, SB); });
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) S_cur[kt] = SB[kt];
+    ++j;
   }
   advance(j);
   if (j < j_mask) consume(std::false_type{}, j, S_cur, [] {});
