@@ -30,12 +30,13 @@
 // Memory pipeline.  K and V blocks go from HBM straight into LDS
 // (global_load_lds_dwordx4, no register staging), double-buffered: while
 // block j is consumed, blocks j+1 (V) and j+2 (K) are in flight, with one
-// workgroup barrier per block.  Each direct load writes 1 KB of LDS (whole key
-// rows); those 1 KB pieces sit 1040 bytes apart, and which rows share a piece
-// is chosen so that both the K fragment reads (16 rows x 16 bytes per pass)
-// and the transposing V reads (ds_read_b64_tr_b16: 4 rows x 64 bytes per
-// pass) touch every LDS bank once, while every fragment address stays one
-// per-lane base plus a compile-time offset.
+// workgroup barrier per block.  Each direct load writes 1 KB of LDS.  K: whole
+// key rows in 1 KB pieces that sit 1040 bytes apart, with the rows that share
+// a piece chosen so that the K fragment reads (16 rows x 16 bytes per pass)
+// touch every LDS bank once.  V: 128-byte blocks of 4 key rows x 16 dims, so
+// that each 16-lane group of a transposing read (ds_read_b64_tr_b16) reads
+// one contiguous block, the pattern the LDS serves fastest.  Every fragment
+// address is one per-lane base plus a compile-time offset.
 //
 // Overlap.  The MFMAs of block j+1's S = K Q^T are issued in the same basic
 // block as block j's softmax (vector ALU: exp2, row max/sum, bf16 packing), so
@@ -101,6 +102,7 @@ __host__ __device__ constexpr int slot(int r) {
 }
 template <int D>
 __host__ __device__ constexpr int lds_off(int r) { return blk<D>(r) * kPiece + slot<D>(r) * 2 * D; }
+// V layout: element (key row r, dim d) at (r/4)*4*2D + (d/16)*128 + 32*(r%4) + 2*(d%16).
 
 // Value of x combined with the one held 32 lanes away (the two lane halves of
 // a 32x32 MFMA tile hold different keys of the same query row).
@@ -130,14 +132,24 @@ fa2_fwd_bf16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict_
   constexpr int RPP = 1024 / ROWB;           // key rows per 1 KB piece
   constexpr int PIECES = BN / RPP;           // pieces per K or V block
   constexpr int LOADS = PIECES / kWaves;     // direct loads per thread per block
-  constexpr int TB = PIECES * kPiece;        // bytes per K or V block buffer
-  constexpr int USTEP = lds_off<D>(16) - lds_off<D>(0);  // 16 keys further in a block
-  constexpr int KTSTEP = lds_off<D>(32) - lds_off<D>(0); // 32 keys further in a block
+  constexpr int TB = PIECES * kPiece;        // bytes per K block buffer
+  constexpr int TBV = BN * ROWB;             // bytes per V block buffer
+  constexpr int LOADS_V = TBV / 1024 / kWaves;  // direct V loads per thread per block
+  constexpr int NSEG = D / 16;               // 16-dim segments per V row
+  constexpr int KTSTEP = lds_off<D>(32) - lds_off<D>(0); // 32 keys further in a K block
   static_assert(LOADS >= 1 && PIECES % kWaves == 0, "block must split evenly over wavefronts");
-  static_assert(3 * TB + 2 * kPiece + USTEP * (U - 1) + 64 * DT + 1024 < 65536,
+  // blk()/slot() place the rows of a K block on exactly 16 pieces (8 for D = 64)
+  // of RPP rows each; any other block size would address rows and pieces
+  // outside the block and its buffer.
+  static_assert(PIECES == (D == 64 ? 8 : 16) && BN == PIECES * RPP,
+                "K LDS layout is defined for BN = 64 (D = 64, 128) and BN = 32 (D = 256) only");
+  static_assert(lds_off<D>(BN - 1) + ROWB <= TB, "K rows stay inside their buffer");
+  static_assert(LOADS_V >= 1 && TBV % (1024 * kWaves) == 0, "V block must split evenly");
+  static_assert(TBV + 16 * ROWB * (U - 1) + 8 * ROWB + 256 * (DT - 1) < 65536 &&
+                    2 * TBV + TB + KTSTEP * (KT - 1) + 32 * (KS - 1) < 65536,
                 "LDS offsets fit the 16-bit instruction offset");
 
-  __shared__ __attribute__((aligned(1024))) char smem[4 * TB];  // K0 K1 V0 V1
+  __shared__ __attribute__((aligned(1024))) char smem[2 * TBV + 2 * TB];  // V0 V1 K0 K1
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -217,6 +229,37 @@ fa2_fwd_bf16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict_
     }
   };
 
+  // V staging: load i of this thread fills 1 KB chunk n = wave*LOADS_V + i,
+  // whose lane L writes 16 bytes: 128-byte block bk = 8n + L/8 (row group
+  // bk / NSEG, dim segment bk % NSEG), row (L%8)/2 of that group, dims
+  // 8*(L%2) ..+8 of that segment.  The lane's share of the key row and dims is
+  // the same for every n; n only adds a wave-uniform row / dim offset.
+  int vrow_l, vdim_l;
+  {
+    const int x = lane / 8;
+    if constexpr (NSEG <= 8) {
+      vrow_l = 4 * (x / NSEG) + (lane % 8) / 2;
+      vdim_l = 16 * (x % NSEG) + 8 * (lane % 2);
+    } else {
+      vrow_l = (lane % 8) / 2;
+      vdim_l = 16 * x + 8 * (lane % 2);
+    }
+  }
+  const uint32_t vlane = (uint32_t)(vrow_l * D + vdim_l) * 2;
+  auto issue_v = [&](int k0, char* buf) __attribute__((always_inline)) {
+    const char* base = (const char*)(Vh + (size_t)k0 * D);
+    const bool tail = k0 + BN > N;  // rows past N are clamped to row N-1 (P~ is 0 there)
+#pragma unroll
+    for (int i = 0; i < LOADS_V; ++i) {
+      const int n = wave * LOADS_V + i;
+      const int row_u = NSEG <= 8 ? 4 * n * (8 / NSEG) : 4 * (n / 2);
+      const int dim_u = NSEG <= 8 ? 0 : 128 * (n % 2);
+      const char* src = base + (row_u * D + dim_u) * 2 + vlane;
+      if (tail) src += (ptrdiff_t)(min(k0 + row_u + vrow_l, N - 1) - (k0 + row_u + vrow_l)) * ROWB;
+      __builtin_amdgcn_global_load_lds((global_ptr_t)src, (lds_ptr_t)(buf + n * 1024), 16, 0, 0);
+    }
+  };
+
   // ---- LDS fragment addresses (bytes within a block buffer).
   // K (A operand of S^T): key row kt*32 + col, dims 16*ks + 8*half ..+8.
   const uint32_t kaddr = lds_off<D>(col) + 16 * half;
@@ -226,14 +269,9 @@ fa2_fwd_bf16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict_
   // group the 4 keys kbase..kbase+3 of dim d0 + t.  kbase = 16u + 4*half (the
   // first 4 slots of the operand) or 16u + 8 + 4*half (the last 4), matching
   // the keys 8*(r/4) + 4*half + r%4 that a lane's S^T accumulators hold.
-  uint32_t vaddr;
-  {
-    const int g = lane >> 4, i16 = lane & 15;
-    const int r = 4 * (g >> 1) + (i16 >> 2);
-    const int d = 16 * (g & 1) + 4 * (i16 & 3);
-    vaddr = lds_off<D>(r) + 2 * d;
-  }
-  static_assert(lds_off<D>(8) - lds_off<D>(0) == 2 * kPiece, "rows 8 apart are 2 pieces apart");
+  // With the V layout, the 16 lanes of a group read one contiguous 128-byte
+  // block: lane i at byte 8i of the block of rows kbase.. and dims d0..d0+15.
+  const uint32_t vaddr = (uint32_t)(((lane >> 4) >> 1) * 4 * ROWB + ((lane >> 4) & 1) * 128 + 8 * (lane & 15));
 
   f32x16_t o[DT];
 #pragma unroll
@@ -248,8 +286,8 @@ fa2_fwd_bf16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict_
     j_end = last / BN + 1;
   }
 
-  char* const Kb0 = smem;
-  char* const Vb0 = smem + 2 * TB;
+  char* const Vb0 = smem;
+  char* const Kb0 = smem + 2 * TBV;
 
   auto compute_S = [&](const char* kb, f32x16_t (&S)[KT]) {
 #pragma unroll
@@ -309,15 +347,15 @@ fa2_fwd_bf16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict_
 #pragma unroll
       for (int t = 0; t < DT; ++t) o[t] *= alpha;
     }
-    const char* vb = Vb0 + (j & 1) * TB + vaddr;
+    const char* vb = Vb0 + (j & 1) * TBV + vaddr;
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int t = 0; t < DT; ++t) {
         const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4_ptr_t)(vb + u * USTEP + t * 64));
+            (lds_s16x4_ptr_t)(vb + u * 16 * ROWB + t * 256));
         const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4_ptr_t)(vb + 2 * kPiece + u * USTEP + t * 64));
+            (lds_s16x4_ptr_t)(vb + 8 * ROWB + u * 16 * ROWB + t * 256));
         const bf16x8_t a = __builtin_bit_cast(
             bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[u], o[t], 0, 0, 0);
@@ -326,12 +364,12 @@ fa2_fwd_bf16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict_
 
   // ---- prologue: K0, V0 and K1 in flight; S for block 0.
   issue_block(Kh, 0, Kb0);
-  issue_block(Vh, 0, Vb0);
+  issue_v(0, Vb0);
   if (j_end > 1) {
     issue_block(Kh, BN, Kb0 + TB);
-    wait_vmcnt<2 * LOADS>();
+    wait_vmcnt<LOADS_V + LOADS>();
   } else {
-    wait_vmcnt<LOADS>();
+    wait_vmcnt<LOADS_V>();
   }
   __syncthreads();
   f32x16_t S_cur[KT];
@@ -344,7 +382,7 @@ fa2_fwd_bf16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict_
     wait_vmcnt<0>();
     __syncthreads();
     if (j + 2 < j_end) issue_block(Kh, (j + 2) * BN, Kb0 + (j & 1) * TB);
-    if (j + 1 < j_end) issue_block(Vh, (j + 1) * BN, Vb0 + ((j + 1) & 1) * TB);
+    if (j + 1 < j_end) issue_v((j + 1) * BN, Vb0 + ((j + 1) & 1) * TBV);
   };
   // Blocks before j_mask need no mask for this wavefront (all keys visible to
   // all of its rows); the loop runs in three stretches so that each loop body
