@@ -425,22 +425,42 @@ fa2_fwd_bf16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict_
   else consume(std::true_type{}, j, S_cur, [] {});
 
   // ---- epilogue (lines 12-13): O = O / l once, L = m + ln(l).
+  // The wavefront's 32 output rows are one contiguous stretch of O.  They go
+  // through LDS (16-byte chunks XOR-swizzled by row against bank conflicts) so
+  // that the global stores are whole rows, 16 bytes per lane.  The K buffers
+  // are free once the last barrier has passed (the last block reads only V);
+  // with D = 256 the staging needs all of LDS and waits for the last V reads.
   const float l_tot = halves_sum(l_part);
   const float inv = 1.f / l_tot;
-  if (qrow < N) {
-    uint16_t* orow = Oh + (size_t)qrow * D;
+  constexpr int CHK = D / 8;                    // 16-byte chunks per output row
+  constexpr int SWZ = CHK < 16 ? CHK - 1 : 15;  // swizzle mask
+  constexpr int STAGE = 32 * ROWB;              // bytes per wavefront
+  constexpr bool IN_K = kWaves * STAGE <= 2 * TB;
+  static_assert(kWaves * STAGE <= 2 * TBV + 2 * TB, "staging fits in LDS");
+  if constexpr (!IN_K) __syncthreads();
+  char* const stage = (IN_K ? Kb0 : smem) + wave * STAGE;
 #pragma unroll
-    for (int t = 0; t < DT; ++t)
+  for (int t = 0; t < DT; ++t)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        bf16x4_t w;
+    for (int g = 0; g < 4; ++g) {
+      bf16x4_t w;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) w[r] = (__bf16)(o[t][g * 4 + r] * inv);
-        *(bf16x4_t*)(orow + t * 32 + 8 * g + 4 * half) = w;
-      }
-    if (half == 0)
-      Lh[qrow] = __builtin_fmaf(__builtin_amdgcn_logf(l_tot), kLn2, scale_abs * m_ref);
+      for (int r = 0; r < 4; ++r) w[r] = (__bf16)(o[t][g * 4 + r] * inv);
+      const int d = t * 32 + 8 * g + 4 * half;
+      *(bf16x4_t*)(stage + col * ROWB + (((d >> 3) ^ (col & SWZ)) << 4) + (d & 7) * 2) = w;
+    }
+  __builtin_amdgcn_s_waitcnt((15 << 0) | (3 << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0)
+  __builtin_amdgcn_wave_barrier();
+  constexpr int RPI = 64 / CHK;  // rows per store instruction
+#pragma unroll
+  for (int i = 0; i < 32 / RPI; ++i) {
+    const int row = i * RPI + lane / CHK;
+    const int ch = lane % CHK;
+    const u32x4_t v = *(const u32x4_t*)(stage + row * ROWB + ((ch ^ (row & SWZ)) << 4));
+    if (q0 + row < N) *(u32x4_t*)(Oh + (size_t)(q0 + row) * D + ch * 8) = v;
   }
+  if (qrow < N && half == 0)
+    Lh[qrow] = __builtin_fmaf(__builtin_amdgcn_logf(l_tot), kLn2, scale_abs * m_ref);
 }
 
 template <int D, bool CAUSAL>
