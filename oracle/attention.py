@@ -8,8 +8,8 @@ What it computes
 ----------------
 The FlashAttention-2 forward pass is exact attention computed tile by tile:
 after the inner loop has visited every K/V block, the running result equals
-the global softmax result (page "Flash Attention V2原理解读", FWD pseudo-code
-commentary on lines 9-10).  So the oracle is that plain definition, written
+the global softmax result (page "Flash Attention V2原理解读", commentary on
+the FWD pseudo-code's inner loop).  So the oracle is that plain definition, written
 out with the whole score row materialised, for every (batch, head):
 
     S[i, j] = scale * sum_k Q[i, k] * K[j, k]

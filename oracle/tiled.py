@@ -9,21 +9,20 @@ algorithm in the pages' order and notation:
     m_i, l_i stay local for the whole inner loop (page "FlashAttention学习笔记(2)",
     opening section; page "Flash Attention V2原理解读", FWD commentary);
   * inner loop over key/value blocks K_j, V_j of Bc rows:
-      - the score block S_i^(j) = scale * Q_i K_j^T          (pseudo-code line 8)
-      - m_i^(j) = max(m_i^(j-1), rowmax S_i^(j)),
+      - the score block S_i^(j) = scale * Q_i K_j^T
+      - the softmax update: m_i^(j) = max(m_i^(j-1), rowmax S_i^(j)),
         P~ = exp(S_i^(j) - m_i^(j)),
-        l_i^(j) = exp(m_i^(j-1) - m_i^(j)) l_i^(j-1) + rowsum P~   (line 9)
-      - O_i^(j) = diag(exp(m_i^(j-1) - m_i^(j))) O_i^(j-1) + P~ V_j, with no
-        division by l inside the loop                             (line 10)
-  * after the loop, O_i = diag(l_i)^-1 O_i once                   (line 12)
-    and L_i = m_i + log(l_i)                                       (line 13)
+        l_i^(j) = exp(m_i^(j-1) - m_i^(j)) l_i^(j-1) + rowsum P~
+      - the output update: O_i^(j) = diag(exp(m_i^(j-1) - m_i^(j))) O_i^(j-1)
+        + P~ V_j, with no division by l inside the loop
+  * after the loop, O_i = diag(l_i)^-1 O_i once and L_i = m_i + log(l_i)
     (page "FlashAttention学习笔记(2)", forward; page
     "flash-attention123和ring-attention", 优化1 and 优化2);
   * with the causal mask, K/V blocks that lie entirely above the diagonal
     are skipped, not computed and then masked (page
     "flash-attention123和ring-attention", 优化3).
 
-The text of pseudo-code lines 8-13 did not survive on the pages; the steps
+The text of the pseudo-code's inner-loop steps did not survive on the pages; the steps
 above are rebuilt from the surviving prose plus the online-softmax
 mathematics.  ``deferred_norm=False`` gives the per-step normalised variant
 (dividing by the running l every step) that 优化2 says the deferral removes;
@@ -75,7 +74,7 @@ def fa2_forward_tiled_fp64(q, k, v, causal: bool = False, scale: float | None = 
                 for j in range(j_end):
                     c0, c1 = j * Bc, min(N, (j + 1) * Bc)
                     Kj, Vj = k[b, h, c0:c1], v[b, h, c0:c1]
-                    S = scale * (Qi @ Kj.T)  # line 8
+                    S = scale * (Qi @ Kj.T)  # score block
                     if causal:
                         S = np.where(np.arange(c0, c1)[None, :] > rows[:, None], -np.inf, S)
                     m_new = np.maximum(mi, S.max(axis=1))
@@ -84,14 +83,14 @@ def fa2_forward_tiled_fp64(q, k, v, causal: bool = False, scale: float | None = 
                     shift = np.where(np.isneginf(m_new), 0.0, m_new)
                     P = np.exp(S - shift[:, None])
                     alpha = np.exp(mi - shift)
-                    l_new = alpha * li + P.sum(axis=1)  # line 9
+                    l_new = alpha * li + P.sum(axis=1)  # running sum
                     if deferred_norm:
-                        Oi = alpha[:, None] * Oi + P @ Vj  # line 10
+                        Oi = alpha[:, None] * Oi + P @ Vj  # output update, unnormalised
                     else:
                         Oi = ((alpha * li)[:, None] * Oi + P @ Vj) / l_new[:, None]
                     mi, li = m_new, l_new
                 if deferred_norm:
-                    Oi = Oi / li[:, None]  # line 12
+                    Oi = Oi / li[:, None]  # normalise once
                 O[b, h, r0:r1] = Oi
-                L[b, h, r0:r1] = mi + np.log(li)  # line 13
+                L[b, h, r0:r1] = mi + np.log(li)  # logsumexp
     return O, L

@@ -3,7 +3,7 @@
 These pin the identities the pages state and the GPU kernel relies on:
   * the Q-outer / KV-inner loop with a running max and sum reaches the global
     softmax result once every K/V block has been visited (page
-    "Flash Attention V2原理解读", FWD commentary on lines 9-10) - checked by
+    "Flash Attention V2原理解读", commentary on the FWD inner loop) - checked by
     brute force over many tile shapes, ragged lengths and Br != Bc;
   * normalising once at the end equals normalising every step (page
     "flash-attention123和ring-attention", 优化2);
