@@ -97,7 +97,7 @@ const char* fa2_strerror(fa2_status_t s) {
 const char* fa2_last_error(void) { return g_last_error; }
 
 fa2_status_t fa2_launch_shape(int64_t B, int64_t H, int64_t N, int64_t d, fa2_dtype_t dtype,
-                              int64_t* kBlockM, int64_t* num_m_block, int64_t* blocks) {
+                              int64_t* kBlockM, int64_t* num_m_block, int64_t* items) {
   g_last_error[0] = '\0';
   int64_t bm = 0;
   fa2_status_t s = check_shape(B, H, N, d, dtype, &bm);
@@ -105,7 +105,7 @@ fa2_status_t fa2_launch_shape(int64_t B, int64_t H, int64_t N, int64_t d, fa2_dt
   const int64_t nmb = (N + bm - 1) / bm;
   if (kBlockM) *kBlockM = bm;
   if (num_m_block) *num_m_block = nmb;
-  if (blocks) *blocks = nmb * B * H;
+  if (items) *items = nmb * B * H;
   return FA2_OK;
 }
 

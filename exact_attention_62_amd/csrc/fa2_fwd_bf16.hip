@@ -2,8 +2,8 @@
 //
 // The algorithm (pages "FlashAttention学习笔记(2)" and "Flash Attention V2原理解读",
 // forward sections; "flash-attention123和ring-attention", 优化1-优化4):
-//   outer loop: one workgroup per block of kBlockM = 128 query rows, grid over
-//               (query block, batch, head);
+//   outer loop: one work item per block of kBlockM = 128 query rows of one
+//               (batch, head); items are independent;
 //   inner loop: K_j, V_j blocks of BN keys, staged in LDS and shared by the
 //               workgroup's four wavefronts;
 //   per block:  S = scale * Q_i K_j^T on MFMA, online row max / row sum, the
@@ -11,6 +11,14 @@
 //               MFMA, no division by l inside the loop;
 //   after:      O = O / l once, L = m + ln(l); K/V blocks that the causal mask
 //               covers entirely are neither loaded nor computed.
+//
+// Persistent grid.  The page's grid has one thread block per (query block,
+// batch, head).  Here as many workgroups run as fit on the chip at once and
+// each walks a fixed sequence of work items: the items of one XCD are the
+// query blocks of a contiguous range of heads (which read the same K/V and so
+// share that XCD's L2), dealt to its workgroups in a snake order so that heavy
+// and light causal blocks balance.  While the last K/V block of an item is
+// processed, the next item's Q rows and first K/V blocks are already loading.
 //
 // Wavefront layout (the pages' split-Q warp scheme, re-derived for 64-wide
 // wavefronts and 32x32 MFMA tiles): each wavefront owns 32 query rows against
@@ -36,7 +44,14 @@
 // touch every LDS bank once.  V: 128-byte blocks of 4 key rows x 16 dims, so
 // that each 16-lane group of a transposing read (ds_read_b64_tr_b16) reads
 // one contiguous block, the pattern the LDS serves fastest.  Every fragment
-// address is one per-lane base plus a compile-time offset.
+// address is one per-lane base plus a compile-time offset.  The direct loads,
+// and the waits and barriers that order them, are inline assembly, so the
+// compiler does not serialise them against the LDS reads in between.
+//
+// Epilogue.  O and L go straight from registers to global memory through
+// buffer stores whose resource covers only the rows < N: rows past the end
+// are dropped by the hardware, and every wavefront issues the same number of
+// stores, which the next item's first wait counts past.
 //
 // Overlap.  The MFMAs of block j+1's S = K Q^T are issued in the same basic
 // block as block j's softmax (vector ALU: exp2, row max/sum, bf16 packing), so
@@ -50,6 +65,8 @@
 // with fewer rescales of O.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include <stdint.h>
 
 #include <type_traits>
@@ -61,6 +78,7 @@ namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
 typedef __attribute__((ext_vector_type(4))) short s16x4_t;
@@ -76,6 +94,8 @@ static_assert(kBM == kBlockM_bf16, "kBlockM mismatch");
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_inff();
+// Word 3 of a raw buffer resource on this GPU family (stride 0, 32-bit data).
+constexpr int kBufferFlags = 0x00020000;
 constexpr float kTau = 8.0f;  // lazy-rescale threshold, log2 units
 
 // Keys per K/V block and wavefronts per SIMD for each head dimension.
@@ -109,18 +129,51 @@ __host__ __device__ constexpr int lds_off(int r) { return blk<D>(r) * kPiece + s
 __device__ __forceinline__ float halves_max(float x) { return fmaxf(x, __shfl_xor(x, 32, 64)); }
 __device__ __forceinline__ float halves_sum(float x) { return x + __shfl_xor(x, 32, 64); }
 
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+// Direct global -> LDS loads of 16 bytes per lane (lane i fills LDS bytes
+// lds + 16i .. +16), and the waits and barriers that order them.  They are
+// inline assembly on purpose: the compiler treats every LDS read that follows
+// a direct load it knows about as a possible reader of that load and waits for
+// all of them, which would cut the prefetch distance to a fraction of a block.
+// The kernel orders these loads itself (vmcnt waits, then a barrier), and the
+// memory clobbers keep the compiler from moving LDS accesses across them.
+__device__ __forceinline__ void lds_dma(const void* base, uint32_t voff, uint32_t lds) {
+  // address = base (scalar) + voff (per lane)
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               : : "s"(lds), "v"(voff), "s"(base) : "memory", "m0");
+}
+__device__ __forceinline__ void lds_dma(const void* addr, uint32_t lds) {
+  // address = addr (per lane)
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               : : "s"(lds), "v"(addr) : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t lds_addr(const char* p) {
+  return (uint32_t)(uintptr_t)(lds_ptr_t)p;
+}
+// Wait until at most N vector-memory operations of this wavefront are in
+// flight (they complete in issue order).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+// The lane index, recomputed where it is used: values derived from it that
+// only the masked or ragged-tail paths need are then not kept in registers
+// across the whole KV loop.
+__device__ __forceinline__ int fresh_lane() {
+  int l = (int)threadIdx.x;
+  asm volatile("" : "+v"(l));
+  return l & 63;
+}
+// Workgroup barrier after this wavefront's own LDS accesses have completed.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
 }
 
 template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(kThreads, Cfg<D>::kWavesPerSimd)
 fa2_fwd_bf16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
                     const uint16_t* __restrict__ Vg, uint16_t* __restrict__ Og,
-                    float* __restrict__ Lg, int N, int num_m_block, int total_blocks,
+                    float* __restrict__ Lg, int N, int num_m_block, int total_items,
                     float c, float scale_abs, uint32_t qsign, uint32_t qkeep) {
   constexpr int BN = Cfg<D>::BN;
   constexpr int CH = D / 8;                  // 16-byte chunks per key row
@@ -137,6 +190,7 @@ fa2_fwd_bf16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict_
   constexpr int LOADS_V = TBV / 1024 / kWaves;  // direct V loads per thread per block
   constexpr int NSEG = D / 16;               // 16-dim segments per V row
   constexpr int KTSTEP = lds_off<D>(32) - lds_off<D>(0); // 32 keys further in a K block
+  constexpr int NSTORE = DT * 4 + 1;         // O and L stores per wavefront per item
   static_assert(LOADS >= 1 && PIECES % kWaves == 0, "block must split evenly over wavefronts");
   // blk()/slot() place the rows of a K block on exactly 16 pieces (8 for D = 64)
   // of RPP rows each; any other block size would address rows and pieces
@@ -150,6 +204,8 @@ fa2_fwd_bf16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict_
                 "LDS offsets fit the 16-bit instruction offset");
 
   __shared__ __attribute__((aligned(1024))) char smem[2 * TBV + 2 * TB];  // V0 V1 K0 K1
+  char* const Vb0 = smem;
+  char* const Kb0 = smem + 2 * TBV;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -157,107 +213,165 @@ fa2_fwd_bf16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict_
   const int col = lane & 31;  // this lane's query row within the wavefront's 32
   const int half = lane >> 5;
 
-  // Workgroup -> (query block, batch*head).  Consecutive workgroup ids are
-  // dispatched round-robin over the 8 XCDs; remap so that each XCD receives a
-  // contiguous range of logical blocks, i.e. the query blocks of the same few
-  // heads, which read the same K/V and so share that XCD's L2.  With the causal
-  // mask, a head's heaviest (last) query block is issued first.
-  int logical;
-  {
-    const int p = blockIdx.x;
-    const int per = total_blocks / 8, rem = total_blocks % 8;
-    const int x = p % 8, s = p / 8;
-    logical = x * per + (x < rem ? x : rem) + s;
-  }
-  const int bh = logical / num_m_block;
-  const int mi = logical - bh * num_m_block;
-  const int m = CAUSAL ? num_m_block - 1 - mi : mi;
+  // ---- work schedule.  The grid is persistent: each workgroup processes a
+  // sequence of work items (query block, batch*head).  Workgroup ids reach the
+  // 8 XCDs round-robin; XCD x takes a contiguous range of logical items (the
+  // query blocks of the same few heads, which read the same K/V and so share
+  // that XCD's L2), ordered head by head with a head's heaviest causal query
+  // block first.  The workgroups of an XCD walk that range in groups, in a
+  // snake order (group k: slot s takes position s, or P-1-s when k is odd), so
+  // that heavy and light causal blocks alternate per workgroup.
+  // (With fewer than 8 workgroups the ranges are split over that many.)
+  const int nx = gridDim.x < 8 ? (int)gridDim.x : 8;
+  const int xcd = blockIdx.x % nx;
+  const int lslot = blockIdx.x / nx;
+  const int P = ((int)gridDim.x - xcd + nx - 1) / nx;  // workgroups on this XCD
+  const int per = total_items / nx, rem = total_items % nx;
+  const int x_base = xcd * per + (xcd < rem ? xcd : rem);
+  const int x_items = per + (xcd < rem ? 1 : 0);
+  auto logical_of = [&](int k) -> int {  // the k-th item of this workgroup, or -1
+    const int pos = k * P + ((k & 1) ? P - 1 - lslot : lslot);
+    return pos < x_items ? x_base + pos : -1;
+  };
 
-  const size_t slice = (size_t)bh * (size_t)N * D;
-  const uint16_t* Qh = Qg + slice;
-  const uint16_t* Kh = Kg + slice;
-  const uint16_t* Vh = Vg + slice;
-  uint16_t* Oh = Og + slice;
-  float* Lh = Lg + (size_t)bh * N;
+  // ---- per-item state
+  int bh = 0, m = 0, q0 = 0, qrow = 0, j_end = 0, j_mask = 0;
+  const uint16_t *Qh = Qg, *Kh = Kg, *Vh = Vg;
+  // O and L of the item's query block as buffer resources whose size covers
+  // only the rows < N: the hardware drops stores to rows past the end, so
+  // every wavefront issues the same number of stores for every item.
+  __amdgpu_buffer_rsrc_t o_rsrc, l_rsrc;
+  auto decode = [&](int logical, int& bh_, int& m_) __attribute__((always_inline)) {
+    bh_ = logical / num_m_block;
+    const int mi = logical - bh_ * num_m_block;
+    m_ = CAUSAL ? num_m_block - 1 - mi : mi;
+  };
+  auto blocks_of = [&](int m_) __attribute__((always_inline)) -> int {
+    if (CAUSAL) return (min(N, (m_ + 1) * kBM) - 1) / BN + 1;
+    return (N + BN - 1) / BN;
+  };
+  auto set_item = [&](int logical) __attribute__((always_inline)) {
+    decode(logical, bh, m);
+    const size_t slice = (size_t)bh * (size_t)N * D;
+    Qh = Qg + slice;
+    Kh = Kg + slice;
+    Vh = Vg + slice;
+    const int rows = min(kBM, N - m * kBM);
+    o_rsrc = __builtin_amdgcn_make_buffer_rsrc(Og + slice + (size_t)m * kBM * D, (short)0,
+                                               rows * ROWB, kBufferFlags);
+    l_rsrc = __builtin_amdgcn_make_buffer_rsrc(Lg + (size_t)bh * N + (size_t)m * kBM, (short)0,
+                                               rows * 4, kBufferFlags);
+    q0 = m * kBM + wave * 32;  // first query row of this wavefront
+    qrow = q0 + col;
+    j_end = blocks_of(m);
+    // Blocks before j_mask need no mask for this wavefront (every key visible
+    // to every one of its rows).
+    j_mask = CAUSAL ? min((q0 + 1) / BN, N / BN) : N / BN;
+  };
 
-  const int q0 = m * kBM + wave * 32;  // first query row of this wavefront
-  const int qrow = q0 + col;
-
-  // Q fragments (the B operand of S^T = K Q^T), kept in registers for the whole
-  // loop.  A negative scale flips Q's sign (exact); a zero scale zeroes Q, which
-  // gives the same all-zero logits.
+  // Q fragments (the B operand of S^T = K Q^T), kept in registers for an item.
+  // A negative scale flips Q's sign (exact); a zero scale zeroes Q, which gives
+  // the same all-zero logits.
   bf16x8_t qf[KS];
+  auto load_q = [&](const uint16_t* qh, int row) __attribute__((always_inline)) {
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    u32x4_t t = {0u, 0u, 0u, 0u};
-    if (qrow < N) t = *(const u32x4_t*)(Qh + (size_t)qrow * D + ks * 16 + 8 * half);
-    t = (t & qkeep) ^ qsign;
-    qf[ks] = __builtin_bit_cast(bf16x8_t, t);
-  }
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4_t t = {0u, 0u, 0u, 0u};
+      if (row < N) t = *(const u32x4_t*)(qh + (size_t)row * D + ks * 16 + 8 * half);
+      qf[ks] = __builtin_bit_cast(bf16x8_t, t);
+    }
+  };
+  // After the sign/zero fix, the fragments pass through an empty asm
+  // statement: the compiler waits for the Q loads there, once per item, and
+  // from then on sees register values with no load pending (it cannot see the
+  // direct LDS loads, so a pending Q load inside the KV loop would make it
+  // wait for every load in flight).
+  auto fix_q = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4_t t = (__builtin_bit_cast(u32x4_t, qf[ks]) & qkeep) ^ qsign;
+      asm volatile("" : "+v"(t));
+      qf[ks] = __builtin_bit_cast(bf16x8_t, t);
+    }
+  };
 
-  // ---- global -> LDS staging map: load i of this thread fills piece
+  // ---- global -> LDS staging.  K: load i of this thread fills piece
   // b = wave*LOADS + i, whose lane L writes bytes 16L.. of the piece: row slot
   // L / CH, 16-byte chunk L % CH of the key row r with blk(r) = b and
   // slot(r) = L / CH.  That row splits into a per-lane part and a per-piece
   // (wave-uniform) part 4*(b&3) + (b>>2).
-  int lane_row, lane_col;
-  {
-    const int sl = lane / CH;
-    lane_row = D == 64 ? 16 * (sl >> 1) + 2 * (sl & 1) : 16 * sl;
-    lane_col = (lane % CH) * 8;
-  }
-  const uint32_t lane_bytes = (uint32_t)(lane_row * D + lane_col) * 2;
-  auto issue_block = [&](const uint16_t* head, int k0, char* buf) {
+  auto k_lane_row = [](int l) { const int sl = l / CH; return D == 64 ? 16 * (sl >> 1) + 2 * (sl & 1) : 16 * sl; };
+  auto k_lane_col = [](int l) { return (l % CH) * 8; };
+  const uint32_t lane_bytes = (uint32_t)(k_lane_row(lane) * D + k_lane_col(lane)) * 2;
+  // k0 goes through an empty asm statement: for the constant first blocks of an
+  // item the compiler would otherwise precompute the clamped tail addresses
+  // once, outside the item loop, and keep them in (spilled) registers.
+  auto issue_k = [&](const uint16_t* head, int k0, char* buf) __attribute__((always_inline)) {
+    asm volatile("" : "+s"(k0));
     if (k0 + BN <= N) {
       // Scalar base (the piece's first row) plus a constant 32-bit per-lane offset.
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
         const int b = wave * LOADS + i;
-        const char* base = (const char*)(head + (size_t)(k0 + 4 * (b & 3) + (b >> 2)) * D);
-        __builtin_amdgcn_global_load_lds((global_ptr_t)(base + lane_bytes),
-                                         (lds_ptr_t)(buf + b * kPiece), 16, 0, 0);
+        lds_dma(head + (size_t)(k0 + 4 * (b & 3) + (b >> 2)) * D, lane_bytes,
+                lds_addr(buf + b * kPiece));
       }
     } else {
       // Ragged last block: rows past N are clamped to row N-1 (their keys are masked).
+      const int tl = fresh_lane();
+      const int lane_row = k_lane_row(tl), lane_col = k_lane_col(tl);
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
         const int b = wave * LOADS + i;
         const int r = min(k0 + 4 * (b & 3) + (b >> 2) + lane_row, N - 1);
-        __builtin_amdgcn_global_load_lds((global_ptr_t)(head + (size_t)r * D + lane_col),
-                                         (lds_ptr_t)(buf + b * kPiece), 16, 0, 0);
+        lds_dma(head + (size_t)r * D + lane_col, lds_addr(buf + b * kPiece));
       }
     }
   };
-
-  // V staging: load i of this thread fills 1 KB chunk n = wave*LOADS_V + i,
-  // whose lane L writes 16 bytes: 128-byte block bk = 8n + L/8 (row group
-  // bk / NSEG, dim segment bk % NSEG), row (L%8)/2 of that group, dims
-  // 8*(L%2) ..+8 of that segment.  The lane's share of the key row and dims is
-  // the same for every n; n only adds a wave-uniform row / dim offset.
-  int vrow_l, vdim_l;
-  {
-    const int x = lane / 8;
-    if constexpr (NSEG <= 8) {
-      vrow_l = 4 * (x / NSEG) + (lane % 8) / 2;
-      vdim_l = 16 * (x % NSEG) + 8 * (lane % 2);
-    } else {
-      vrow_l = (lane % 8) / 2;
-      vdim_l = 16 * x + 8 * (lane % 2);
-    }
-  }
-  const uint32_t vlane = (uint32_t)(vrow_l * D + vdim_l) * 2;
-  auto issue_v = [&](int k0, char* buf) __attribute__((always_inline)) {
-    const char* base = (const char*)(Vh + (size_t)k0 * D);
-    const bool tail = k0 + BN > N;  // rows past N are clamped to row N-1 (P~ is 0 there)
+  // V: load i of this thread fills 1 KB chunk n = wave*LOADS_V + i, whose lane
+  // L writes 16 bytes: 128-byte block bk = 8n + L/8 (row group bk / NSEG, dim
+  // segment bk % NSEG), row (L%8)/2 of that group, dims 8*(L%2) ..+8 of that
+  // segment.  The lane's share of the key row and dims is the same for every
+  // n; n only adds a wave-uniform row / dim offset.
+  auto v_lane_row = [](int l) { return NSEG <= 8 ? 4 * ((l / 8) / NSEG) + (l % 8) / 2 : (l % 8) / 2; };
+  auto v_lane_dim = [](int l) {
+    return NSEG <= 8 ? 16 * ((l / 8) % NSEG) + 8 * (l % 2) : 16 * (l / 8) + 8 * (l % 2);
+  };
+  const uint32_t vlane = (uint32_t)(v_lane_row(lane) * D + v_lane_dim(lane)) * 2;
+  auto issue_v = [&](const uint16_t* head, int k0, char* buf) __attribute__((always_inline)) {
+    asm volatile("" : "+s"(k0));
+    const char* base = (const char*)(head + (size_t)k0 * D);
+    if (k0 + BN <= N) {
 #pragma unroll
-    for (int i = 0; i < LOADS_V; ++i) {
-      const int n = wave * LOADS_V + i;
-      const int row_u = NSEG <= 8 ? 4 * n * (8 / NSEG) : 4 * (n / 2);
-      const int dim_u = NSEG <= 8 ? 0 : 128 * (n % 2);
-      const char* src = base + (row_u * D + dim_u) * 2 + vlane;
-      if (tail) src += (ptrdiff_t)(min(k0 + row_u + vrow_l, N - 1) - (k0 + row_u + vrow_l)) * ROWB;
-      __builtin_amdgcn_global_load_lds((global_ptr_t)src, (lds_ptr_t)(buf + n * 1024), 16, 0, 0);
+      for (int i = 0; i < LOADS_V; ++i) {
+        const int n = wave * LOADS_V + i;
+        const int row_u = NSEG <= 8 ? 4 * n * (8 / NSEG) : 4 * (n / 2);
+        const int dim_u = NSEG <= 8 ? 0 : 128 * (n % 2);
+        lds_dma(base + (row_u * D + dim_u) * 2, vlane, lds_addr(buf + n * 1024));
+      }
+    } else {
+      // Ragged last block: rows past N are clamped to row N-1 (P~ is 0 there).
+      const int tl = fresh_lane();
+      const int vrow_l = v_lane_row(tl), vdim_l = v_lane_dim(tl);
+#pragma unroll
+      for (int i = 0; i < LOADS_V; ++i) {
+        const int n = wave * LOADS_V + i;
+        const int row_u = NSEG <= 8 ? 4 * n * (8 / NSEG) : 4 * (n / 2);
+        const int dim_u = NSEG <= 8 ? 0 : 128 * (n % 2);
+        const int r = min(k0 + row_u + vrow_l, N - 1);
+        lds_dma(head + (size_t)r * D + dim_u + vdim_l, lds_addr(buf + n * 1024));
+      }
     }
+  };
+  // The first blocks of an item: Q rows, K_0 and V_0, and K_1 if there is one.
+  // g is the running block count of this workgroup: block g of the sequence
+  // uses K and V buffers g & 1.
+  auto issue_item_start = [&](const uint16_t* qh, const uint16_t* kh, const uint16_t* vh, int row,
+                              int blocks, int g) __attribute__((always_inline)) {
+    load_q(qh, row);
+    issue_k(kh, 0, Kb0 + (g & 1) * TB);
+    issue_v(vh, 0, Vb0 + (g & 1) * TBV);
+    if (blocks > 1) issue_k(kh, BN, Kb0 + ((g + 1) & 1) * TB);
   };
 
   // ---- LDS fragment addresses (bytes within a block buffer).
@@ -268,28 +382,19 @@ fa2_fwd_bf16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict_
   // (d0 + 4c ..) of key row (kbase + r); the hardware hands lane t of the
   // group the 4 keys kbase..kbase+3 of dim d0 + t.  kbase = 16u + 4*half (the
   // first 4 slots of the operand) or 16u + 8 + 4*half (the last 4), matching
-  // the keys 8*(r/4) + 4*half + r%4 that a lane's S^T accumulators hold.
-  // With the V layout, the 16 lanes of a group read one contiguous 128-byte
-  // block: lane i at byte 8i of the block of rows kbase.. and dims d0..d0+15.
-  const uint32_t vaddr = (uint32_t)(((lane >> 4) >> 1) * 4 * ROWB + ((lane >> 4) & 1) * 128 + 8 * (lane & 15));
+  // the keys 8*(r/4) + 4*half + r%4 that a lane's S^T accumulators hold.  With
+  // the V layout, the 16 lanes of a group read one contiguous 128-byte block:
+  // lane i at byte 8i of the block of rows kbase.. and dims d0..d0+15.
+  const uint32_t vaddr =
+      (uint32_t)(((lane >> 4) >> 1) * 4 * ROWB + ((lane >> 4) & 1) * 128 + 8 * (lane & 15));
 
   f32x16_t o[DT];
-#pragma unroll
-  for (int t = 0; t < DT; ++t) o[t] = f32x16_t{};
   float m_ref = kNegInf;  // reference max of the (sign-adjusted) raw logits
   float l_part = 0.f;     // running sum over this lane's half of the keys
+  int g0 = 0;             // running block count at the current item's block 0
+  int k_item = 0;         // index of the current item in this workgroup's sequence
 
-  const int n_blocks = (N + BN - 1) / BN;
-  int j_end = n_blocks;
-  if (CAUSAL) {
-    const int last = min(N, (m + 1) * kBM) - 1;
-    j_end = last / BN + 1;
-  }
-
-  char* const Vb0 = smem;
-  char* const Kb0 = smem + 2 * TBV;
-
-  auto compute_S = [&](const char* kb, f32x16_t (&S)[KT]) {
+  auto compute_S = [&](const char* kb, f32x16_t (&S)[KT]) __attribute__((always_inline)) {
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) {
       S[kt] = f32x16_t{};
@@ -301,19 +406,28 @@ fa2_fwd_bf16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict_
     }
   };
 
-  // Softmax of block j (pseudo-code line 9) and the O update (line 10);
+  // Block j's step of the online softmax (new running max, rescaled running
+  // sum, unnormalised probabilities) and the rescaled O update;
   // `during` issues independent MFMA work (the next block's S) alongside.
-  auto consume = [&](auto masked_tag, int j, f32x16_t(&S)[KT], auto&& during) {
+  auto consume = [&](auto masked_tag, int j, f32x16_t(&S)[KT],
+                     auto&& during) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked_tag)::value;
     const int k0 = j * BN;
     if constexpr (MASKED) {
+      // key = k0 + cr + 4*half with cr = kt*32 + 8*(r/4) + r%4 (a constant):
+      // it is hidden when cr + (k0 - q0) > col - 4*half (after the lane's query
+      // row) or cr + (k0 - N) >= -4*half (past the sequence), i.e. when cr
+      // exceeds one per-lane threshold.
+      const int ml = fresh_lane();
+      const int mh = -4 * (ml >> 5);
+      int th = mh - (k0 - N) - 1;
+      if (CAUSAL) th = min(th, (ml & 31) + mh - (k0 - q0));
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = k0 + kt * 32 + 8 * (r / 4) + 4 * half + (r % 4);
-          const bool hide = (CAUSAL && key > qrow) || key >= N;
-          S[kt][r] = hide ? kNegInf : S[kt][r];
+          const int cr = kt * 32 + 8 * (r / 4) + (r % 4);
+          S[kt][r] = cr > th ? kNegInf : S[kt][r];
         }
     }
     during();
@@ -323,14 +437,11 @@ fa2_fwd_bf16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict_
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[kt][r]);
     mx = halves_max(mx);
-    float alpha = 1.f;
-    if (m_ref == kNegInf) {  // first block with a visible key: O and l are still zero
-      m_ref = mx;
-      alpha = 0.f;
-    } else if (c * (mx - m_ref) > kTau) {
-      alpha = __builtin_amdgcn_exp2f(c * (m_ref - mx));
-      m_ref = mx;
-    }
+    // The first block with a visible key always moves the reference (alpha =
+    // exp2(-inf) = 0 then: O and l are still zero).
+    const bool move = m_ref == kNegInf || c * (mx - m_ref) > kTau;
+    const float alpha = move ? __builtin_amdgcn_exp2f(c * (m_ref - mx)) : 1.f;
+    m_ref = move ? mx : m_ref;
     const float mc = m_ref == kNegInf ? 0.f : c * m_ref;
     float ls = 0.f;
     bf16x8_t pb[U];
@@ -347,7 +458,7 @@ fa2_fwd_bf16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict_
 #pragma unroll
       for (int t = 0; t < DT; ++t) o[t] *= alpha;
     }
-    const char* vb = Vb0 + (j & 1) * TBV + vaddr;
+    const char* vb = Vb0 + ((g0 + j) & 1) * TBV + vaddr;
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
@@ -362,117 +473,165 @@ fa2_fwd_bf16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict_
       }
   };
 
-  // ---- prologue: K0, V0 and K1 in flight; S for block 0.
-  issue_block(Kh, 0, Kb0);
-  issue_v(0, Vb0);
-  if (j_end > 1) {
-    issue_block(Kh, BN, Kb0 + TB);
-    wait_vmcnt<LOADS_V + LOADS>();
-  } else {
-    wait_vmcnt<LOADS_V>();
-  }
-  __syncthreads();
-  f32x16_t S_cur[KT];
-  compute_S(Kb0, S_cur);
-
   // One barrier per block: block j's V and block j+1's K have landed in LDS,
   // and every wavefront is done with the buffers of block j-1, which the loads
   // for blocks j+2 (K) and j+1 (V) issued right after reuse.
-  auto advance = [&](int j) {
-    wait_vmcnt<0>();
-    __syncthreads();
-    if (j + 2 < j_end) issue_block(Kh, (j + 2) * BN, Kb0 + (j & 1) * TB);
-    if (j + 1 < j_end) issue_v((j + 1) * BN, Vb0 + ((j + 1) & 1) * TBV);
+  auto advance = [&](int j) __attribute__((always_inline)) {
+    // At an item's first block the previous item's O and L stores, issued
+    // last, need not have completed.
+    if (j == 0 && k_item > 0) wait_vmcnt<NSTORE>();
+    else wait_vmcnt<0>();
+    lds_barrier();
+    if (j + 2 < j_end) issue_k(Kh, (j + 2) * BN, Kb0 + ((g0 + j) & 1) * TB);
+    if (j + 1 < j_end) issue_v(Vh, (j + 1) * BN, Vb0 + ((g0 + j + 1) & 1) * TBV);
   };
-  // Blocks before j_mask need no mask for this wavefront (all keys visible to
-  // all of its rows); the loop runs in three stretches so that each loop body
-  // holds a single variant: unmasked, masked (causal diagonal, ragged tail),
-  // and the last block, which has no successor to overlap with.
-  const int j_mask = CAUSAL ? min((q0 + 1) / BN, N / BN) : N / BN;
-  const int j_unmasked = min(j_mask, j_end - 1);  // unmasked blocks that have a successor
-  f32x16_t SB[KT];
-  int j = 0;
-  // Unrolled by two so that the S registers alternate between S_cur and SB
-  // instead of being copied every block.
-  for (; j + 2 <= j_unmasked; j += 2) {
-    advance(j);
-    consume(std::false_type{}, j, S_cur, [&]() { compute_S(Kb0 + ((j + 1) & 1) * TB, SB); });
-    advance(j + 1);
-    consume(std::false_type{}, j + 1, SB, [&]() { compute_S(Kb0 + (j & 1) * TB, S_cur); });
-  }
-  if (j < j_unmasked) {
-    advance(j);
-    consume(std::false_type{}, j, S_cur, [&]() { compute_S(Kb0 + ((j + 1) & 1) * TB, SB); });
-#pragma unroll
-    for (int kt = 0; kt < KT; ++kt) S_cur[kt] = SB[kt];
-    ++j;
-  }
-  for (; j + 2 < j_end; j += 2) {
-    advance(j);
-    consume(std::true_type{}, j, S_cur, [&]() { compute_S(Kb0 + ((j + 1) & 1) * TB, SB); });
-    advance(j + 1);
-    consume(std::true_type{}, j + 1, SB, [&]() { compute_S(Kb0 + (j & 1) * TB, S_cur); });
-  }
-  if (j + 1 < j_end) {
-    advance(j);
-    consume(std::true_type{}, j, S_cur, [&]() { compute_S(Kb0 + ((j + 1) & 1) * TB, SB); });
-#pragma unroll
-    for (int kt = 0; kt < KT; ++kt) S_cur[kt] = SB[kt];
-    ++j;
-  }
-  advance(j);
-  if (j < j_mask) consume(std::false_type{}, j, S_cur, [] {});
-  else consume(std::true_type{}, j, S_cur, [] {});
 
-  // ---- epilogue (lines 12-13): O = O / l once, L = m + ln(l).
-  // The wavefront's 32 output rows are one contiguous stretch of O.  They go
-  // through LDS (16-byte chunks XOR-swizzled by row against bank conflicts) so
-  // that the global stores are whole rows, 16 bytes per lane.  The K buffers
-  // are free once the last barrier has passed (the last block reads only V);
-  // with D = 256 the staging needs all of LDS and waits for the last V reads.
-  const float l_tot = halves_sum(l_part);
-  const float inv = 1.f / l_tot;
-  constexpr int CHK = D / 8;                    // 16-byte chunks per output row
-  constexpr int SWZ = CHK < 16 ? CHK - 1 : 15;  // swizzle mask
-  constexpr int STAGE = 32 * ROWB;              // bytes per wavefront
-  constexpr bool IN_K = kWaves * STAGE <= 2 * TB;
-  static_assert(kWaves * STAGE <= 2 * TBV + 2 * TB, "staging fits in LDS");
-  if constexpr (!IN_K) __syncthreads();
-  char* const stage = (IN_K ? Kb0 : smem) + wave * STAGE;
-#pragma unroll
-  for (int t = 0; t < DT; ++t)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      bf16x4_t w;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) w[r] = (__bf16)(o[t][g * 4 + r] * inv);
-      const int d = t * 32 + 8 * g + 4 * half;
-      *(bf16x4_t*)(stage + col * ROWB + (((d >> 3) ^ (col & SWZ)) << 4) + (d & 7) * 2) = w;
+  // ---- item prologue: wait for Q and K_0, then S for block 0.  Vector
+  // memory operations complete in issue order, and V_0 and K_1 (and, after
+  // the first item, the previous item's O and L stores) were issued after
+  // K_0, so the wait leaves that many operations in flight; then a barrier.
+  // The first item's prologue is separate from the later items' (at the end
+  // of the loop), so that the compiler's own wait for the Q registers counts
+  // the stores on the later path instead of draining everything.
+  f32x16_t S_cur[KT];
+  auto prologue = [&](auto later_tag) __attribute__((always_inline)) {
+    fix_q();
+    if constexpr (decltype(later_tag)::value) {
+      if (j_end > 1) wait_vmcnt<LOADS_V + LOADS + NSTORE>();
+      else wait_vmcnt<LOADS_V + NSTORE>();
+    } else {
+      if (j_end > 1) wait_vmcnt<LOADS_V + LOADS>();
+      else wait_vmcnt<LOADS_V>();
     }
-  __builtin_amdgcn_s_waitcnt((15 << 0) | (3 << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0)
-  __builtin_amdgcn_wave_barrier();
-  constexpr int RPI = 64 / CHK;  // rows per store instruction
+    lds_barrier();
 #pragma unroll
-  for (int i = 0; i < 32 / RPI; ++i) {
-    const int row = i * RPI + lane / CHK;
-    const int ch = lane % CHK;
-    const u32x4_t v = *(const u32x4_t*)(stage + row * ROWB + ((ch ^ (row & SWZ)) << 4));
-    if (q0 + row < N) *(u32x4_t*)(Oh + (size_t)(q0 + row) * D + ch * 8) = v;
+    for (int t = 0; t < DT; ++t) o[t] = f32x16_t{};
+    m_ref = kNegInf;
+    l_part = 0.f;
+    compute_S(Kb0 + (g0 & 1) * TB, S_cur);
+  };
+
+  int logical = logical_of(0);
+  if (logical < 0) return;  // uniform for the workgroup
+  set_item(logical);
+  issue_item_start(Qh, Kh, Vh, qrow, j_end, 0);
+  prologue(std::false_type{});
+
+  for (;;) {
+    const int j_unmasked = min(j_mask, j_end - 1);  // unmasked blocks that have a successor
+    f32x16_t SB[KT];
+    int j = 0;
+    // Unrolled by two so that the S registers alternate between S_cur and SB
+    // instead of being copied every block.
+    for (; j + 2 <= j_unmasked; j += 2) {
+      advance(j);
+      consume(std::false_type{}, j, S_cur,
+              [&]() { compute_S(Kb0 + ((g0 + j + 1) & 1) * TB, SB); });
+      advance(j + 1);
+      consume(std::false_type{}, j + 1, SB,
+              [&]() { compute_S(Kb0 + ((g0 + j) & 1) * TB, S_cur); });
+    }
+    if (j < j_unmasked) {
+      advance(j);
+      consume(std::false_type{}, j, S_cur,
+              [&]() { compute_S(Kb0 + ((g0 + j + 1) & 1) * TB, SB); });
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) S_cur[kt] = SB[kt];
+      ++j;
+    }
+    for (; j + 2 < j_end; j += 2) {
+      advance(j);
+      consume(std::true_type{}, j, S_cur,
+              [&]() { compute_S(Kb0 + ((g0 + j + 1) & 1) * TB, SB); });
+      advance(j + 1);
+      consume(std::true_type{}, j + 1, SB,
+              [&]() { compute_S(Kb0 + ((g0 + j) & 1) * TB, S_cur); });
+    }
+    if (j + 1 < j_end) {
+      advance(j);
+      consume(std::true_type{}, j, S_cur,
+              [&]() { compute_S(Kb0 + ((g0 + j + 1) & 1) * TB, SB); });
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) S_cur[kt] = SB[kt];
+      ++j;
+    }
+    // Last block of the item.  Both K buffers and the other V buffer are free
+    // now, and so are the Q registers: the next item's Q, K_0, V_0, K_1 go out
+    // here and overlap this block's softmax, its PV product and the O stores.
+    advance(j);
+    const int next = logical_of(k_item + 1);
+    if (next >= 0) {
+      int nbh, nm;
+      decode(next, nbh, nm);
+      const size_t nslice = (size_t)nbh * (size_t)N * D;
+      issue_item_start(Qg + nslice, Kg + nslice, Vg + nslice, nm * kBM + wave * 32 + col,
+                       blocks_of(nm), g0 + j_end);
+    }
+    // Always the masked form: one copy of the code, and for an unmasked block
+    // the threshold test hides nothing.
+    consume(std::true_type{}, j, S_cur, [] {});
+
+    // ---- item epilogue, after the KV loop: O = O / l once, L = m + ln(l).
+    const float l_tot = halves_sum(l_part);
+    const float inv = 1.f / l_tot;
+    const int orow = (wave * 32 + col) * ROWB;  // byte offset of this lane's row in the block
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bf16x4_t w;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) w[r] = (__bf16)(o[t][g * 4 + r] * inv);
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, w), o_rsrc,
+                                              orow + (t * 32 + 8 * g + 4 * half) * 2, 0, 0);
+      }
+    // Both halves of a row hold the same l and m: they store the same L.
+    __builtin_amdgcn_raw_buffer_store_b32(
+        __builtin_bit_cast(uint32_t,
+                           __builtin_fmaf(__builtin_amdgcn_logf(l_tot), kLn2, scale_abs * m_ref)),
+        l_rsrc, (wave * 32 + col) * 4, 0, 0);
+    if (next < 0) break;
+    g0 += j_end;
+    ++k_item;
+    set_item(next);
+    prologue(std::true_type{});
   }
-  if (qrow < N && half == 0)
-    Lh[qrow] = __builtin_fmaf(__builtin_amdgcn_logf(l_tot), kLn2, scale_abs * m_ref);
+}
+
+// Compute units of the current device, queried once per device.
+hipError_t cu_count(int* cus) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cache[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < kMaxDevices && (*cus = cache[dev].load(std::memory_order_relaxed)) > 0)
+    return hipSuccess;
+  e = hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  if (*cus < 1) *cus = 1;
+  if (dev >= 0 && dev < kMaxDevices) cache[dev].store(*cus, std::memory_order_relaxed);
+  return hipSuccess;
 }
 
 template <int D, bool CAUSAL>
 hipError_t launch(const FwdArgs& a) {
   const int total = a.num_m_block * a.BH;
+  // Persistent grid: as many workgroups as fit on the chip at once (a 4-wave
+  // workgroup puts one wave on each SIMD of a CU, so kWavesPerSimd workgroups
+  // per CU), each walking its share of the work items.
+  int cus = 0;
+  const hipError_t e = cu_count(&cus);
+  if (e != hipSuccess) return e;
+  const int resident = Cfg<D>::kWavesPerSimd * cus;
+  const int grid = total < resident ? total : resident;
   // The kernel works with c = |scale| * log2(e) > 0: a negative scale flips the
   // sign of Q and a zero scale zeroes Q (both exact), with |scale| = 1 then.
   const bool zero = a.scale == 0.f;
   const float sa = zero ? 1.f : (a.scale < 0.f ? -a.scale : a.scale);
   const uint32_t qsign = a.scale < 0.f ? 0x80008000u : 0u;
   const uint32_t qkeep = zero ? 0u : 0xFFFFFFFFu;
-  hipLaunchKernelGGL((fa2_fwd_bf16_kernel<D, CAUSAL>), dim3(total), dim3(kThreads), 0, a.stream,
+  hipLaunchKernelGGL((fa2_fwd_bf16_kernel<D, CAUSAL>), dim3(grid), dim3(kThreads), 0, a.stream,
                      (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V,
                      (uint16_t*)a.O, a.L, a.N, a.num_m_block, total, sa * kLog2e, sa, qsign,
                      qkeep);

@@ -83,7 +83,7 @@ def _check(status: int) -> None:
 
 
 def fa2_launch_shape(B: int, H: int, N: int, d: int, dtype: torch.dtype = torch.bfloat16):
-    """(kBlockM, num_m_block, blocks) of the grid fa2_fwd launches for this problem."""
+    """(kBlockM, num_m_block, items): the work decomposition fa2_fwd uses (one item per query block of one (batch, head))."""
     lib = load_library()
     out = [ctypes.c_int64(0) for _ in range(3)]
     _check(lib.fa2_launch_shape(B, H, N, d, _DTYPES.get(dtype, -1), *(ctypes.byref(o) for o in out)))

@@ -80,16 +80,18 @@ fa2_status_t fa2_fwd(const void* Q, const void* K, const void* V, void* O, float
 /*
  * fa2_launch_shape - the work decomposition fa2_fwd uses, as a host-only query.
  *
- * The grid has one workgroup per (query block, batch, head), num_m_block =
- * ceil(N / kBlockM) query blocks per head (page "FlashAttention学习笔记(2)",
- * section "V2中的thread blocks排布"; "Flash Attention V2原理解读", the
- * thread-block grid section).  Writes kBlockM, num_m_block and the total
- * workgroup count B*H*num_m_block through the non-NULL out pointers.  Makes
- * no HIP call.  Returns FA2_EINVAL / FA2_ENOTSUP for arguments fa2_fwd would
- * reject on those grounds.
+ * The work is one independent item per (query block, batch, head), with
+ * num_m_block = ceil(N / kBlockM) query blocks per head: the pages' thread
+ * blocks (page "FlashAttention学习笔记(2)", section "V2中的thread blocks排布";
+ * "Flash Attention V2原理解读", the thread-block grid section).  Writes
+ * kBlockM, num_m_block and the item count B*H*num_m_block through the
+ * non-NULL out pointers.  The bf16 kernel runs the items on a persistent grid
+ * of min(items, resident workgroups) workgroups; the fp32 kernel launches one
+ * workgroup per item.  Makes no HIP call.  Returns FA2_EINVAL / FA2_ENOTSUP
+ * for arguments fa2_fwd would reject on those grounds.
  */
 fa2_status_t fa2_launch_shape(int64_t B, int64_t H, int64_t N, int64_t d, fa2_dtype_t dtype,
-                              int64_t* kBlockM, int64_t* num_m_block, int64_t* blocks);
+                              int64_t* kBlockM, int64_t* num_m_block, int64_t* items);
 
 /* fa2_strerror - static description of a status code (never NULL). */
 const char* fa2_strerror(fa2_status_t status);
