@@ -5,6 +5,8 @@ benchmark's CPU-baseline leg, never by the library.  It shares no code with
 the HIP path and never imports it.
 """
 from .attention import attention_fp64, attention_rows_fp64, scaled_logits_fp64
+from .splitkv import (attention_keyrange_fp64, combine_fp64, num_splits_heuristic, split_ranges,
+                      utilisation)
 from .tiled import causal_block_end, fa2_forward_tiled_fp64
 
 __all__ = [
@@ -13,4 +15,9 @@ __all__ = [
     "scaled_logits_fp64",
     "fa2_forward_tiled_fp64",
     "causal_block_end",
+    "attention_keyrange_fp64",
+    "combine_fp64",
+    "num_splits_heuristic",
+    "split_ranges",
+    "utilisation",
 ]
