@@ -109,36 +109,43 @@ fa2_status_t fa2_launch_shape(int64_t B, int64_t H, int64_t N, int64_t d, fa2_dt
   return FA2_OK;
 }
 
-fa2_status_t fa2_fwd(const void* Q, const void* K, const void* V, void* O, float* L, int64_t B,
+}  // extern "C"
+
+namespace {
+
+// Pointer checks shared by the forward entry points: non-NULL, aligned, outputs
+// disjoint from everything else (extra[i] are further buffers, e.g. a
+// workspace, treated as outputs), then device residency of every range.
+// Fills the launch arguments.  Returns FA2_OK with a.BH == 0 for an empty
+// problem (nothing to launch).
+fa2_status_t prepare(const void* Q, const void* K, const void* V, void* O, float* L, int64_t B,
                      int64_t H, int64_t N, int64_t d, int causal, float scale, fa2_dtype_t dtype,
-                     void* stream) {
-  g_last_error[0] = '\0';
+                     void* stream, const void* ws, int64_t ws_bytes, fa2::FwdArgs* a) {
   int64_t bm = 0;
   fa2_status_t s = check_shape(B, H, N, d, dtype, &bm);
   if (s != FA2_OK) return s;
   if (causal != 0 && causal != 1) return fail(FA2_EINVAL, "causal=%d must be 0 or 1", causal);
   if (!std::isfinite(scale)) return fail(FA2_EINVAL, "scale must be finite");
+  a->BH = 0;
   if (B * H * N == 0) return FA2_OK;  // empty problem: nothing to read or write
 
   const int64_t tensor_bytes = B * H * N * d * elem_size(dtype);
   const int64_t l_bytes = B * H * N * 4;
-  const void* ptrs[5] = {Q, K, V, O, L};
-  const char* names[5] = {"Q", "K", "V", "O", "L"};
-  for (int i = 0; i < 5; ++i) {
+  const int n = ws ? 6 : 5;
+  const void* ptrs[6] = {Q, K, V, O, L, ws};
+  const int64_t sizes[6] = {tensor_bytes, tensor_bytes, tensor_bytes, tensor_bytes, l_bytes,
+                            ws_bytes};
+  const char* names[6] = {"Q", "K", "V", "O", "L", "workspace"};
+  for (int i = 0; i < n; ++i) {
     if (ptrs[i] == nullptr) return fail(FA2_EINVAL, "%s is NULL", names[i]);
     const uintptr_t align = i == 4 ? 4 : 16;
     if (reinterpret_cast<uintptr_t>(ptrs[i]) % align != 0)
       return fail(FA2_EINVAL, "%s=%p is not %d-byte aligned", names[i], ptrs[i], (int)align);
   }
-  for (int o = 3; o < 5; ++o) {
-    const int64_t no = o == 4 ? l_bytes : tensor_bytes;
-    for (int i = 0; i < 5; ++i) {
-      if (i == o) continue;
-      const int64_t ni = i == 4 ? l_bytes : tensor_bytes;
-      if (overlaps(ptrs[o], no, ptrs[i], ni))
-        return fail(FA2_EINVAL, "output %s overlaps %s", names[o], names[i]);
-    }
-  }
+  for (int o = 3; o < n; ++o)
+    for (int i = 0; i < n; ++i)
+      if (i != o && overlaps(ptrs[o], sizes[o], ptrs[i], sizes[i]))
+        return fail(FA2_EINVAL, "%s overlaps %s", names[o], names[i]);
 
   // From here on the HIP runtime is involved.
   int dev = -1;
@@ -147,27 +154,147 @@ fa2_status_t fa2_fwd(const void* Q, const void* K, const void* V, void* O, float
     (void)hipGetLastError();
     return fail_hip(e, "hipGetDevice");
   }
-  for (int i = 0; i < 5; ++i) {
-    s = check_device_range(ptrs[i], i == 4 ? l_bytes : tensor_bytes, names[i]);
+  for (int i = 0; i < n; ++i) {
+    s = check_device_range(ptrs[i], sizes[i], names[i]);
     if (s != FA2_OK) return s;
   }
+  a->Q = Q;
+  a->K = K;
+  a->V = V;
+  a->O = O;
+  a->L = L;
+  a->BH = static_cast<int>(B * H);
+  a->N = static_cast<int>(N);
+  a->d = static_cast<int>(d);
+  a->causal = causal;
+  a->scale = scale;
+  a->num_m_block = static_cast<int>((N + bm - 1) / bm);
+  a->stream = static_cast<hipStream_t>(stream);
+  return FA2_OK;
+}
 
+// The pages' rule (page "Flash Attention V2原理解读", the thread-block grid
+// section): for each candidate number of splits compute the utilisation of
+// the GPU, take the highest, and choose the smallest candidate reaching 0.95
+// of it.  Utilisation of n work units on `slots` concurrent workgroups: the
+// busy fraction of the last round, (n / slots) / ceil(n / slots).
+int choose_num_splits(int64_t items, int64_t slots, int64_t max_splits) {
+  if (max_splits < 1) max_splits = 1;
+  double best = 0.0;
+  for (int64_t s = 1; s <= max_splits; ++s) {
+    const double rounds = double(items * s) / double(slots);
+    best = std::fmax(best, rounds / std::ceil(rounds));
+  }
+  for (int64_t s = 1; s <= max_splits; ++s) {
+    const double rounds = double(items * s) / double(slots);
+    if (rounds / std::ceil(rounds) >= 0.95 * best) return static_cast<int>(s);
+  }
+  return 1;
+}
+
+int64_t splitkv_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int64_t splits) {
+  return splits * B * H * N * (d + 1) * 4;  // O_s [splits][B*H][N][d] then L_s [splits][B*H][N]
+}
+
+fa2_status_t check_splits(int64_t B, int64_t H, int64_t N, int num_splits) {
+  if (num_splits < 1 || num_splits > FA2_MAX_SPLITS)
+    return fail(FA2_EINVAL, "num_splits=%d is not in 1..%d", num_splits, FA2_MAX_SPLITS);
+  const int64_t nmb = (N + fa2::kBlockM_bf16 - 1) / fa2::kBlockM_bf16;
+  if (B * H * N > 0 && (nmb * num_splits > ((int64_t(1) << 31) - 1) / (B * H) ||
+                        N * num_splits > ((int64_t(1) << 31) - 1) / (B * H)))
+    return fail(FA2_EINVAL, "B*H=%lld with N=%lld and %d splits exceeds 2^31 - 1 items or rows",
+                (long long)(B * H), (long long)N, num_splits);
+  return FA2_OK;
+}
+
+fa2_status_t heuristic_splits(int64_t B, int64_t H, int64_t N, int64_t d, int* num_splits) {
+  int slots = 0;
+  const hipError_t e = fa2::bf16_resident_workgroups(static_cast<int>(d), &slots);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail_hip(e, "device query");
+  }
+  const int64_t nmb = (N + fa2::kBlockM_bf16 - 1) / fa2::kBlockM_bf16;
+  const int64_t kv_blocks = (N + fa2::bf16_block_n(static_cast<int>(d)) - 1) /
+                            fa2::bf16_block_n(static_cast<int>(d));
+  const int64_t max_splits = kv_blocks < FA2_MAX_SPLITS ? kv_blocks : FA2_MAX_SPLITS;
+  *num_splits = choose_num_splits(nmb * B * H, slots, max_splits);
+  return FA2_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fa2_status_t fa2_fwd(const void* Q, const void* K, const void* V, void* O, float* L, int64_t B,
+                     int64_t H, int64_t N, int64_t d, int causal, float scale, fa2_dtype_t dtype,
+                     void* stream) {
+  g_last_error[0] = '\0';
   fa2::FwdArgs a;
-  a.Q = Q;
-  a.K = K;
-  a.V = V;
-  a.O = O;
-  a.L = L;
-  a.BH = static_cast<int>(B * H);
-  a.N = static_cast<int>(N);
-  a.d = static_cast<int>(d);
-  a.causal = causal;
-  a.scale = scale;
-  a.num_m_block = static_cast<int>((N + bm - 1) / bm);
-  a.stream = static_cast<hipStream_t>(stream);
-
+  fa2_status_t s =
+      prepare(Q, K, V, O, L, B, H, N, d, causal, scale, dtype, stream, nullptr, 0, &a);
+  if (s != FA2_OK || a.BH == 0) return s;
   (void)hipGetLastError();  // clear a stale error so the status below is this launch's
-  e = dtype == FA2_BF16 ? fa2::launch_fwd_bf16(a) : fa2::launch_fwd_f32(a);
+  hipError_t e = dtype == FA2_BF16 ? fa2::launch_fwd_bf16(a) : fa2::launch_fwd_f32(a);
+  if (e == hipSuccess) e = hipGetLastError();
+  if (e != hipSuccess) return fail_hip(e, "kernel launch");
+  return FA2_OK;
+}
+
+fa2_status_t fa2_splitkv_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d,
+                                        int num_splits, size_t* bytes) {
+  g_last_error[0] = '\0';
+  int64_t bm = 0;
+  fa2_status_t s = check_shape(B, H, N, d, FA2_BF16, &bm);
+  if (s != FA2_OK) return s;
+  s = check_splits(B, H, N, num_splits);
+  if (s != FA2_OK) return s;
+  if (!bytes) return fail(FA2_EINVAL, "bytes is NULL");
+  *bytes = static_cast<size_t>(splitkv_bytes(B, H, N, d, num_splits));
+  return FA2_OK;
+}
+
+fa2_status_t fa2_num_splits(int64_t B, int64_t H, int64_t N, int64_t d, int* num_splits) {
+  g_last_error[0] = '\0';
+  int64_t bm = 0;
+  fa2_status_t s = check_shape(B, H, N, d, FA2_BF16, &bm);
+  if (s != FA2_OK) return s;
+  if (!num_splits) return fail(FA2_EINVAL, "num_splits is NULL");
+  return heuristic_splits(B, H, N, d, num_splits);
+}
+
+fa2_status_t fa2_fwd_splitkv(const void* Q, const void* K, const void* V, void* O, float* L,
+                             int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
+                             fa2_dtype_t dtype, int num_splits, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  g_last_error[0] = '\0';
+  if (dtype != FA2_BF16)
+    return fail(FA2_ENOTSUP, "split-KV is implemented for FA2_BF16 only (dtype %d)", (int)dtype);
+  int64_t bm = 0;
+  fa2_status_t s = check_shape(B, H, N, d, dtype, &bm);
+  if (s != FA2_OK) return s;
+  if (num_splits < 0) return fail(FA2_EINVAL, "num_splits=%d must be >= 0", num_splits);
+  if (B * H * N == 0) return FA2_OK;
+  if (num_splits == 0) {
+    s = heuristic_splits(B, H, N, d, &num_splits);
+    if (s != FA2_OK) return s;
+  }
+  s = check_splits(B, H, N, num_splits);
+  if (s != FA2_OK) return s;
+  const int64_t need = splitkv_bytes(B, H, N, d, num_splits);
+  if (workspace == nullptr) return fail(FA2_EINVAL, "workspace is NULL");
+  if (static_cast<int64_t>(workspace_bytes) < need)
+    return fail(FA2_EINVAL, "workspace of %llu bytes is smaller than the %lld bytes needed",
+                (unsigned long long)workspace_bytes, (long long)need);
+  fa2::FwdArgs a;
+  s = prepare(Q, K, V, O, L, B, H, N, d, causal, scale, dtype, stream, workspace, need, &a);
+  if (s != FA2_OK) return s;
+  a.num_splits = num_splits;
+  a.ws_O = static_cast<float*>(workspace);
+  a.ws_L = a.ws_O + static_cast<size_t>(num_splits) * B * H * N * d;
+  (void)hipGetLastError();
+  hipError_t e = fa2::launch_fwd_bf16(a);
+  if (e == hipSuccess) e = fa2::launch_combine_bf16(a);
   if (e == hipSuccess) e = hipGetLastError();
   if (e != hipSuccess) return fail_hip(e, "kernel launch");
   return FA2_OK;

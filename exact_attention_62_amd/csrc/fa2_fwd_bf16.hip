@@ -81,6 +81,7 @@ typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((ext_vector_type(4))) short s16x4_t;
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef __attribute__((address_space(3))) s16x4_t* lds_s16x4_ptr_t;
@@ -103,6 +104,9 @@ template <int D> struct Cfg;
 template <> struct Cfg<64> { static constexpr int BN = 64, kWavesPerSimd = 2; };
 template <> struct Cfg<128> { static constexpr int BN = 64, kWavesPerSimd = 2; };
 template <> struct Cfg<256> { static constexpr int BN = 32, kWavesPerSimd = 1; };
+static_assert(Cfg<64>::BN == bf16_block_n(64) && Cfg<128>::BN == bf16_block_n(128) &&
+                  Cfg<256>::BN == bf16_block_n(256),
+              "host view of the block size");
 
 // LDS layout of a K or V block: key row r lives in 1 KB piece blk(r) at row
 // slot slot(r); pieces are kPiece bytes apart.  Rows 0..15 of any aligned group
@@ -169,11 +173,16 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
 }
 
-template <int D, bool CAUSAL>
+// SPLIT: the key/value range of each query block is cut into num_splits
+// contiguous parts, each a work item of its own; an item writes its partial
+// result (O normalised within the part, fp32, and its L) to Ow / Lw, indexed
+// [split][batch*head][row], for a separate merge.
+template <int D, bool CAUSAL, bool SPLIT>
 __global__ void __launch_bounds__(kThreads, Cfg<D>::kWavesPerSimd)
 fa2_fwd_bf16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
                     const uint16_t* __restrict__ Vg, uint16_t* __restrict__ Og,
-                    float* __restrict__ Lg, int N, int num_m_block, int total_items,
+                    float* __restrict__ Lg, float* __restrict__ Ow, float* __restrict__ Lw,
+                    int N, int BH, int num_m_block, int num_splits, int total_items,
                     float c, float scale_abs, uint32_t qsign, uint32_t qkeep) {
   constexpr int BN = Cfg<D>::BN;
   constexpr int CH = D / 8;                  // 16-byte chunks per key row
@@ -235,35 +244,69 @@ fa2_fwd_bf16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict_
   };
 
   // ---- per-item state
-  int bh = 0, m = 0, q0 = 0, qrow = 0, j_end = 0, j_mask = 0;
+  int bh = 0, m = 0, q0 = 0, qrow = 0, j_beg = 0, j_end = 0, j_mask = 0;
+  int g0 = 0;      // running block count of this workgroup at the current item's first block
+  int k_item = 0;  // index of the current item in this workgroup's sequence
   const uint16_t *Qh = Qg, *Kh = Kg, *Vh = Vg;
   // O and L of the item's query block as buffer resources whose size covers
   // only the rows < N: the hardware drops stores to rows past the end, so
   // every wavefront issues the same number of stores for every item.
   __amdgpu_buffer_rsrc_t o_rsrc, l_rsrc;
-  auto decode = [&](int logical, int& bh_, int& m_) __attribute__((always_inline)) {
-    bh_ = logical / num_m_block;
-    const int mi = logical - bh_ * num_m_block;
+  int gb = 0;  // buffer parity base: block j uses K and V buffers (gb + j) & 1
+  // logical item -> (batch*head, query block, split): splits fastest, then the
+  // query blocks of a head (heaviest causal block first), then the heads.
+  auto decode = [&](int logical, int& bh_, int& m_, int& s_) __attribute__((always_inline)) {
+    int mi = logical;
+    s_ = 0;
+    if constexpr (SPLIT) {
+      mi = logical / num_splits;
+      s_ = logical - mi * num_splits;
+    }
+    bh_ = mi / num_m_block;
+    mi -= bh_ * num_m_block;
     m_ = CAUSAL ? num_m_block - 1 - mi : mi;
   };
   auto blocks_of = [&](int m_) __attribute__((always_inline)) -> int {
     if (CAUSAL) return (min(N, (m_ + 1) * kBM) - 1) / BN + 1;
     return (N + BN - 1) / BN;
   };
+  // KV blocks [beg, end) of split s of query block m: ceil(blocks / num_splits)
+  // blocks per split, so split 0 is never empty (and holds key 0, which every
+  // row sees); later splits can be.
+  auto range_of = [&](int m_, int s_, int& beg, int& end) __attribute__((always_inline)) {
+    const int jt = blocks_of(m_);
+    if constexpr (SPLIT) {
+      const int per = (jt + num_splits - 1) / num_splits;
+      beg = min(s_ * per, jt);
+      end = min(beg + per, jt);
+    } else {
+      beg = 0;
+      end = jt;
+    }
+  };
   auto set_item = [&](int logical) __attribute__((always_inline)) {
-    decode(logical, bh, m);
+    int sp;
+    decode(logical, bh, m, sp);
+    range_of(m, sp, j_beg, j_end);
     const size_t slice = (size_t)bh * (size_t)N * D;
     Qh = Qg + slice;
     Kh = Kg + slice;
     Vh = Vg + slice;
     const int rows = min(kBM, N - m * kBM);
-    o_rsrc = __builtin_amdgcn_make_buffer_rsrc(Og + slice + (size_t)m * kBM * D, (short)0,
-                                               rows * ROWB, kBufferFlags);
-    l_rsrc = __builtin_amdgcn_make_buffer_rsrc(Lg + (size_t)bh * N + (size_t)m * kBM, (short)0,
-                                               rows * 4, kBufferFlags);
+    if constexpr (SPLIT) {
+      const size_t prow = ((size_t)sp * BH + bh) * N + (size_t)m * kBM;  // first partial row
+      o_rsrc = __builtin_amdgcn_make_buffer_rsrc(Ow + prow * D, (short)0, rows * D * 4,
+                                                 kBufferFlags);
+      l_rsrc = __builtin_amdgcn_make_buffer_rsrc(Lw + prow, (short)0, rows * 4, kBufferFlags);
+    } else {
+      o_rsrc = __builtin_amdgcn_make_buffer_rsrc(Og + slice + (size_t)m * kBM * D, (short)0,
+                                                 rows * ROWB, kBufferFlags);
+      l_rsrc = __builtin_amdgcn_make_buffer_rsrc(Lg + (size_t)bh * N + (size_t)m * kBM, (short)0,
+                                                 rows * 4, kBufferFlags);
+    }
     q0 = m * kBM + wave * 32;  // first query row of this wavefront
     qrow = q0 + col;
-    j_end = blocks_of(m);
+    gb = g0 - j_beg;
     // Blocks before j_mask need no mask for this wavefront (every key visible
     // to every one of its rows).
     j_mask = CAUSAL ? min((q0 + 1) / BN, N / BN) : N / BN;
@@ -363,15 +406,15 @@ fa2_fwd_bf16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict_
       }
     }
   };
-  // The first blocks of an item: Q rows, K_0 and V_0, and K_1 if there is one.
-  // g is the running block count of this workgroup: block g of the sequence
-  // uses K and V buffers g & 1.
+  // The first blocks of an item (blocks beg, beg+1, ... of its range): Q rows,
+  // K_beg and V_beg, and K_beg+1 if the range has it.  g is the running block
+  // count of this workgroup: block g of the sequence uses buffers g & 1.
   auto issue_item_start = [&](const uint16_t* qh, const uint16_t* kh, const uint16_t* vh, int row,
-                              int blocks, int g) __attribute__((always_inline)) {
+                              int beg, int blocks, int g) __attribute__((always_inline)) {
     load_q(qh, row);
-    issue_k(kh, 0, Kb0 + (g & 1) * TB);
-    issue_v(vh, 0, Vb0 + (g & 1) * TBV);
-    if (blocks > 1) issue_k(kh, BN, Kb0 + ((g + 1) & 1) * TB);
+    issue_k(kh, beg * BN, Kb0 + (g & 1) * TB);
+    issue_v(vh, beg * BN, Vb0 + (g & 1) * TBV);
+    if (blocks > 1) issue_k(kh, (beg + 1) * BN, Kb0 + ((g + 1) & 1) * TB);
   };
 
   // ---- LDS fragment addresses (bytes within a block buffer).
@@ -391,8 +434,6 @@ fa2_fwd_bf16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict_
   f32x16_t o[DT];
   float m_ref = kNegInf;  // reference max of the (sign-adjusted) raw logits
   float l_part = 0.f;     // running sum over this lane's half of the keys
-  int g0 = 0;             // running block count at the current item's block 0
-  int k_item = 0;         // index of the current item in this workgroup's sequence
 
   auto compute_S = [&](const char* kb, f32x16_t (&S)[KT]) __attribute__((always_inline)) {
 #pragma unroll
@@ -438,8 +479,12 @@ fa2_fwd_bf16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict_
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[kt][r]);
     mx = halves_max(mx);
     // The first block with a visible key always moves the reference (alpha =
-    // exp2(-inf) = 0 then: O and l are still zero).
-    const bool move = m_ref == kNegInf || c * (mx - m_ref) > kTau;
+    // exp2(-inf) = 0 then: O and l are still zero).  A split's range can hold
+    // no key a row sees (mx = -inf): the reference then stays at -inf and the
+    // block adds nothing, without forming exp2(-inf + inf).
+    bool move;
+    if constexpr (SPLIT) move = m_ref == kNegInf ? mx != kNegInf : c * (mx - m_ref) > kTau;
+    else move = m_ref == kNegInf || c * (mx - m_ref) > kTau;
     const float alpha = move ? __builtin_amdgcn_exp2f(c * (m_ref - mx)) : 1.f;
     m_ref = move ? mx : m_ref;
     const float mc = m_ref == kNegInf ? 0.f : c * m_ref;
@@ -458,7 +503,7 @@ fa2_fwd_bf16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict_
 #pragma unroll
       for (int t = 0; t < DT; ++t) o[t] *= alpha;
     }
-    const char* vb = Vb0 + ((g0 + j) & 1) * TBV + vaddr;
+    const char* vb = Vb0 + ((gb + j) & 1) * TBV + vaddr;
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
@@ -479,28 +524,30 @@ fa2_fwd_bf16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict_
   auto advance = [&](int j) __attribute__((always_inline)) {
     // At an item's first block the previous item's O and L stores, issued
     // last, need not have completed.
-    if (j == 0 && k_item > 0) wait_vmcnt<NSTORE>();
+    if (j == j_beg && k_item > 0) wait_vmcnt<NSTORE>();
     else wait_vmcnt<0>();
     lds_barrier();
-    if (j + 2 < j_end) issue_k(Kh, (j + 2) * BN, Kb0 + ((g0 + j) & 1) * TB);
-    if (j + 1 < j_end) issue_v(Vh, (j + 1) * BN, Vb0 + ((g0 + j + 1) & 1) * TBV);
+    if (j + 2 < j_end) issue_k(Kh, (j + 2) * BN, Kb0 + ((gb + j) & 1) * TB);
+    if (j + 1 < j_end) issue_v(Vh, (j + 1) * BN, Vb0 + ((gb + j + 1) & 1) * TBV);
   };
 
-  // ---- item prologue: wait for Q and K_0, then S for block 0.  Vector
-  // memory operations complete in issue order, and V_0 and K_1 (and, after
-  // the first item, the previous item's O and L stores) were issued after
-  // K_0, so the wait leaves that many operations in flight; then a barrier.
-  // The first item's prologue is separate from the later items' (at the end
-  // of the loop), so that the compiler's own wait for the Q registers counts
-  // the stores on the later path instead of draining everything.
+  // ---- item prologue: wait for Q and K_beg, then S for the first block.
+  // Vector memory operations complete in issue order, and V_beg and K_beg+1
+  // (and, after the first item, the previous item's O and L stores) were
+  // issued after K_beg, so the wait leaves that many operations in flight;
+  // then a barrier.  The first item's prologue is separate from the later
+  // items' (at the end of the loop), so that the compiler's own wait for the
+  // Q registers counts the stores on the later path instead of draining
+  // everything.
   f32x16_t S_cur[KT];
   auto prologue = [&](auto later_tag) __attribute__((always_inline)) {
     fix_q();
+    const bool two = j_end - j_beg > 1;
     if constexpr (decltype(later_tag)::value) {
-      if (j_end > 1) wait_vmcnt<LOADS_V + LOADS + NSTORE>();
+      if (two) wait_vmcnt<LOADS_V + LOADS + NSTORE>();
       else wait_vmcnt<LOADS_V + NSTORE>();
     } else {
-      if (j_end > 1) wait_vmcnt<LOADS_V + LOADS>();
+      if (two) wait_vmcnt<LOADS_V + LOADS>();
       else wait_vmcnt<LOADS_V>();
     }
     lds_barrier();
@@ -510,31 +557,107 @@ fa2_fwd_bf16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict_
     l_part = 0.f;
     compute_S(Kb0 + (g0 & 1) * TB, S_cur);
   };
+  // The item after the current one, and its key range.
+  int next = -1, nbh = 0, nm = 0, nsp = 0, nbeg = 0, nend = 0;
+  auto look_ahead = [&]() __attribute__((always_inline)) {
+    next = logical_of(k_item + 1);
+    if (next >= 0) {
+      decode(next, nbh, nm, nsp);
+      range_of(nm, nsp, nbeg, nend);
+    }
+  };
+  // The next item's Q and first K/V blocks; issued while this item's last
+  // block is processed (or at once, for an empty item).
+  auto prefetch_next = [&]() __attribute__((always_inline)) {
+    if (next >= 0 && nend > nbeg) {
+      const size_t nslice = (size_t)nbh * (size_t)N * D;
+      issue_item_start(Qg + nslice, Kg + nslice, Vg + nslice, nm * kBM + wave * 32 + col, nbeg,
+                       nend - nbeg, g0 + (j_end - j_beg));
+    }
+  };
+  // ---- item epilogue, after the KV loop: O = O / l once, L = m + ln(l).
+  // (A split row that saw no key has l = 0: O_s = 0 and L_s = -inf.)
+  auto store_result = [&]() __attribute__((always_inline)) {
+    const float l_tot = halves_sum(l_part);
+    float inv = 1.f / l_tot;
+    if constexpr (SPLIT) inv = l_tot > 0.f ? inv : 0.f;
+    const int lrow = wave * 32 + col;  // this lane's row in the query block
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int dim = t * 32 + 8 * g + 4 * half;
+        if constexpr (SPLIT) {
+          f32x4_t w;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) w[r] = o[t][g * 4 + r] * inv;
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, w), o_rsrc,
+                                                 (lrow * D + dim) * 4, 0, 0);
+        } else {
+          bf16x4_t w;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) w[r] = (__bf16)(o[t][g * 4 + r] * inv);
+          __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, w), o_rsrc,
+                                                lrow * ROWB + dim * 2, 0, 0);
+        }
+      }
+    // Both halves of a row hold the same l and m: they store the same L.
+    __builtin_amdgcn_raw_buffer_store_b32(
+        __builtin_bit_cast(uint32_t,
+                           __builtin_fmaf(__builtin_amdgcn_logf(l_tot), kLn2, scale_abs * m_ref)),
+        l_rsrc, lrow * 4, 0, 0);
+  };
+  // Split items whose key range is empty are finished here (O_s = 0,
+  // L_s = -inf), so that the KV loop below is only ever entered through a
+  // prologue.  Returns false when the workgroup's sequence ends.
+  auto finish_empty_items = [&]() __attribute__((always_inline)) -> bool {
+    if constexpr (SPLIT) {
+      while (j_end == j_beg) {
+        look_ahead();
+        prefetch_next();
+#pragma unroll
+        for (int t = 0; t < DT; ++t) o[t] = f32x16_t{};
+        m_ref = kNegInf;
+        l_part = 0.f;
+        store_result();
+        if (next < 0) return false;
+        ++k_item;
+        set_item(next);
+      }
+    }
+    return true;
+  };
 
   int logical = logical_of(0);
   if (logical < 0) return;  // uniform for the workgroup
   set_item(logical);
-  issue_item_start(Qh, Kh, Vh, qrow, j_end, 0);
-  prologue(std::false_type{});
+  if (!finish_empty_items()) return;
+  if (k_item == 0) {
+    issue_item_start(Qh, Kh, Vh, qrow, j_beg, j_end - j_beg, g0);
+    prologue(std::false_type{});
+  } else {
+    prologue(std::true_type{});  // prefetched by the last empty item, stores after it
+  }
 
   for (;;) {
+    look_ahead();
     const int j_unmasked = min(j_mask, j_end - 1);  // unmasked blocks that have a successor
     f32x16_t SB[KT];
-    int j = 0;
+    int j = j_beg;
     // Unrolled by two so that the S registers alternate between S_cur and SB
     // instead of being copied every block.
     for (; j + 2 <= j_unmasked; j += 2) {
       advance(j);
       consume(std::false_type{}, j, S_cur,
-              [&]() { compute_S(Kb0 + ((g0 + j + 1) & 1) * TB, SB); });
+              [&]() { compute_S(Kb0 + ((gb + j + 1) & 1) * TB, SB); });
       advance(j + 1);
       consume(std::false_type{}, j + 1, SB,
-              [&]() { compute_S(Kb0 + ((g0 + j) & 1) * TB, S_cur); });
+              [&]() { compute_S(Kb0 + ((gb + j) & 1) * TB, S_cur); });
     }
     if (j < j_unmasked) {
       advance(j);
       consume(std::false_type{}, j, S_cur,
-              [&]() { compute_S(Kb0 + ((g0 + j + 1) & 1) * TB, SB); });
+              [&]() { compute_S(Kb0 + ((gb + j + 1) & 1) * TB, SB); });
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt) S_cur[kt] = SB[kt];
       ++j;
@@ -542,58 +665,34 @@ fa2_fwd_bf16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict_
     for (; j + 2 < j_end; j += 2) {
       advance(j);
       consume(std::true_type{}, j, S_cur,
-              [&]() { compute_S(Kb0 + ((g0 + j + 1) & 1) * TB, SB); });
+              [&]() { compute_S(Kb0 + ((gb + j + 1) & 1) * TB, SB); });
       advance(j + 1);
       consume(std::true_type{}, j + 1, SB,
-              [&]() { compute_S(Kb0 + ((g0 + j) & 1) * TB, S_cur); });
+              [&]() { compute_S(Kb0 + ((gb + j) & 1) * TB, S_cur); });
     }
     if (j + 1 < j_end) {
       advance(j);
       consume(std::true_type{}, j, S_cur,
-              [&]() { compute_S(Kb0 + ((g0 + j + 1) & 1) * TB, SB); });
+              [&]() { compute_S(Kb0 + ((gb + j + 1) & 1) * TB, SB); });
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt) S_cur[kt] = SB[kt];
       ++j;
     }
     // Last block of the item.  Both K buffers and the other V buffer are free
-    // now, and so are the Q registers: the next item's Q, K_0, V_0, K_1 go out
-    // here and overlap this block's softmax, its PV product and the O stores.
+    // now, and so are the Q registers: the next item's Q, K_beg, V_beg,
+    // K_beg+1 go out here and overlap this block's softmax, its PV product and
+    // the O stores.
     advance(j);
-    const int next = logical_of(k_item + 1);
-    if (next >= 0) {
-      int nbh, nm;
-      decode(next, nbh, nm);
-      const size_t nslice = (size_t)nbh * (size_t)N * D;
-      issue_item_start(Qg + nslice, Kg + nslice, Vg + nslice, nm * kBM + wave * 32 + col,
-                       blocks_of(nm), g0 + j_end);
-    }
+    prefetch_next();
     // Always the masked form: one copy of the code, and for an unmasked block
     // the threshold test hides nothing.
     consume(std::true_type{}, j, S_cur, [] {});
-
-    // ---- item epilogue, after the KV loop: O = O / l once, L = m + ln(l).
-    const float l_tot = halves_sum(l_part);
-    const float inv = 1.f / l_tot;
-    const int orow = (wave * 32 + col) * ROWB;  // byte offset of this lane's row in the block
-#pragma unroll
-    for (int t = 0; t < DT; ++t)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        bf16x4_t w;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) w[r] = (__bf16)(o[t][g * 4 + r] * inv);
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, w), o_rsrc,
-                                              orow + (t * 32 + 8 * g + 4 * half) * 2, 0, 0);
-      }
-    // Both halves of a row hold the same l and m: they store the same L.
-    __builtin_amdgcn_raw_buffer_store_b32(
-        __builtin_bit_cast(uint32_t,
-                           __builtin_fmaf(__builtin_amdgcn_logf(l_tot), kLn2, scale_abs * m_ref)),
-        l_rsrc, (wave * 32 + col) * 4, 0, 0);
+    store_result();
     if (next < 0) break;
-    g0 += j_end;
+    g0 += j_end - j_beg;
     ++k_item;
     set_item(next);
+    if (!finish_empty_items()) break;
     prologue(std::true_type{});
   }
 }
@@ -614,9 +713,10 @@ hipError_t cu_count(int* cus) {
   return hipSuccess;
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool SPLIT>
 hipError_t launch(const FwdArgs& a) {
-  const int total = a.num_m_block * a.BH;
+  const int splits = SPLIT ? a.num_splits : 1;
+  const int total = a.num_m_block * a.BH * splits;
   // Persistent grid: as many workgroups as fit on the chip at once (a 4-wave
   // workgroup puts one wave on each SIMD of a CU, so kWavesPerSimd workgroups
   // per CU), each walking its share of the work items.
@@ -631,25 +731,38 @@ hipError_t launch(const FwdArgs& a) {
   const float sa = zero ? 1.f : (a.scale < 0.f ? -a.scale : a.scale);
   const uint32_t qsign = a.scale < 0.f ? 0x80008000u : 0u;
   const uint32_t qkeep = zero ? 0u : 0xFFFFFFFFu;
-  hipLaunchKernelGGL((fa2_fwd_bf16_kernel<D, CAUSAL>), dim3(grid), dim3(kThreads), 0, a.stream,
-                     (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V,
-                     (uint16_t*)a.O, a.L, a.N, a.num_m_block, total, sa * kLog2e, sa, qsign,
-                     qkeep);
+  hipLaunchKernelGGL((fa2_fwd_bf16_kernel<D, CAUSAL, SPLIT>), dim3(grid), dim3(kThreads), 0,
+                     a.stream, (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V,
+                     (uint16_t*)a.O, a.L, a.ws_O, a.ws_L, a.N, a.BH, a.num_m_block, splits, total,
+                     sa * kLog2e, sa, qsign, qkeep);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_fwd_bf16(const FwdArgs& a) {
-  switch (a.d * 2 + a.causal) {
-    case 64 * 2 + 0: return launch<64, false>(a);
-    case 64 * 2 + 1: return launch<64, true>(a);
-    case 128 * 2 + 0: return launch<128, false>(a);
-    case 128 * 2 + 1: return launch<128, true>(a);
-    case 256 * 2 + 0: return launch<256, false>(a);
-    case 256 * 2 + 1: return launch<256, true>(a);
+  const bool split = a.num_splits > 0;
+  switch ((a.d * 2 + a.causal) * 2 + split) {
+#define FA2_CASE(D, C)                                                  \
+  case (D * 2 + C) * 2 + 0: return launch<D, (bool)C, false>(a);       \
+  case (D * 2 + C) * 2 + 1: return launch<D, (bool)C, true>(a);
+    FA2_CASE(64, 0)
+    FA2_CASE(64, 1)
+    FA2_CASE(128, 0)
+    FA2_CASE(128, 1)
+    FA2_CASE(256, 0)
+    FA2_CASE(256, 1)
+#undef FA2_CASE
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t bf16_resident_workgroups(int d, int* slots) {
+  int cus = 0;
+  const hipError_t e = cu_count(&cus);
+  if (e != hipSuccess) return e;
+  *slots = (d == 256 ? Cfg<256>::kWavesPerSimd : Cfg<128>::kWavesPerSimd) * cus;
+  return hipSuccess;
 }
 
 }  // namespace fa2

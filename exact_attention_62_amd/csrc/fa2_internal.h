@@ -10,6 +10,8 @@ namespace fa2 {
 // rows each.  fp32 exact mode: four wavefronts of one row each.
 constexpr int kBlockM_bf16 = 128;
 constexpr int kBlockM_f32 = 4;
+// Keys per K/V block of the bf16 kernel.
+constexpr int bf16_block_n(int d) { return d == 256 ? 32 : 64; }
 
 struct FwdArgs {
   const void* Q;
@@ -24,10 +26,19 @@ struct FwdArgs {
   float scale;      // softmax scale
   int num_m_block;  // ceil(N / kBlockM)
   hipStream_t stream;
+  // Split-KV (bf16 only): num_splits > 0 writes partial results to ws_O
+  // [num_splits][BH][N][d] and ws_L [num_splits][BH][N] (fp32) instead of O/L.
+  int num_splits = 0;
+  float* ws_O = nullptr;
+  float* ws_L = nullptr;
 };
 
 // Enqueue the kernel; returns the launch's hipError_t.
 hipError_t launch_fwd_bf16(const FwdArgs& a);
 hipError_t launch_fwd_f32(const FwdArgs& a);
+// Merge num_splits partial results (ws_O, ws_L) into O (bf16) and L.
+hipError_t launch_combine_bf16(const FwdArgs& a);
+// Workgroups of the bf16 kernel resident at once on the current device.
+hipError_t bf16_resident_workgroups(int d, int* slots);
 
 }  // namespace fa2

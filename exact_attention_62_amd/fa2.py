@@ -16,8 +16,9 @@ import threading
 
 import torch
 
-__all__ = ["FA2Error", "fa2_fwd", "fa2_launch_shape", "fa2_strerror", "fa2_last_error",
-           "attention", "library_path", "load_library"]
+__all__ = ["FA2Error", "fa2_fwd", "fa2_fwd_splitkv", "fa2_launch_shape", "fa2_num_splits",
+           "fa2_splitkv_workspace_size", "fa2_strerror", "fa2_last_error", "attention",
+           "library_path", "load_library"]
 
 FA2_OK, FA2_EINVAL, FA2_ENOTSUP, FA2_EHIP = 0, -1, -2, -3
 FA2_BF16, FA2_FP32 = 0, 1
@@ -61,6 +62,15 @@ def load_library() -> ctypes.CDLL:
                                          ctypes.POINTER(i64), ctypes.POINTER(i64),
                                          ctypes.POINTER(i64)]
         lib.fa2_launch_shape.restype = ctypes.c_int
+        lib.fa2_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int,
+                                        ctypes.c_float, ctypes.c_int, ctypes.c_int, vp,
+                                        ctypes.c_size_t, vp]
+        lib.fa2_fwd_splitkv.restype = ctypes.c_int
+        lib.fa2_splitkv_workspace_size.argtypes = [i64, i64, i64, i64, ctypes.c_int,
+                                                   ctypes.POINTER(ctypes.c_size_t)]
+        lib.fa2_splitkv_workspace_size.restype = ctypes.c_int
+        lib.fa2_num_splits.argtypes = [i64, i64, i64, i64, ctypes.POINTER(ctypes.c_int)]
+        lib.fa2_num_splits.restype = ctypes.c_int
         lib.fa2_strerror.argtypes = [ctypes.c_int]
         lib.fa2_strerror.restype = ctypes.c_char_p
         lib.fa2_last_error.argtypes = []
@@ -90,15 +100,7 @@ def fa2_launch_shape(B: int, H: int, N: int, d: int, dtype: torch.dtype = torch.
     return tuple(o.value for o in out)
 
 
-def fa2_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
-            lse: torch.Tensor, causal: bool = False, scale: float | None = None,
-            stream: torch.cuda.Stream | None = None) -> None:
-    """Enqueue the forward pass on ``stream`` (default: the current stream).
-
-    q, k, v, o: contiguous [B, H, N, d] tensors of one dtype (bfloat16 or
-    float32) on the current GPU; lse: contiguous float32 [B, H, N].  Writes
-    o and lse in place.
-    """
+def _check_tensors(q, k, v, o, lse):
     if q.dim() != 4:
         raise ValueError(f"q must be [B, H, N, d], got shape {tuple(q.shape)}")
     B, H, N, d = q.shape
@@ -117,9 +119,22 @@ def fa2_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
             raise ValueError("every tensor must be on the GPU")
         if not t.is_contiguous():
             raise ValueError("every tensor must be contiguous")
-    dev = q.device
-    if any(t.device != dev for t in tensors):
+    if any(t.device != q.device for t in tensors):
         raise ValueError("every tensor must be on the same device")
+    return B, H, N, d
+
+
+def fa2_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+            lse: torch.Tensor, causal: bool = False, scale: float | None = None,
+            stream: torch.cuda.Stream | None = None) -> None:
+    """Enqueue the forward pass on ``stream`` (default: the current stream).
+
+    q, k, v, o: contiguous [B, H, N, d] tensors of one dtype (bfloat16 or
+    float32) on the current GPU; lse: contiguous float32 [B, H, N].  Writes
+    o and lse in place.
+    """
+    B, H, N, d = _check_tensors(q, k, v, o, lse)
+    dev = q.device
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if stream is None:
@@ -132,10 +147,59 @@ def fa2_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
     _check(st)
 
 
+def fa2_splitkv_workspace_size(B: int, H: int, N: int, d: int, num_splits: int) -> int:
+    """Bytes of workspace fa2_fwd_splitkv needs with ``num_splits`` splits (no GPU call)."""
+    out = ctypes.c_size_t(0)
+    _check(load_library().fa2_splitkv_workspace_size(B, H, N, d, int(num_splits), ctypes.byref(out)))
+    return out.value
+
+
+def fa2_num_splits(B: int, H: int, N: int, d: int, device=None) -> int:
+    """The pages' num_splits rule for this problem on ``device`` (default: the current GPU)."""
+    out = ctypes.c_int(0)
+    with torch.cuda.device(device if device is not None else torch.cuda.current_device()):
+        _check(load_library().fa2_num_splits(B, H, N, d, ctypes.byref(out)))
+    return out.value
+
+
+def fa2_fwd_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+                    lse: torch.Tensor, workspace: torch.Tensor, num_splits: int = 0,
+                    causal: bool = False, scale: float | None = None,
+                    stream: torch.cuda.Stream | None = None) -> None:
+    """Enqueue the split-KV forward pass (bfloat16).  ``workspace`` is a contiguous GPU
+    tensor of at least fa2_splitkv_workspace_size(...) bytes; num_splits = 0 takes
+    fa2_num_splits's choice.  Writes o and lse in place."""
+    B, H, N, d = _check_tensors(q, k, v, o, lse)
+    dev = q.device
+    if not workspace.is_cuda or not workspace.is_contiguous() or workspace.device != dev:
+        raise ValueError("workspace must be a contiguous tensor on the inputs' GPU")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    lib = load_library()
+    with torch.cuda.device(dev):
+        st = lib.fa2_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                 lse.data_ptr(), B, H, N, d, 1 if causal else 0, float(scale),
+                                 _DTYPES[q.dtype], int(num_splits), workspace.data_ptr(),
+                                 workspace.numel() * workspace.element_size(),
+                                 ctypes.c_void_p(stream.cuda_stream))
+    _check(st)
+
+
 def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
-              scale: float | None = None):
-    """Allocate O and L and run the forward pass.  Returns (o, lse)."""
+              scale: float | None = None, num_splits: int | None = None):
+    """Allocate O and L and run the forward pass.  Returns (o, lse).
+
+    num_splits=None runs fa2_fwd; an integer runs fa2_fwd_splitkv with that many
+    splits (0: the pages' rule), with a workspace allocated here."""
     o = torch.empty_like(q, memory_format=torch.contiguous_format)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
-    fa2_fwd(q, k, v, o, lse, causal=causal, scale=scale)
+    if num_splits is None:
+        fa2_fwd(q, k, v, o, lse, causal=causal, scale=scale)
+        return o, lse
+    B, H, N, d = q.shape
+    s = num_splits if num_splits > 0 else fa2_num_splits(B, H, N, d, q.device)
+    ws = torch.empty(fa2_splitkv_workspace_size(B, H, N, d, s), dtype=torch.uint8, device=q.device)
+    fa2_fwd_splitkv(q, k, v, o, lse, ws, num_splits=s, causal=causal, scale=scale)
     return o, lse

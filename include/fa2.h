@@ -12,7 +12,7 @@
  *     O[b][h][i][:] = sum_j softmax_j(S[i][:]) * V[b][h][j][:]
  *     L[b][h][i]    = m_i + ln(l_i),  m_i = max_j S[i][j],  l_i = sum_j exp(S[i][j] - m_i)
  *
- * computed tile by tile: one workgroup per block of query rows (the outer
+ * computed tile by tile: one work item per block of query rows (the outer
  * loop), K/V blocks streamed through LDS (the inner loop), an online running
  * row max and row sum, the division by l applied once after the loop, K/V
  * blocks that the causal mask covers entirely skipped, and only O and the
@@ -24,8 +24,8 @@
  *     Queries and keys have the same length N.
  *   - Ownership: every array pointer is device memory of the current HIP device,
  *     allocated and owned by the caller.  The library allocates nothing, frees
- *     nothing and keeps no pointer after the call returns.  O and L must not
- *     overlap each other or Q, K, V.
+ *     nothing and keeps no pointer after the call returns.  O and L (and a
+ *     workspace, where one is taken) must not overlap each other or Q, K, V.
  *   - Asynchrony: work is enqueued on `stream` (a hipStream_t; NULL means the
  *     default stream) and the call returns without synchronising.
  *   - Thread safety: calls may be made from any number of host threads.  The only
@@ -37,6 +37,7 @@
 #ifndef FA2_H
 #define FA2_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -76,6 +77,64 @@ typedef enum {
 fa2_status_t fa2_fwd(const void* Q, const void* K, const void* V, void* O, float* L,
                      int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
                      fa2_dtype_t dtype, void* stream);
+
+/* Largest number of key/value splits fa2_fwd_splitkv accepts. */
+#define FA2_MAX_SPLITS 128
+
+/*
+ * fa2_fwd_splitkv - the forward pass with the key/value sequence split across
+ * work items, for problems whose query blocks alone cannot fill the GPU.
+ *
+ * The pages (page "Flash Attention V2原理解读", the thread-block grid section)
+ * allow splitting the key/value sequence as well as the queries when the
+ * (query block, batch, head) grid leaves the GPU partly idle, at the price of
+ * one more combine step: each row of O then gets one part from every split.
+ * Here the K/V blocks a query block visits (all of them, or those up to the
+ * diagonal when causal) are cut into num_splits contiguous parts of
+ * ceil(blocks / num_splits) blocks.  Each (query block, batch, head, part) is a
+ * work item that writes its partial result to the workspace: O_s, normalised
+ * within its keys, and L_s = m_s + ln(l_s) (-inf for a row that sees none of
+ * its keys).  A second kernel on the same stream merges them:
+ *   L = ln sum_s exp(L_s),   O = sum_s exp(L_s - L) O_s.
+ * The result is the operation fa2_fwd computes, up to rounding.
+ *
+ *   Q, K, V, O, L, B, H, N, d, causal, scale, stream: as for fa2_fwd.
+ *   dtype            FA2_BF16 only (FA2_FP32 gives FA2_ENOTSUP).
+ *   num_splits       1..FA2_MAX_SPLITS, or 0 for the value fa2_num_splits gives.
+ *   workspace        device memory owned by the caller, 16-byte aligned, of at
+ *                    least fa2_splitkv_workspace_size() bytes for the number of
+ *                    splits used; it must not overlap Q, K, V, O or L.  Its
+ *                    contents on entry do not matter; on return they are
+ *                    unspecified.  Calls sharing a workspace must be ordered.
+ *   workspace_bytes  the workspace's size; too small gives FA2_EINVAL.
+ *
+ * Every element of O and L is written; results are deterministic.
+ */
+fa2_status_t fa2_fwd_splitkv(const void* Q, const void* K, const void* V, void* O, float* L,
+                             int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
+                             fa2_dtype_t dtype, int num_splits, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/*
+ * fa2_splitkv_workspace_size - bytes of workspace fa2_fwd_splitkv needs with
+ * num_splits splits: num_splits * B*H*N * (d + 1) * 4 (the float32 partial O_s
+ * and L_s of every split).  Host-only: makes no HIP call.  Returns the
+ * argument errors fa2_fwd_splitkv would (sizes, d, num_splits out of range).
+ */
+fa2_status_t fa2_splitkv_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d,
+                                        int num_splits, size_t* bytes);
+
+/*
+ * fa2_num_splits - the number of splits the pages' rule chooses for this
+ * problem on the current device (page "Flash Attention V2原理解读", the
+ * thread-block grid section): for every candidate s in 1..min(K/V blocks,
+ * FA2_MAX_SPLITS), the utilisation of the GPU by items * s work items, items
+ * = B*H*ceil(N / kBlockM), over the device's concurrently resident workgroups
+ * (the busy fraction of the last round: (n / slots) / ceil(n / slots)); then
+ * the smallest s whose utilisation is at least 0.95 of the best.  Queries the
+ * current device's compute-unit count (a HIP call; FA2_EHIP if that fails).
+ */
+fa2_status_t fa2_num_splits(int64_t B, int64_t H, int64_t N, int64_t d, int* num_splits);
 
 /*
  * fa2_launch_shape - the work decomposition fa2_fwd uses, as a host-only query.

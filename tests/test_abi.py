@@ -32,7 +32,9 @@ def _declared_functions():
 
 
 def test_header_declares_the_boundary():
-    assert _declared_functions() == ["fa2_fwd", "fa2_last_error", "fa2_launch_shape", "fa2_strerror"]
+    assert _declared_functions() == ["fa2_fwd", "fa2_fwd_splitkv", "fa2_last_error",
+                                     "fa2_launch_shape", "fa2_num_splits",
+                                     "fa2_splitkv_workspace_size", "fa2_strerror"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -148,3 +150,56 @@ def test_last_error_is_thread_local():
     t.join()
     assert seen["msg"] == ""
     assert "causal=5" in F.fa2_last_error()
+
+
+# ---- split-KV entry points ---------------------------------------------------------------
+def _split(ws=FAKE + 0x500000, ws_bytes=1 << 24, num_splits=2, dtype=F.FA2_BF16, **kw):
+    args = dict(q=FAKE, k=FAKE + 0x100000, v=FAKE + 0x200000, o=FAKE + 0x300000,
+                L=FAKE + 0x400000, B=1, H=1, N=16, d=64, causal=0, scale=0.125)
+    args.update(kw)
+    lib = F.load_library()
+    return lib.fa2_fwd_splitkv(args["q"], args["k"], args["v"], args["o"], args["L"], args["B"],
+                               args["H"], args["N"], args["d"], args["causal"], args["scale"],
+                               dtype, num_splits, ws, ws_bytes, None)
+
+
+def test_workspace_size_formula():
+    # num_splits * B*H*N * (d + 1) float32 values: O_s and L_s of every split
+    assert F.fa2_splitkv_workspace_size(2, 4, 1024, 64, 8) == 8 * 2 * 4 * 1024 * 65 * 4
+    assert F.fa2_splitkv_workspace_size(1, 1, 1, 256, 1) == 257 * 4
+    assert F.fa2_splitkv_workspace_size(0, 4, 1024, 64, 3) == 0
+
+
+@pytest.mark.parametrize("s", [0, -1, 129])
+def test_workspace_size_rejects_split_counts(s):
+    with pytest.raises(F.FA2Error) as e:
+        F.fa2_splitkv_workspace_size(1, 1, 64, 64, s)
+    assert e.value.status == F.FA2_EINVAL and "num_splits" in str(e.value)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(dtype=F.FA2_FP32), F.FA2_ENOTSUP, "FA2_BF16 only"),
+    (dict(d=96), F.FA2_ENOTSUP, "d=96"),
+    (dict(num_splits=-1), F.FA2_EINVAL, "num_splits=-1"),
+    (dict(num_splits=200), F.FA2_EINVAL, "num_splits=200"),
+    (dict(ws=None), F.FA2_EINVAL, "workspace is NULL"),
+    (dict(ws=FAKE + 0x500004), F.FA2_EINVAL, "workspace="),
+    (dict(ws_bytes=100), F.FA2_EINVAL, "smaller than"),
+    (dict(ws=FAKE + 0x300000 + 512), F.FA2_EINVAL, "overlaps"),
+    (dict(o=FAKE + 0x500000 + 64), F.FA2_EINVAL, "overlaps"),
+    (dict(causal=3), F.FA2_EINVAL, "causal=3"),
+])
+def test_splitkv_invalid_arguments_before_any_hip_call(kw, status, needle):
+    assert _split(**kw) == status
+    assert needle in F.fa2_last_error()
+
+
+def test_splitkv_empty_problem_is_a_no_op():
+    assert _split(q=None, k=None, v=None, o=None, L=None, ws=None, ws_bytes=0, B=0) == F.FA2_OK
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="needs a host without a visible GPU")
+def test_num_splits_without_a_device_reports_the_hip_error():
+    out = ctypes.c_int(0)
+    assert F.load_library().fa2_num_splits(1, 1, 1024, 64, ctypes.byref(out)) == F.FA2_EHIP
+    assert _split(num_splits=0) == F.FA2_EHIP  # the rule needs the device's CU count
