@@ -1,9 +1,10 @@
 """Benchmark of the FlashAttention-2 forward pass on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload train]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload train] [--splits S]
 
 A step is one fa2_fwd call (the whole hot path: one kernel launch) over the
-workload's inputs, which are generated with the seeded recipe and copied to
+workload's inputs (with --splits: one fa2_fwd_splitkv call, the split kernel and
+the merge kernel), which are generated with the seeded recipe and copied to
 HBM before timing starts.  W untimed steps, then exactly K timed steps
 bracketed by torch.cuda.synchronize(); the launches are also bracketed by HIP
 events recorded on the stream the kernel is enqueued on, which gives the
@@ -45,6 +46,8 @@ def parse_args(argv=None):
     p.add_argument("--causal", type=int, choices=(0, 1), default=None,
                    help="override the workload's first mask setting")
     p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--splits", type=int, default=None, metavar="S",
+                   help="time the split-KV path (fa2_fwd_splitkv) with S splits; 0 = the pages' rule")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target duration of the CPU-oracle baseline sample (0 disables it)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -140,7 +143,8 @@ def main(argv=None) -> int:
 
     import torch
 
-    from exact_attention_62_amd import fa2_fwd, load_library
+    from exact_attention_62_amd import (fa2_fwd, fa2_fwd_splitkv, fa2_num_splits,
+                                        fa2_splitkv_workspace_size, load_library)
     from exact_attention_62_amd.inputs import WORKLOADS, make
 
     if not torch.cuda.is_available():
@@ -158,9 +162,23 @@ def main(argv=None) -> int:
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
     flops = w.flops(causal)
+    splits = None
+    if args.splits is not None:
+        if w.dtype != "bf16":
+            print("the split-KV path is bf16 only", file=sys.stderr)
+            return 1
+        splits = args.splits if args.splits > 0 else fa2_num_splits(w.B, w.H, w.N, w.d)
+        ws = torch.empty(fa2_splitkv_workspace_size(w.B, w.H, w.N, w.d, splits), dtype=torch.uint8,
+                         device=dev)
+
+        def step():
+            fa2_fwd_splitkv(q, k, v, o, lse, ws, num_splits=splits, causal=causal, scale=w.scale)
+    else:
+        def step():
+            fa2_fwd(q, k, v, o, lse, causal=causal, scale=w.scale)
 
     for _ in range(args.warmup):
-        fa2_fwd(q, k, v, o, lse, causal=causal, scale=w.scale)
+        step()
     torch.cuda.synchronize()
 
     ev0 = torch.cuda.Event(enable_timing=True)
@@ -169,7 +187,7 @@ def main(argv=None) -> int:
     t0 = time.perf_counter()
     ev0.record(stream)
     for _ in range(args.steps):
-        fa2_fwd(q, k, v, o, lse, causal=causal, scale=w.scale)
+        step()
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -179,7 +197,12 @@ def main(argv=None) -> int:
     achieved = flops / (kernel_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
 
-    traffic = measured_traffic(w.name, causal, w.dtype)
+    traffic = measured_traffic(w.name, causal, w.dtype) if splits is None else None
+    kname = f"fa2_fwd_{w.dtype}_kernel<{w.d},{'true' if causal else 'false'}" + (
+        ",false>" if w.dtype == "bf16" else ">")
+    if splits is not None:
+        kname = (f"fa2_fwd_bf16_kernel<{w.d},{'true' if causal else 'false'},true> + "
+                 f"fa2_combine_kernel<{w.d}> (both per step; kernel_ms covers the two)")
     out = {
         "metric": METRIC,
         "value": round(tflops, 2),
@@ -195,12 +218,13 @@ def main(argv=None) -> int:
         "data": "synthetic (seeded normal Q, K, V; see exact_attention_62_amd/inputs.py)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
                    "causal": causal, "scale": w.scale, "kBlockM": 128,
-                   "flops_per_step": flops},
+                   "flops_per_step": flops,
+                   **({"path": "split-KV", "num_splits": splits} if splits is not None else {})},
         "pct_of_peak": round(100.0 * tflops / peak, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": traffic,
-                     "kernel": f"fa2_fwd_{w.dtype}_kernel<{w.d},{'true' if causal else 'false'}>",
+                     "kernel": kname,
                      "kernel_ms": round(kernel_ms, 5),
                      "kernel_source_hash": kernel_source_hash(w.dtype)},
     }
