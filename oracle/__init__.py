@@ -5,6 +5,7 @@ benchmark's CPU-baseline leg, never by the library.  It shares no code with
 the HIP path and never imports it.
 """
 from .attention import attention_fp64, attention_rows_fp64, scaled_logits_fp64
+from .backward import attention_bwd_fp64, delta_fp64
 from .splitkv import (attention_keyrange_fp64, combine_fp64, num_splits_heuristic, split_ranges,
                       utilisation)
 from .tiled import causal_block_end, fa2_forward_tiled_fp64
@@ -20,4 +21,6 @@ __all__ = [
     "num_splits_heuristic",
     "split_ranges",
     "utilisation",
+    "attention_bwd_fp64",
+    "delta_fp64",
 ]
