@@ -300,4 +300,84 @@ fa2_status_t fa2_fwd_splitkv(const void* Q, const void* K, const void* V, void* 
   return FA2_OK;
 }
 
+fa2_status_t fa2_bwd_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d, size_t* bytes) {
+  g_last_error[0] = '\0';
+  int64_t bm = 0;
+  fa2_status_t s = check_shape(B, H, N, d, FA2_BF16, &bm);
+  if (s != FA2_OK) return s;
+  if (d == 256) return fail(FA2_ENOTSUP, "the backward pass supports d = 64 and 128 (d=256)");
+  if (!bytes) return fail(FA2_EINVAL, "bytes is NULL");
+  *bytes = static_cast<size_t>(B * H * N * 4);  // D = rowsum(dO * O), float32 per row
+  return FA2_OK;
+}
+
+fa2_status_t fa2_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                     const float* L, void* dQ, void* dK, void* dV, int64_t B, int64_t H,
+                     int64_t N, int64_t d, int causal, float scale, fa2_dtype_t dtype,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error[0] = '\0';
+  if (dtype != FA2_BF16)
+    return fail(FA2_ENOTSUP, "the backward pass is implemented for FA2_BF16 only (dtype %d)",
+                (int)dtype);
+  int64_t bm = 0;
+  fa2_status_t s = check_shape(B, H, N, d, dtype, &bm);
+  if (s != FA2_OK) return s;
+  if (d == 256) return fail(FA2_ENOTSUP, "the backward pass supports d = 64 and 128 (d=256)");
+  if (causal != 0 && causal != 1) return fail(FA2_EINVAL, "causal=%d must be 0 or 1", causal);
+  if (!std::isfinite(scale)) return fail(FA2_EINVAL, "scale must be finite");
+  if (B * H * N == 0) return FA2_OK;
+
+  const int64_t tb = B * H * N * d * 2, lb = B * H * N * 4;
+  constexpr int n = 10;
+  const void* ptrs[n] = {Q, K, V, O, dO, L, dQ, dK, dV, workspace};
+  const int64_t sizes[n] = {tb, tb, tb, tb, tb, lb, tb, tb, tb, lb};
+  const char* names[n] = {"Q", "K", "V", "O", "dO", "L", "dQ", "dK", "dV", "workspace"};
+  for (int i = 0; i < n; ++i) {
+    if (ptrs[i] == nullptr) return fail(FA2_EINVAL, "%s is NULL", names[i]);
+    const uintptr_t align = (i == 5 || i == 9) ? 4 : 16;
+    if (reinterpret_cast<uintptr_t>(ptrs[i]) % align != 0)
+      return fail(FA2_EINVAL, "%s=%p is not %d-byte aligned", names[i], ptrs[i], (int)align);
+  }
+  if (static_cast<int64_t>(workspace_bytes) < lb)
+    return fail(FA2_EINVAL, "workspace of %llu bytes is smaller than the %lld bytes needed",
+                (unsigned long long)workspace_bytes, (long long)lb);
+  for (int o = 6; o < n; ++o)  // outputs and workspace: disjoint from everything else
+    for (int i = 0; i < n; ++i)
+      if (i != o && overlaps(ptrs[o], sizes[o], ptrs[i], sizes[i]))
+        return fail(FA2_EINVAL, "%s overlaps %s", names[o], names[i]);
+
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail_hip(e, "hipGetDevice");
+  }
+  for (int i = 0; i < n; ++i) {
+    s = check_device_range(ptrs[i], sizes[i], names[i]);
+    if (s != FA2_OK) return s;
+  }
+  fa2::BwdArgs a;
+  a.Q = Q;
+  a.K = K;
+  a.V = V;
+  a.O = O;
+  a.dO = dO;
+  a.L = L;
+  a.dQ = dQ;
+  a.dK = dK;
+  a.dV = dV;
+  a.Dvec = static_cast<float*>(workspace);
+  a.BH = static_cast<int>(B * H);
+  a.N = static_cast<int>(N);
+  a.d = static_cast<int>(d);
+  a.causal = causal;
+  a.scale = scale;
+  a.stream = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  e = fa2::launch_bwd_bf16(a);
+  if (e == hipSuccess) e = hipGetLastError();
+  if (e != hipSuccess) return fail_hip(e, "kernel launch");
+  return FA2_OK;
+}
+
 }  // extern "C"

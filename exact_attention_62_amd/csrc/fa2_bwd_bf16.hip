@@ -1,0 +1,371 @@
+// FlashAttention-2 backward pass, bf16 in / bf16 out, for gfx950 (MI355X).
+//
+// The pages fix the structure (page "FlashAttention学习笔记(2)", sections on the
+// forward and on the forward/backward thread-block split; page "Flash Attention
+// V2原理解读", the backward discussion; page "flash-attention123和ring-attention",
+// 优化1): the backward recomputes S and P block by block from the stored
+// L = m + ln(l) alone (exp(S - L) is already the normalised weight), and runs
+// with K/V outer and Q inner, so that dK and dV accumulate along a K/V block
+// while dQ accumulates across K/V blocks.  The gradient formulas are the plain
+// chain rule of softmax attention:
+//   P = exp(scale * Q K^T - L),  dV = P^T dO,  dP = dO V^T,
+//   D = rowsum(dO * O),  dS = P * (dP - D),  dQ = scale * dS K,  dK = scale * dS^T Q.
+//
+// Three kernels:
+//   fa2_bwd_prep     D per row (bandwidth-bound).
+//   fa2_bwd_dkdv     one workgroup per block of 128 keys (the pages' K/V-outer
+//                    worker); each wavefront owns 32 keys and walks every query
+//                    block that sees them, so its dK and dV stay in its own
+//                    registers and no wavefronts exchange partial sums (the
+//                    inter-warp reduction the pages point out for a split-Q
+//                    warp layout does not arise).
+//   fa2_bwd_dq       one workgroup per block of 128 queries, walking the K/V
+//                    blocks like the forward pass, for dQ; this recomputes S
+//                    and dP once more instead of accumulating dQ with atomics
+//                    across workgroups, so the result is deterministic.
+//
+// Every product is a 32x32x16 bf16 MFMA with fp32 accumulation.  As in the
+// forward pass, accumulators are kept transposed where that puts one output
+// row in one lane: lane l of a 32x32 tile holds column l % 32 and rows
+// 8*(r/4) + 4*(l/32) + r%4.  Tiles staged in LDS use one layout (128-byte
+// blocks of 4 rows x 16 dims) that serves both 16-byte row reads (the A
+// operand of S and dP) and transposing reads (ds_read_b64_tr_b16, the A operand
+// of dV^T, dK^T and dQ^T).
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include "fa2_device.h"
+#include "fa2_internal.h"
+
+namespace fa2 {
+namespace {
+
+using namespace dev;
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRows = 32 * kWaves;  // keys (dK/dV) or queries (dQ) per workgroup
+constexpr int kStep = 64;           // queries (dK/dV) or keys (dQ) per inner step
+
+// Byte offset of element (row r, dim c) of a staged [64][D] bf16 tile.
+template <int D>
+__device__ __forceinline__ constexpr int toff(int r, int c) {
+  return (r >> 2) * (8 * D) + (c >> 4) * 128 + 32 * (r & 3) + 2 * (c & 15);
+}
+
+// Stage rows [r0, r0 + 64) of a [N][D] bf16 slice into LDS in the tile layout
+// (rows past N are clamped to row N - 1; callers mask them).  Load i of this
+// thread fills 1 KB chunk n = wave*LOADS + i: its lane L writes 16 bytes, row
+// 4*(bk / NSEG) + (L%8)/2 and dims 16*(bk % NSEG) + 8*(L%2) of 128-byte block
+// bk = 8n + L/8.
+template <int D>
+__device__ __forceinline__ void stage_tile(const uint16_t* head, int r0, int N, char* buf,
+                                           int wave, int lane) {
+  constexpr int NSEG = D / 16;
+  constexpr int LOADS = kStep * D * 2 / 1024 / kWaves;
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int n = wave * LOADS + i;
+    const int bk = 8 * n + lane / 8;
+    const int r = min(r0 + 4 * (bk / NSEG) + (lane % 8) / 2, N - 1);
+    const int c = 16 * (bk % NSEG) + 8 * (lane % 2);
+    lds_dma(head + (size_t)r * D + c, lds_addr(buf + n * 1024));
+  }
+}
+
+// Stage 64 floats v[r0 .. r0+64) (clamped to index N - 1) into LDS: one
+// 4-byte direct load per lane.
+__device__ __forceinline__ void stage_vec(const float* v, int r0, int N, char* buf, int lane) {
+  const float* src = v + min(r0 + lane, N - 1);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
+               : : "s"(lds_addr(buf)), "v"(src) : "memory", "m0");
+}
+
+// A operand of a 32x32x16 MFMA from a staged tile, rows m = row0 + lane%32
+// and dims 16*ks + 8*(lane/32) .. +8: one 16-byte read.
+template <int D>
+__device__ __forceinline__ bf16x8_t row_frag(const char* tile, int row0, int ks, int lane) {
+  return *(const bf16x8_t*)(tile + toff<D>(row0 + (lane & 31), 16 * ks + 8 * (lane >> 5)));
+}
+
+// A operand (the transpose of a staged tile: dims x rows) for rows 16u .. 16u+15
+// of the tile and dims 32t .. 32t+31, in the permuted row order that matches a
+// B operand packed from accumulator registers 8*(u%2) .. 8*(u%2)+7 of the
+// 32-row tile u/2.  Within each 16-lane group, lane 4*r + c points at 4
+// consecutive dims of row kbase + r; ds_read_b64_tr_b16 hands lane t of the
+// group the 4 rows kbase .. kbase+3 of dim t.  kbase = 16u + 4*half (first 4
+// slots of the operand) and 16u + 8 + 4*half (last 4).
+template <int D>
+__device__ __forceinline__ bf16x8_t tr_frag(const char* tile, int u, int t, int lane) {
+  const int g = lane >> 4, i = lane & 15;
+  const int half = lane >> 5;
+  const int rb = 16 * u + 4 * half;  // first row of the first 4
+  const int c = 32 * t + 16 * (g & 1) + 4 * (i & 3);
+  const char* p_lo = tile + toff<D>(rb + (i >> 2), c);
+  const char* p_hi = tile + toff<D>(rb + 8 + (i >> 2), c);
+  const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr_t)p_lo);
+  const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr_t)p_hi);
+  return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// B operand fragments of a [N][D] bf16 slice held in registers: for k-step ks,
+// lane l holds row r0 + l%32, dims 16*ks + 8*(l/32) .. +8 (zero past N).
+template <int D>
+__device__ __forceinline__ void load_frags(bf16x8_t (&f)[D / 16], const uint16_t* head, int row,
+                                           int N, int half) {
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    u32x4_t t = {0u, 0u, 0u, 0u};
+    if (row < N) t = *(const u32x4_t*)(head + (size_t)row * D + 16 * ks + 8 * half);
+    f[ks] = __builtin_bit_cast(bf16x8_t, t);
+  }
+}
+
+// Store a transposed accumulator (DT tiles of 32 dims x 32 rows; lane = row)
+// times `mul` as bf16 rows [row0, row0+32) of a [N][D] slice, through a buffer
+// resource bounded to rows < N.
+template <int D>
+__device__ __forceinline__ void store_rows(const f32x16_t (&acc)[D / 32], float mul,
+                                           uint16_t* head, int row0, int N, int lane) {
+  const int rows = max(0, min(32, N - row0));  // 0 for a wavefront past the end: no store lands
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(head + (size_t)row0 * D, (short)0, rows * D * 2,
+                                        kBufferFlags);
+  const int half = lane >> 5, col = lane & 31;
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      bf16x4_t w;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) w[r] = (__bf16)(acc[t][g * 4 + r] * mul);
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, w), rs,
+                                            (col * D + t * 32 + 8 * g + 4 * half) * 2, 0, 0);
+    }
+}
+
+// ---------------------------------------------------------------- D = rowsum(dO * O)
+template <int D>
+__global__ void __launch_bounds__(kThreads)
+fa2_bwd_prep_kernel(const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO,
+                    float* __restrict__ Dv, int rows) {
+  constexpr int TPR = D / 8;  // threads per row, 8 dims each
+  const int row = blockIdx.x * (kThreads / TPR) + threadIdx.x / TPR;
+  const int t = threadIdx.x % TPR;
+  float acc = 0.f;
+  if (row < rows) {
+    const bf16x8_t o = *(const bf16x8_t*)(O + (size_t)row * D + 8 * t);
+    const bf16x8_t g = *(const bf16x8_t*)(dO + (size_t)row * D + 8 * t);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc += (float)o[i] * (float)g[i];
+  }
+#pragma unroll
+  for (int m = TPR / 2; m >= 1; m /= 2) acc += __shfl_xor(acc, m, 64);
+  if (row < rows && t == 0) Dv[row] = acc;
+}
+
+// ---------------------------------------------------------------- dK, dV
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(kThreads, 1)
+fa2_bwd_dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
+                    const uint16_t* __restrict__ Vg, const uint16_t* __restrict__ dOg,
+                    const float* __restrict__ Lg, const float* __restrict__ Dg,
+                    uint16_t* __restrict__ dKg, uint16_t* __restrict__ dVg, int N,
+                    int num_k_block, float c, float scale) {
+  constexpr int KS = D / 16, DT = D / 32;
+  constexpr int TILE = kStep * D * 2;  // bytes of one staged [64][D] tile
+  // Q, dO tiles, then the 64 L and 64 D values, for two steps.
+  __shared__ __attribute__((aligned(1024))) char smem[2 * (2 * TILE + 512)];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int half = lane >> 5, col = lane & 31;
+  // With the causal mask the first key blocks are the heaviest; they go out first.
+  const int kb = (int)blockIdx.x % num_k_block;
+  const int bh = blockIdx.x / num_k_block;
+  const size_t slice = (size_t)bh * N * D;
+  const uint16_t *Qh = Qg + slice, *dOh = dOg + slice;
+  const float *Lh = Lg + (size_t)bh * N, *Dh = Dg + (size_t)bh * N;
+  const int k0 = kb * kRows + 32 * wave;  // this wavefront's first key
+
+  bf16x8_t kf[KS], vf[KS];
+  load_frags<D>(kf, Kg + slice, k0 + col, N, half);
+  load_frags<D>(vf, Vg + slice, k0 + col, N, half);
+  f32x16_t dk[DT], dv[DT];
+#pragma unroll
+  for (int t = 0; t < DT; ++t) dk[t] = dv[t] = f32x16_t{};
+
+  // Query steps: from the first that can see the block's keys to the end.
+  const int i_beg = CAUSAL ? (kb * kRows) / kStep : 0;
+  const int i_end = (N + kStep - 1) / kStep;
+  auto buf = [&](int i) { return smem + (i & 1) * (2 * TILE + 512); };
+  auto stage = [&](int i) {
+    char* b = buf(i);
+    stage_tile<D>(Qh, i * kStep, N, b, wave, lane);
+    stage_tile<D>(dOh, i * kStep, N, b + TILE, wave, lane);
+    if (wave == 0) stage_vec(Lh, i * kStep, N, b + 2 * TILE, lane);
+    if (wave == 1) stage_vec(Dh, i * kStep, N, b + 2 * TILE + 256, lane);
+  };
+  if (i_beg < i_end) stage(i_beg);
+  for (int i = i_beg; i < i_end; ++i) {
+    wait_vmcnt<0>();
+    lds_barrier();
+    if (i + 1 < i_end) stage(i + 1);
+    const char* b = buf(i);
+    const char* qtile = b;
+    const char* dtile = b + TILE;
+    const float* lv = (const float*)(b + 2 * TILE);
+    const float* dv_ = (const float*)(b + 2 * TILE + 256);
+    const int q_base = i * kStep;
+    bf16x8_t pb[4], sb[4];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      f32x16_t S = f32x16_t{}, dP = f32x16_t{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(qtile, 32 * qt, ks, lane), kf[ks],
+                                                    S, 0, 0, 0);
+        dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(dtile, 32 * qt, ks, lane), vf[ks],
+                                                     dP, 0, 0, 0);
+      }
+      // This lane's key is k0 + col; accumulator r holds query
+      // q_base + 32*qt + 8*(r/4) + 4*half + r%4.
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int qr = 32 * qt + 8 * g + 4 * half;  // first of 4 consecutive queries
+        const f32x4_t L4 = *(const f32x4_t*)(lv + qr);
+        const f32x4_t D4 = *(const f32x4_t*)(dv_ + qr);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int q = q_base + qr + r;
+          const bool hide = q >= N || (CAUSAL && k0 + col > q);
+          const float p = hide ? 0.f
+                               : __builtin_amdgcn_exp2f(__builtin_fmaf(S[g * 4 + r], c,
+                                                                       -L4[r] * kLog2e));
+          const float ds = p * (dP[g * 4 + r] - D4[r]);
+          pb[qt * 2 + g / 2][(g % 2) * 4 + r] = (__bf16)p;
+          sb[qt * 2 + g / 2][(g % 2) * 4 + r] = (__bf16)ds;
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int t = 0; t < DT; ++t) {
+        dv[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(dtile, u, t, lane), pb[u],
+                                                        dv[t], 0, 0, 0);
+        dk[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(qtile, u, t, lane), sb[u],
+                                                        dk[t], 0, 0, 0);
+      }
+  }
+  store_rows<D>(dv, 1.f, dVg + slice, k0, N, lane);
+  store_rows<D>(dk, scale, dKg + slice, k0, N, lane);
+}
+
+// ---------------------------------------------------------------- dQ
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(kThreads, 1)
+fa2_bwd_dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
+                  const uint16_t* __restrict__ Vg, const uint16_t* __restrict__ dOg,
+                  const float* __restrict__ Lg, const float* __restrict__ Dg,
+                  uint16_t* __restrict__ dQg, int N, int num_m_block, float c, float scale) {
+  constexpr int KS = D / 16, DT = D / 32;
+  constexpr int TILE = kStep * D * 2;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * TILE];  // K, V tiles, two steps
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int half = lane >> 5, col = lane & 31;
+  const int mi = (int)blockIdx.x % num_m_block;
+  const int m = CAUSAL ? num_m_block - 1 - mi : mi;  // heaviest query blocks first
+  const int bh = blockIdx.x / num_m_block;
+  const size_t slice = (size_t)bh * N * D;
+  const uint16_t *Kh = Kg + slice, *Vh = Vg + slice;
+  const int q0 = m * kRows + 32 * wave;
+  const int qrow = q0 + col;
+
+  bf16x8_t qf[KS], df[KS];
+  load_frags<D>(qf, Qg + slice, qrow, N, half);
+  load_frags<D>(df, dOg + slice, qrow, N, half);
+  const float l2 = qrow < N ? Lg[(size_t)bh * N + qrow] * kLog2e : 0.f;
+  const float dd = qrow < N ? Dg[(size_t)bh * N + qrow] : 0.f;
+  f32x16_t dq[DT];
+#pragma unroll
+  for (int t = 0; t < DT; ++t) dq[t] = f32x16_t{};
+
+  const int j_end = CAUSAL ? (min(N, (m + 1) * kRows) - 1) / kStep + 1 : (N + kStep - 1) / kStep;
+  auto buf = [&](int j) { return smem + (j & 1) * (2 * TILE); };
+  auto stage = [&](int j) {
+    stage_tile<D>(Kh, j * kStep, N, buf(j), wave, lane);
+    stage_tile<D>(Vh, j * kStep, N, buf(j) + TILE, wave, lane);
+  };
+  stage(0);
+  for (int j = 0; j < j_end; ++j) {
+    wait_vmcnt<0>();
+    lds_barrier();
+    if (j + 1 < j_end) stage(j + 1);
+    const char* kt_ = buf(j);
+    const char* vt = buf(j) + TILE;
+    bf16x8_t sb[4];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      f32x16_t S = f32x16_t{}, dP = f32x16_t{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(kt_, 32 * kt, ks, lane), qf[ks], S,
+                                                    0, 0, 0);
+        dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(vt, 32 * kt, ks, lane), df[ks],
+                                                     dP, 0, 0, 0);
+      }
+      // This lane's query is qrow; accumulator r holds key
+      // j*64 + 32*kt + 8*(r/4) + 4*half + r%4.
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = j * kStep + 32 * kt + 8 * (r / 4) + 4 * half + (r % 4);
+        const bool hide = key >= N || (CAUSAL && key > qrow);
+        const float p = hide ? 0.f : __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], c, -l2));
+        sb[kt * 2 + r / 8][r % 8] = (__bf16)(p * (dP[r] - dd));
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int t = 0; t < DT; ++t)
+        dq[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(kt_, u, t, lane), sb[u], dq[t],
+                                                        0, 0, 0);
+  }
+  store_rows<D>(dq, scale, dQg + slice, q0, N, lane);
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch(const BwdArgs& a) {
+  const float c = a.scale * kLog2e;
+  const int rows = a.BH * a.N;
+  constexpr int RPB = kThreads / (D / 8);
+  hipLaunchKernelGGL((fa2_bwd_prep_kernel<D>), dim3((rows + RPB - 1) / RPB), dim3(kThreads), 0,
+                     a.stream, (const uint16_t*)a.O, (const uint16_t*)a.dO, a.Dvec, rows);
+  const int nkb = (a.N + kRows - 1) / kRows;
+  hipLaunchKernelGGL((fa2_bwd_dkdv_kernel<D, CAUSAL>), dim3(nkb * a.BH), dim3(kThreads), 0,
+                     a.stream, (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V,
+                     (const uint16_t*)a.dO, a.L, a.Dvec, (uint16_t*)a.dK, (uint16_t*)a.dV, a.N,
+                     nkb, c, a.scale);
+  hipLaunchKernelGGL((fa2_bwd_dq_kernel<D, CAUSAL>), dim3(nkb * a.BH), dim3(kThreads), 0,
+                     a.stream, (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V,
+                     (const uint16_t*)a.dO, a.L, a.Dvec, (uint16_t*)a.dQ, a.N, nkb, c, a.scale);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_bf16(const BwdArgs& a) {
+  switch (a.d * 2 + a.causal) {
+    case 64 * 2 + 0: return launch<64, false>(a);
+    case 64 * 2 + 1: return launch<64, true>(a);
+    case 128 * 2 + 0: return launch<128, false>(a);
+    case 128 * 2 + 1: return launch<128, true>(a);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fa2

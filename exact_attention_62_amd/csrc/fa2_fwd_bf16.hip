@@ -71,32 +71,19 @@
 
 #include <type_traits>
 
+#include "fa2_device.h"
 #include "fa2_internal.h"
 
 namespace fa2 {
 namespace {
 
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
-typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
-typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
-typedef __attribute__((ext_vector_type(16))) float f32x16_t;
-typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
-typedef __attribute__((ext_vector_type(4))) float f32x4_t;
-typedef __attribute__((ext_vector_type(4))) short s16x4_t;
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-typedef __attribute__((address_space(3))) s16x4_t* lds_s16x4_ptr_t;
-typedef __attribute__((address_space(1))) const void* global_ptr_t;
+using namespace dev;
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBM = 32 * kWaves;  // query rows per workgroup
 static_assert(kBM == kBlockM_bf16, "kBlockM mismatch");
 
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kNegInf = -__builtin_inff();
-// Word 3 of a raw buffer resource on this GPU family (stride 0, 32-bit data).
-constexpr int kBufferFlags = 0x00020000;
 constexpr float kTau = 8.0f;  // lazy-rescale threshold, log2 units
 
 // Keys per K/V block and wavefronts per SIMD for each head dimension.
@@ -128,55 +115,6 @@ template <int D>
 __host__ __device__ constexpr int lds_off(int r) { return blk<D>(r) * kPiece + slot<D>(r) * 2 * D; }
 // V layout: element (key row r, dim d) at (r/4)*4*2D + (d/16)*128 + 32*(r%4) + 2*(d%16).
 
-// Value of x combined with the one held 32 lanes away (the two lane halves of
-// a 32x32 MFMA tile hold different keys of the same query row).
-__device__ __forceinline__ float halves_max(float x) { return fmaxf(x, __shfl_xor(x, 32, 64)); }
-__device__ __forceinline__ float halves_sum(float x) { return x + __shfl_xor(x, 32, 64); }
-
-// Direct global -> LDS loads of 16 bytes per lane (lane i fills LDS bytes
-// lds + 16i .. +16), and the waits and barriers that order them.  They are
-// inline assembly on purpose: the compiler treats every LDS read that follows
-// a direct load it knows about as a possible reader of that load and waits for
-// all of them, which would cut the prefetch distance to a fraction of a block.
-// The kernel orders these loads itself (vmcnt waits, then a barrier), and the
-// memory clobbers keep the compiler from moving LDS accesses across them.
-__device__ __forceinline__ void lds_dma(const void* base, uint32_t voff, uint32_t lds) {
-  // address = base (scalar) + voff (per lane)
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-               : : "s"(lds), "v"(voff), "s"(base) : "memory", "m0");
-}
-__device__ __forceinline__ void lds_dma(const void* addr, uint32_t lds) {
-  // address = addr (per lane)
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-               : : "s"(lds), "v"(addr) : "memory", "m0");
-}
-__device__ __forceinline__ uint32_t lds_addr(const char* p) {
-  return (uint32_t)(uintptr_t)(lds_ptr_t)p;
-}
-// Wait until at most N vector-memory operations of this wavefront are in
-// flight (they complete in issue order).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
-}
-// The lane index, recomputed where it is used: values derived from it that
-// only the masked or ragged-tail paths need are then not kept in registers
-// across the whole KV loop.
-__device__ __forceinline__ int fresh_lane() {
-  int l = (int)threadIdx.x;
-  asm volatile("" : "+v"(l));
-  return l & 63;
-}
-// Workgroup barrier after this wavefront's own LDS accesses have completed.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
-}
-
-// SPLIT: the key/value range of each query block is cut into num_splits
-// contiguous parts, each a work item of its own; an item writes its partial
-// result (O normalised within the part, fp32, and its L) to Ow / Lw, indexed
-// [split][batch*head][row], for a separate merge.
 template <int D, bool CAUSAL, bool SPLIT>
 __global__ void __launch_bounds__(kThreads, Cfg<D>::kWavesPerSimd)
 fa2_fwd_bf16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,

@@ -33,11 +33,29 @@ struct FwdArgs {
   float* ws_L = nullptr;
 };
 
+struct BwdArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  const void* O;
+  const void* dO;
+  const float* L;
+  void* dQ;
+  void* dK;
+  void* dV;
+  float* Dvec;  // workspace: rowsum(dO * O), [BH][N]
+  int BH, N, d, causal;
+  float scale;
+  hipStream_t stream;
+};
+
 // Enqueue the kernel; returns the launch's hipError_t.
 hipError_t launch_fwd_bf16(const FwdArgs& a);
 hipError_t launch_fwd_f32(const FwdArgs& a);
 // Merge num_splits partial results (ws_O, ws_L) into O (bf16) and L.
 hipError_t launch_combine_bf16(const FwdArgs& a);
+// Enqueue the backward pass (three kernels) on a.stream.
+hipError_t launch_bwd_bf16(const BwdArgs& a);
 // Workgroups of the bf16 kernel resident at once on the current device.
 hipError_t bf16_resident_workgroups(int d, int* slots);
 

@@ -16,8 +16,9 @@ import threading
 
 import torch
 
-__all__ = ["FA2Error", "fa2_fwd", "fa2_fwd_splitkv", "fa2_launch_shape", "fa2_num_splits",
-           "fa2_splitkv_workspace_size", "fa2_strerror", "fa2_last_error", "attention",
+__all__ = ["FA2Error", "FlashAttention", "attention", "attention_backward", "fa2_bwd",
+           "fa2_bwd_workspace_size", "fa2_fwd", "fa2_fwd_splitkv", "fa2_launch_shape",
+           "fa2_num_splits", "fa2_splitkv_workspace_size", "fa2_strerror", "fa2_last_error",
            "library_path", "load_library"]
 
 FA2_OK, FA2_EINVAL, FA2_ENOTSUP, FA2_EHIP = 0, -1, -2, -3
@@ -71,6 +72,11 @@ def load_library() -> ctypes.CDLL:
         lib.fa2_splitkv_workspace_size.restype = ctypes.c_int
         lib.fa2_num_splits.argtypes = [i64, i64, i64, i64, ctypes.POINTER(ctypes.c_int)]
         lib.fa2_num_splits.restype = ctypes.c_int
+        lib.fa2_bwd.argtypes = [vp] * 9 + [i64, i64, i64, i64, ctypes.c_int, ctypes.c_float,
+                                           ctypes.c_int, vp, ctypes.c_size_t, vp]
+        lib.fa2_bwd.restype = ctypes.c_int
+        lib.fa2_bwd_workspace_size.argtypes = [i64, i64, i64, i64, ctypes.POINTER(ctypes.c_size_t)]
+        lib.fa2_bwd_workspace_size.restype = ctypes.c_int
         lib.fa2_strerror.argtypes = [ctypes.c_int]
         lib.fa2_strerror.restype = ctypes.c_char_p
         lib.fa2_last_error.argtypes = []
@@ -203,3 +209,64 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = 
     ws = torch.empty(fa2_splitkv_workspace_size(B, H, N, d, s), dtype=torch.uint8, device=q.device)
     fa2_fwd_splitkv(q, k, v, o, lse, ws, num_splits=s, causal=causal, scale=scale)
     return o, lse
+
+
+def fa2_bwd_workspace_size(B: int, H: int, N: int, d: int) -> int:
+    """Bytes of workspace fa2_bwd needs (no GPU call)."""
+    out = ctypes.c_size_t(0)
+    _check(load_library().fa2_bwd_workspace_size(B, H, N, d, ctypes.byref(out)))
+    return out.value
+
+
+def fa2_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+            do: torch.Tensor, lse: torch.Tensor, dq: torch.Tensor, dk: torch.Tensor,
+            dv: torch.Tensor, workspace: torch.Tensor, causal: bool = False,
+            scale: float | None = None, stream: torch.cuda.Stream | None = None) -> None:
+    """Enqueue the backward pass (bfloat16): writes dq, dk, dv in place.  o and lse are
+    fa2_fwd's outputs for q, k, v; workspace holds at least fa2_bwd_workspace_size bytes."""
+    B, H, N, d = _check_tensors(q, k, v, o, lse)
+    for name, t in (("do", do), ("dq", dq), ("dk", dk), ("dv", dv)):
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError(f"{name} must be {q.dtype} {tuple(q.shape)}")
+        if not t.is_cuda or not t.is_contiguous() or t.device != q.device:
+            raise ValueError(f"{name} must be a contiguous tensor on the inputs' GPU")
+    if not workspace.is_cuda or not workspace.is_contiguous() or workspace.device != q.device:
+        raise ValueError("workspace must be a contiguous tensor on the inputs' GPU")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    lib = load_library()
+    with torch.cuda.device(q.device):
+        st = lib.fa2_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                         lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d,
+                         1 if causal else 0, float(scale), _DTYPES[q.dtype], workspace.data_ptr(),
+                         workspace.numel() * workspace.element_size(),
+                         ctypes.c_void_p(stream.cuda_stream))
+    _check(st)
+
+
+def attention_backward(q, k, v, o, lse, do, causal: bool = False, scale: float | None = None):
+    """Allocate dQ, dK, dV and a workspace, run fa2_bwd, return (dq, dk, dv)."""
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    B, H, N, d = q.shape
+    ws = torch.empty(fa2_bwd_workspace_size(B, H, N, d), dtype=torch.uint8, device=q.device)
+    fa2_bwd(q, k, v, o, do.contiguous(), lse, dq, dk, dv, ws, causal=causal, scale=scale)
+    return dq, dk, dv
+
+
+class FlashAttention(torch.autograd.Function):
+    """Autograd wrapper: forward through fa2_fwd, backward through fa2_bwd (bfloat16)."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, causal=False, scale=None):
+        o, lse = attention(q, k, v, causal=causal, scale=scale)
+        ctx.save_for_backward(q, k, v, o, lse)
+        ctx.causal, ctx.scale = causal, scale
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, o, lse = ctx.saved_tensors
+        dq, dk, dv = attention_backward(q, k, v, o, lse, do, causal=ctx.causal, scale=ctx.scale)
+        return dq, dk, dv, None, None

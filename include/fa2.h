@@ -156,6 +156,47 @@ fa2_status_t fa2_launch_shape(int64_t B, int64_t H, int64_t N, int64_t d, fa2_dt
 const char* fa2_strerror(fa2_status_t status);
 
 /*
+ * fa2_bwd - the FlashAttention-2 backward pass: the gradients dQ, dK, dV of
+ * O = fa2_fwd(Q, K, V) for an upstream gradient dO.
+ *
+ * The pages (page "FlashAttention学习笔记(2)", the forward section and the
+ * forward/backward thread-block split; page "Flash Attention V2原理解读", the
+ * backward discussion; page "flash-attention123和ring-attention", 优化1) fix the
+ * structure: P is recomputed block by block as exp(scale * Q K^T - L) from the
+ * forward's L alone, with K/V outer and Q inner (dK, dV accumulate along a K/V
+ * block, dQ across K/V blocks).  The gradients are the chain rule of softmax
+ * attention: D = rowsum(dO * O), dV = P^T dO, dS = P * (dO V^T - D),
+ * dQ = scale * dS K, dK = scale * dS^T Q (with the causal mask, P = 0 above the
+ * diagonal).  dQ is computed by a second, query-outer pass rather than with
+ * atomics, so results are deterministic.
+ *
+ *   Q, K, V, O, dO   [B][H][N][d] bf16 inputs, device memory, 16-byte aligned; O
+ *                    is fa2_fwd's output for Q, K, V (only rowsum(dO * O) is used).
+ *   L                [B][H][N] float32, fa2_fwd's L, device memory, 4-byte aligned.
+ *   dQ, dK, dV       [B][H][N][d] bf16 outputs, device memory, 16-byte aligned.
+ *   B, H, N, causal, scale, stream: as for fa2_fwd (the same values as the
+ *                    forward call).  B*H*N == 0 does nothing and returns FA2_OK.
+ *   d                64 or 128 (256 and others: FA2_ENOTSUP).
+ *   dtype            FA2_BF16 only (others: FA2_ENOTSUP).
+ *   workspace        device memory owned by the caller, 4-byte aligned, at least
+ *                    fa2_bwd_workspace_size() bytes (it receives D); contents on
+ *                    entry do not matter.  workspace_bytes is its size.
+ * The outputs and the workspace must not overlap each other or any input.
+ * Every element of dQ, dK and dV is written; results are deterministic.
+ */
+fa2_status_t fa2_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                     const float* L, void* dQ, void* dK, void* dV, int64_t B, int64_t H,
+                     int64_t N, int64_t d, int causal, float scale, fa2_dtype_t dtype,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fa2_bwd_workspace_size - bytes of workspace fa2_bwd needs: B*H*N * 4 (one
+ * float32 per row).  Host-only: makes no HIP call.  Returns the size and head
+ * dimension errors fa2_bwd would.
+ */
+fa2_status_t fa2_bwd_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d, size_t* bytes);
+
+/*
  * fa2_last_error - detail of the last failure on the calling thread: which
  * argument was rejected, or the HIP error name and text.  Empty string if the
  * thread's last call succeeded.  The pointer stays valid until the thread's

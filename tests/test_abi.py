@@ -32,9 +32,10 @@ def _declared_functions():
 
 
 def test_header_declares_the_boundary():
-    assert _declared_functions() == ["fa2_fwd", "fa2_fwd_splitkv", "fa2_last_error",
-                                     "fa2_launch_shape", "fa2_num_splits",
-                                     "fa2_splitkv_workspace_size", "fa2_strerror"]
+    assert _declared_functions() == ["fa2_bwd", "fa2_bwd_workspace_size", "fa2_fwd",
+                                     "fa2_fwd_splitkv", "fa2_last_error", "fa2_launch_shape",
+                                     "fa2_num_splits", "fa2_splitkv_workspace_size",
+                                     "fa2_strerror"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -203,3 +204,51 @@ def test_num_splits_without_a_device_reports_the_hip_error():
     out = ctypes.c_int(0)
     assert F.load_library().fa2_num_splits(1, 1, 1024, 64, ctypes.byref(out)) == F.FA2_EHIP
     assert _split(num_splits=0) == F.FA2_EHIP  # the rule needs the device's CU count
+
+
+# ---- backward entry points ---------------------------------------------------------------
+def _bwd(dtype=F.FA2_BF16, ws_bytes=1 << 16, **kw):
+    base = FAKE
+    a = dict(q=base, k=base + 0x100000, v=base + 0x200000, o=base + 0x300000, do=base + 0x400000,
+             L=base + 0x500000, dq=base + 0x600000, dk=base + 0x700000, dv=base + 0x800000,
+             ws=base + 0x900000, B=1, H=1, N=16, d=64, causal=0, scale=0.125)
+    a.update(kw)
+    return F.load_library().fa2_bwd(a["q"], a["k"], a["v"], a["o"], a["do"], a["L"], a["dq"],
+                                    a["dk"], a["dv"], a["B"], a["H"], a["N"], a["d"], a["causal"],
+                                    a["scale"], dtype, a["ws"], ws_bytes, None)
+
+
+def test_bwd_workspace_size_formula():
+    assert F.fa2_bwd_workspace_size(2, 4, 1024, 64) == 2 * 4 * 1024 * 4
+    with pytest.raises(F.FA2Error) as e:
+        F.fa2_bwd_workspace_size(1, 1, 16, 256)
+    assert e.value.status == F.FA2_ENOTSUP
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(dtype=F.FA2_FP32), F.FA2_ENOTSUP, "FA2_BF16 only"),
+    (dict(d=256), F.FA2_ENOTSUP, "d=256"),
+    (dict(d=96), F.FA2_ENOTSUP, "d=96"),
+    (dict(do=None), F.FA2_EINVAL, "dO is NULL"),
+    (dict(ws=None), F.FA2_EINVAL, "workspace is NULL"),
+    (dict(dk=FAKE + 0x700008), F.FA2_EINVAL, "dK="),
+    (dict(ws_bytes=8), F.FA2_EINVAL, "smaller than"),
+    (dict(dq=FAKE + 64), F.FA2_EINVAL, "dQ overlaps Q"),
+    (dict(dv=FAKE + 0x600000 + 128), F.FA2_EINVAL, "overlaps"),
+    (dict(causal=7), F.FA2_EINVAL, "causal=7"),
+    (dict(scale=float("nan")), F.FA2_EINVAL, "finite"),
+])
+def test_bwd_invalid_arguments_before_any_hip_call(kw, status, needle):
+    assert _bwd(**kw) == status
+    assert needle in F.fa2_last_error()
+
+
+def test_bwd_empty_problem_is_a_no_op():
+    nulls = dict(q=None, k=None, v=None, o=None, do=None, L=None, dq=None, dk=None, dv=None,
+                 ws=None)
+    assert _bwd(N=0, **nulls) == F.FA2_OK
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="needs a host without a visible GPU")
+def test_bwd_without_a_device_reports_the_hip_error():
+    assert _bwd() == F.FA2_EHIP

@@ -1,0 +1,114 @@
+"""Parity of the backward pass (fa2_bwd through the C ABI) with the fp64 oracle.
+
+Inputs Q, K, V and the upstream gradient dO are seeded bf16; O and L come from this library's
+forward pass (as a caller would pass them).  The oracle (oracle/backward.py) computes dQ, dK, dV
+from the same bf16 values by the plain chain rule in fp64.
+
+Tolerance: max |g - g_ref| <= 2e-2 * max(1, max |g_ref|) for each of dQ, dK, dV.  The errors
+are relative ones: P and dS enter their MFMA products rounded to bf16 (2^-9 relative), D =
+rowsum(dO * O) is formed from the bf16 O, and each output is rounded to bf16 once, so a few
+roundings of 2^-9 of the gradient's own size; 2e-2 is the forward's bound for O (whose values
+stay below ~5.5 here), kept for gradients of magnitude <= 1 and scaled with the gradient
+above that (peaked softmaxes, e.g. |scale| well above 1/sqrt(d), give gradients of 5 or
+more).  The measured errors are printed.  Outputs are pre-filled with NaN.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from exact_attention_62_amd import FlashAttention, attention, attention_backward
+from exact_attention_62_amd.inputs import make_random
+from oracle.backward import attention_bwd_fp64
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+
+
+def _say(msg):
+    print(f"\n[bwd] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def _grad_inputs(B, H, N, d, seed):
+    q, k, v = make_random(B, H, N, d, seed=seed)
+    g = torch.Generator().manual_seed(0x5EED0000 + 7 * seed + 1)
+    do = torch.randn(B, H, N, d, generator=g).to(torch.bfloat16)
+    return q, k, v, do
+
+
+def _check(got, ref, what):
+    errs = []
+    for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
+        g64 = g.double().cpu().numpy()
+        assert np.all(np.isfinite(g64)), f"{what}: non-finite {name}"
+        e = float(np.abs(g64 - r).max())
+        tol = TOL * max(1.0, float(np.abs(r).max()))
+        errs.append(e)
+        assert e <= tol, f"{what}: max |{name} - ref| = {e:.3e} > {tol:.3e} (max |ref| {np.abs(r).max():.2f})"
+    _say(f"{what}: max err dQ {errs[0]:.2e} dK {errs[1]:.2e} dV {errs[2]:.2e}")
+
+
+SHAPES = [(1, 1, 1, 64), (1, 1, 7, 128), (1, 2, 64, 64), (2, 1, 127, 128), (1, 3, 129, 64),
+          (1, 2, 200, 128), (2, 2, 300, 64), (1, 1, 513, 128), (1, 2, 1024, 128)]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_bwd_matches_the_oracle(shape, causal):
+    B, H, N, d = shape
+    _say(f"B={B} H={H} N={N} d={d} causal={causal}")
+    q, k, v, do = _grad_inputs(B, H, N, d, seed=N + d + causal)
+    ref = attention_bwd_fp64(q, k, v, do, causal=causal)
+    qd, kd, vd, dod = (t.cuda() for t in (q, k, v, do))
+    o, lse = attention(qd, kd, vd, causal=causal)
+    got = attention_backward(qd, kd, vd, o, lse, dod, causal=causal)
+    torch.cuda.synchronize()
+    _check(got, ref, f"{shape} causal={causal}")
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.3, 0.3])
+def test_bwd_zero_and_negative_scale(scale):
+    q, k, v, do = _grad_inputs(1, 2, 160, 64, seed=77)
+    ref = attention_bwd_fp64(q, k, v, do, causal=True, scale=scale)
+    qd, kd, vd, dod = (t.cuda() for t in (q, k, v, do))
+    o, lse = attention(qd, kd, vd, causal=True, scale=scale)
+    _check(attention_backward(qd, kd, vd, o, lse, dod, causal=True, scale=scale), ref,
+           f"scale={scale}")
+
+
+def test_bwd_outputs_fully_written_and_deterministic():
+    from exact_attention_62_amd import fa2_bwd, fa2_bwd_workspace_size
+    q, k, v, do = (t.cuda() for t in _grad_inputs(2, 2, 333, 128, seed=5))
+    o, lse = attention(q, k, v, causal=True)
+    outs = []
+    for _ in range(2):
+        dq, dk, dv = (torch.full_like(q, float("nan")) for _ in range(3))
+        ws = torch.full((fa2_bwd_workspace_size(2, 2, 333, 128) // 4,), float("nan"),
+                        device="cuda")
+        fa2_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, causal=True)
+        torch.cuda.synchronize()
+        for t in (dq, dk, dv):
+            assert torch.isfinite(t.float()).all()
+        outs.append((dq, dk, dv))
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
+def test_autograd_wrapper():
+    q, k, v, do = _grad_inputs(1, 2, 96, 64, seed=9)
+    ref = attention_bwd_fp64(q, k, v, do, causal=True)
+    qd, kd, vd = (t.cuda().requires_grad_() for t in (q, k, v))
+    o = FlashAttention.apply(qd, kd, vd, True, None)
+    o.backward(do.cuda())
+    _check((qd.grad, kd.grad, vd.grad), ref, "autograd wrapper")
