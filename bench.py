@@ -30,6 +30,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "attention fwd TFLOP/s (4BHN²d, causal halved) and % of bf16 MFMA peak"
+METRIC_BWD = "attention bwd TFLOP/s (2.5 x 4BHN²d, causal halved) and % of bf16 MFMA peak"
 # MI355X published dense peaks (256 CUs at 2.4 GHz): bf16 MFMA 2.5 PFLOP/s
 # (256 * 4096 flop/clk * 2.4 GHz = 2516.6 TFLOP/s); fp32 vector 157.3 TFLOP/s.
 PEAK_TFLOPS = {"bf16": 2516.6, "fp32": 157.3}
@@ -46,6 +47,8 @@ def parse_args(argv=None):
     p.add_argument("--causal", type=int, choices=(0, 1), default=None,
                    help="override the workload's first mask setting")
     p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--backward", action="store_true",
+                   help="time the backward pass (fa2_bwd) instead; flops = 2.5 x the forward's")
     p.add_argument("--splits", type=int, default=None, metavar="S",
                    help="time the split-KV path (fa2_fwd_splitkv) with S splits; 0 = the pages' rule")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -143,9 +146,10 @@ def main(argv=None) -> int:
 
     import torch
 
-    from exact_attention_62_amd import (fa2_fwd, fa2_fwd_splitkv, fa2_num_splits,
+    from exact_attention_62_amd import (fa2_bwd, fa2_bwd_workspace_size, fa2_fwd,
+                                        fa2_fwd_splitkv, fa2_num_splits,
                                         fa2_splitkv_workspace_size, load_library)
-    from exact_attention_62_amd.inputs import WORKLOADS, make
+    from exact_attention_62_amd.inputs import WORKLOADS, make, make_upstream
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -163,7 +167,20 @@ def main(argv=None) -> int:
     stream = torch.cuda.current_stream(dev)
     flops = w.flops(causal)
     splits = None
-    if args.splits is not None:
+    if args.backward:
+        if w.dtype != "bf16" or w.d not in (64, 128):
+            print("the backward pass is bf16 with d = 64 or 128", file=sys.stderr)
+            return 1
+        fa2_fwd(q, k, v, o, lse, causal=causal, scale=w.scale)
+        do = make_upstream(w.B, w.H, w.N, w.d, args.seed).to(dev)
+        dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+        bws = torch.empty(fa2_bwd_workspace_size(w.B, w.H, w.N, w.d), dtype=torch.uint8,
+                          device=dev)
+        flops = 2.5 * flops  # five products to the forward's two
+
+        def step():
+            fa2_bwd(q, k, v, o, do, lse, dq, dk, dv, bws, causal=causal, scale=w.scale)
+    elif args.splits is not None:
         if w.dtype != "bf16":
             print("the split-KV path is bf16 only", file=sys.stderr)
             return 1
@@ -197,14 +214,18 @@ def main(argv=None) -> int:
     achieved = flops / (kernel_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
 
-    traffic = measured_traffic(w.name, causal, w.dtype) if splits is None else None
+    traffic = (measured_traffic(w.name, causal, w.dtype)
+               if splits is None and not args.backward else None)
     kname = f"fa2_fwd_{w.dtype}_kernel<{w.d},{'true' if causal else 'false'}" + (
         ",false>" if w.dtype == "bf16" else ">")
     if splits is not None:
         kname = (f"fa2_fwd_bf16_kernel<{w.d},{'true' if causal else 'false'},true> + "
                  f"fa2_combine_kernel<{w.d}> (both per step; kernel_ms covers the two)")
+    if args.backward:
+        kname = (f"fa2_bwd_prep_kernel<{w.d}> + fa2_bwd_dkdv_kernel<{w.d},{'true' if causal else 'false'}> + "
+                 f"fa2_bwd_dq_kernel<{w.d},{'true' if causal else 'false'}> (all per step; kernel_ms covers the three)")
     out = {
-        "metric": METRIC,
+        "metric": METRIC if not args.backward else METRIC_BWD,
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -219,7 +240,8 @@ def main(argv=None) -> int:
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
                    "causal": causal, "scale": w.scale, "kBlockM": 128,
                    "flops_per_step": flops,
-                   **({"path": "split-KV", "num_splits": splits} if splits is not None else {})},
+                   **({"path": "split-KV", "num_splits": splits} if splits is not None else {}),
+                   **({"path": "backward"} if args.backward else {})},
         "pct_of_peak": round(100.0 * tflops / peak, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
@@ -228,7 +250,7 @@ def main(argv=None) -> int:
                      "kernel_ms": round(kernel_ms, 5),
                      "kernel_source_hash": kernel_source_hash(w.dtype)},
     }
-    if args.cpu_seconds > 0:
+    if args.cpu_seconds > 0 and not args.backward:
         out["cpu_baseline"] = cpu_baseline(w, q_cpu, k_cpu, v_cpu, causal, args.cpu_seconds)
     print(json.dumps(out), flush=True)
     return 0

@@ -48,22 +48,24 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kRows = 32 * kWaves;  // keys (dK/dV) or queries (dQ) per workgroup
 constexpr int kStep = 64;           // queries (dK/dV) or keys (dQ) per inner step
 
-// Byte offset of element (row r, dim c) of a staged [64][D] bf16 tile.
+// Byte offset of element (row r, dim c) of a staged [rows][D] bf16 tile.
 template <int D>
 __device__ __forceinline__ constexpr int toff(int r, int c) {
   return (r >> 2) * (8 * D) + (c >> 4) * 128 + 32 * (r & 3) + 2 * (c & 15);
 }
 
-// Stage rows [r0, r0 + 64) of a [N][D] bf16 slice into LDS in the tile layout
+// Stage rows [r0, r0 + ROWS) of a [N][D] bf16 slice into LDS in the tile layout
 // (rows past N are clamped to row N - 1; callers mask them).  Load i of this
 // thread fills 1 KB chunk n = wave*LOADS + i: its lane L writes 16 bytes, row
 // 4*(bk / NSEG) + (L%8)/2 and dims 16*(bk % NSEG) + 8*(L%2) of 128-byte block
 // bk = 8n + L/8.
-template <int D>
+template <int D, int ROWS = kStep>
 __device__ __forceinline__ void stage_tile(const uint16_t* head, int r0, int N, char* buf,
                                            int wave, int lane) {
   constexpr int NSEG = D / 16;
-  constexpr int LOADS = kStep * D * 2 / 1024 / kWaves;
+  constexpr int LOADS = ROWS * D * 2 / 1024 / kWaves;
+  static_assert(LOADS >= 1 && ROWS * D * 2 % (1024 * kWaves) == 0, "tile splits over the waves");
+  lane = fresh_lane();  // recomputed here: not kept in registers across the loop
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
     const int n = wave * LOADS + i;
@@ -82,32 +84,43 @@ __device__ __forceinline__ void stage_vec(const float* v, int r0, int N, char* b
                : : "s"(lds_addr(buf)), "v"(src) : "memory", "m0");
 }
 
-// A operand of a 32x32x16 MFMA from a staged tile, rows m = row0 + lane%32
-// and dims 16*ks + 8*(lane/32) .. +8: one 16-byte read.
+// LDS addresses of fragments in a staged tile, as one per-lane base (computed
+// once) plus compile-time offsets.
+//
+// Row fragment: the A operand of a 32x32x16 MFMA, rows m = row0 + lane%32 and
+// dims 16*ks + 8*(lane/32) .. +8, one 16-byte read at
+//   row_base(lane) + (row0/4)*8D + 128*ks,
+//   row_base(lane) = ((lane%32)/4)*8D + 32*(lane%4) + 16*(lane/32).
 template <int D>
-__device__ __forceinline__ bf16x8_t row_frag(const char* tile, int row0, int ks, int lane) {
-  return *(const bf16x8_t*)(tile + toff<D>(row0 + (lane & 31), 16 * ks + 8 * (lane >> 5)));
+__device__ __forceinline__ uint32_t row_base(int lane) {
+  return (uint32_t)(((lane & 31) >> 2) * (8 * D) + 32 * (lane & 3) + 16 * (lane >> 5));
 }
-
-// A operand (the transpose of a staged tile: dims x rows) for rows 16u .. 16u+15
-// of the tile and dims 32t .. 32t+31, in the permuted row order that matches a
-// B operand packed from accumulator registers 8*(u%2) .. 8*(u%2)+7 of the
-// 32-row tile u/2.  Within each 16-lane group, lane 4*r + c points at 4
-// consecutive dims of row kbase + r; ds_read_b64_tr_b16 hands lane t of the
-// group the 4 rows kbase .. kbase+3 of dim t.  kbase = 16u + 4*half (first 4
-// slots of the operand) and 16u + 8 + 4*half (last 4).
 template <int D>
-__device__ __forceinline__ bf16x8_t tr_frag(const char* tile, int u, int t, int lane) {
-  const int g = lane >> 4, i = lane & 15;
-  const int half = lane >> 5;
-  const int rb = 16 * u + 4 * half;  // first row of the first 4
-  const int c = 32 * t + 16 * (g & 1) + 4 * (i & 3);
-  const char* p_lo = tile + toff<D>(rb + (i >> 2), c);
-  const char* p_hi = tile + toff<D>(rb + 8 + (i >> 2), c);
-  const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr_t)p_lo);
-  const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr_t)p_hi);
+__device__ __forceinline__ bf16x8_t row_frag(const char* tile, uint32_t rbase, int row0, int ks) {
+  return *(const bf16x8_t*)(tile + rbase + (row0 / 4) * (8 * D) + 128 * ks);
+}
+// Transposed fragment: the A operand (dims x rows) for rows 16u .. 16u+15 of
+// the tile and dims 32t .. 32t+31, in the permuted row order that matches a B
+// operand packed from accumulator registers 8*(u%2) .. 8*(u%2)+7 of the
+// 32-row tile u/2.  Within each 16-lane group (g = lane/16, i = lane%16),
+// lane 4*r + c points at 4 consecutive dims of row kbase + r;
+// ds_read_b64_tr_b16 hands lane t of the group the 4 rows kbase .. kbase+3 of
+// dim t.  kbase = 16u + 4*half (first 4 slots) and 16u + 8 + 4*half (last 4),
+// so the group reads one whole 128-byte block of the layout:
+//   tr_base(lane) = half*8D + 128*(g%2) + 8*i,
+//   + 32D*u + 256*t, and + 16D for the last 4.
+template <int D>
+__device__ __forceinline__ uint32_t tr_base(int lane) {
+  return (uint32_t)((lane >> 5) * (8 * D) + 128 * ((lane >> 4) & 1) + 8 * (lane & 15));
+}
+template <int D>
+__device__ __forceinline__ bf16x8_t tr_frag(const char* tile, uint32_t tbase, int u, int t) {
+  const char* p = tile + tbase + 32 * D * u + 256 * t;
+  const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr_t)p);
+  const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr_t)(p + 16 * D));
   return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
+static_assert(toff<128>(5, 40) == 1 * 1024 + 2 * 128 + 32 * 1 + 2 * 8, "tile layout");
 
 // B operand fragments of a [N][D] bf16 slice held in registers: for k-step ks,
 // lane l holds row r0 + l%32, dims 16*ks + 8*(l/32) .. +8 (zero past N).
@@ -128,10 +141,15 @@ __device__ __forceinline__ void load_frags(bf16x8_t (&f)[D / 16], const uint16_t
 template <int D>
 __device__ __forceinline__ void store_rows(const f32x16_t (&acc)[D / 32], float mul,
                                            uint16_t* head, int row0, int N, int lane) {
-  const int rows = max(0, min(32, N - row0));  // 0 for a wavefront past the end: no store lands
-  const __amdgpu_buffer_rsrc_t rs =
-      __builtin_amdgcn_make_buffer_rsrc(head + (size_t)row0 * D, (short)0, rows * D * 2,
-                                        kBufferFlags);
+  // 0 rows for a wavefront past the end: no store lands.  Both values are
+  // uniform; readfirstlane keeps the resource in scalar registers (otherwise
+  // the compiler wraps every store in a loop over distinct resources).
+  const int rows = __builtin_amdgcn_readfirstlane(max(0, min(32, N - row0)));
+  const uint64_t base = (uint64_t)(head + (size_t)row0 * D);
+  const uint64_t ubase = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(base >> 32)) << 32) |
+                         (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)base);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)ubase, (short)0, rows * D * 2, kBufferFlags);
   const int half = lane >> 5, col = lane & 31;
 #pragma unroll
   for (int t = 0; t < D / 32; ++t)
@@ -166,16 +184,21 @@ fa2_bwd_prep_kernel(const uint16_t* __restrict__ O, const uint16_t* __restrict__
 }
 
 // ---------------------------------------------------------------- dK, dV
+// Queries per step of the K/V-outer kernel: one 32-query tile, which keeps the
+// live registers (K and V fragments, dK and dV accumulators, one S and one dP
+// tile) within 256 so that two wavefronts share each SIMD.
+constexpr int kQStep = 32;
+
 template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(kThreads, 1)
+__global__ void __launch_bounds__(kThreads, 2)
 fa2_bwd_dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
                     const uint16_t* __restrict__ Vg, const uint16_t* __restrict__ dOg,
                     const float* __restrict__ Lg, const float* __restrict__ Dg,
                     uint16_t* __restrict__ dKg, uint16_t* __restrict__ dVg, int N,
                     int num_k_block, float c, float scale) {
   constexpr int KS = D / 16, DT = D / 32;
-  constexpr int TILE = kStep * D * 2;  // bytes of one staged [64][D] tile
-  // Q, dO tiles, then the 64 L and 64 D values, for two steps.
+  constexpr int TILE = kQStep * D * 2;  // bytes of one staged [32][D] tile
+  // Q, dO tiles, then 64 L and 64 D values (32 used), for two steps.
   __shared__ __attribute__((aligned(1024))) char smem[2 * (2 * TILE + 512)];
 
   const int lane = threadIdx.x & 63;
@@ -188,6 +211,7 @@ fa2_bwd_dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict_
   const uint16_t *Qh = Qg + slice, *dOh = dOg + slice;
   const float *Lh = Lg + (size_t)bh * N, *Dh = Dg + (size_t)bh * N;
   const int k0 = kb * kRows + 32 * wave;  // this wavefront's first key
+  const uint32_t rbase = row_base<D>(lane), tbase = tr_base<D>(lane);
 
   bf16x8_t kf[KS], vf[KS];
   load_frags<D>(kf, Kg + slice, k0 + col, N, half);
@@ -197,15 +221,15 @@ fa2_bwd_dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict_
   for (int t = 0; t < DT; ++t) dk[t] = dv[t] = f32x16_t{};
 
   // Query steps: from the first that can see the block's keys to the end.
-  const int i_beg = CAUSAL ? (kb * kRows) / kStep : 0;
-  const int i_end = (N + kStep - 1) / kStep;
+  const int i_beg = CAUSAL ? (kb * kRows) / kQStep : 0;
+  const int i_end = (N + kQStep - 1) / kQStep;
   auto buf = [&](int i) { return smem + (i & 1) * (2 * TILE + 512); };
   auto stage = [&](int i) {
     char* b = buf(i);
-    stage_tile<D>(Qh, i * kStep, N, b, wave, lane);
-    stage_tile<D>(dOh, i * kStep, N, b + TILE, wave, lane);
-    if (wave == 0) stage_vec(Lh, i * kStep, N, b + 2 * TILE, lane);
-    if (wave == 1) stage_vec(Dh, i * kStep, N, b + 2 * TILE + 256, lane);
+    stage_tile<D, kQStep>(Qh, i * kQStep, N, b, wave, lane);
+    stage_tile<D, kQStep>(dOh, i * kQStep, N, b + TILE, wave, lane);
+    if (wave == 0) stage_vec(Lh, i * kQStep, N, b + 2 * TILE, lane);
+    if (wave == 1) stage_vec(Dh, i * kQStep, N, b + 2 * TILE + 256, lane);
   };
   if (i_beg < i_end) stage(i_beg);
   for (int i = i_beg; i < i_end; ++i) {
@@ -216,46 +240,42 @@ fa2_bwd_dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict_
     const char* qtile = b;
     const char* dtile = b + TILE;
     const float* lv = (const float*)(b + 2 * TILE);
-    const float* dv_ = (const float*)(b + 2 * TILE + 256);
-    const int q_base = i * kStep;
-    bf16x8_t pb[4], sb[4];
+    const float* dvec = (const float*)(b + 2 * TILE + 256);
+    const int q_base = i * kQStep;
+    f32x16_t S = f32x16_t{}, dP = f32x16_t{};
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-      f32x16_t S = f32x16_t{}, dP = f32x16_t{};
+    for (int ks = 0; ks < KS; ++ks) {
+      S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(qtile, rbase, 0, ks), kf[ks], S, 0,
+                                                  0, 0);
+      dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(dtile, rbase, 0, ks), vf[ks], dP,
+                                                   0, 0, 0);
+    }
+    // This lane's key is k0 + col; accumulator r holds query
+    // q_base + 8*(r/4) + 4*half + r%4.
+    bf16x8_t pb[2], sb[2];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(qtile, 32 * qt, ks, lane), kf[ks],
-                                                    S, 0, 0, 0);
-        dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(dtile, 32 * qt, ks, lane), vf[ks],
-                                                     dP, 0, 0, 0);
-      }
-      // This lane's key is k0 + col; accumulator r holds query
-      // q_base + 32*qt + 8*(r/4) + 4*half + r%4.
+    for (int g = 0; g < 4; ++g) {
+      const int qr = 8 * g + 4 * half;  // first of 4 consecutive queries
+      const f32x4_t L4 = *(const f32x4_t*)(lv + qr);
+      const f32x4_t D4 = *(const f32x4_t*)(dvec + qr);
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int qr = 32 * qt + 8 * g + 4 * half;  // first of 4 consecutive queries
-        const f32x4_t L4 = *(const f32x4_t*)(lv + qr);
-        const f32x4_t D4 = *(const f32x4_t*)(dv_ + qr);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int q = q_base + qr + r;
-          const bool hide = q >= N || (CAUSAL && k0 + col > q);
-          const float p = hide ? 0.f
-                               : __builtin_amdgcn_exp2f(__builtin_fmaf(S[g * 4 + r], c,
-                                                                       -L4[r] * kLog2e));
-          const float ds = p * (dP[g * 4 + r] - D4[r]);
-          pb[qt * 2 + g / 2][(g % 2) * 4 + r] = (__bf16)p;
-          sb[qt * 2 + g / 2][(g % 2) * 4 + r] = (__bf16)ds;
-        }
+      for (int r = 0; r < 4; ++r) {
+        const int q = q_base + qr + r;
+        const bool hide = q >= N || (CAUSAL && k0 + col > q);
+        const float p = hide ? 0.f
+                             : __builtin_amdgcn_exp2f(__builtin_fmaf(S[g * 4 + r], c,
+                                                                     -L4[r] * kLog2e));
+        pb[g / 2][(g % 2) * 4 + r] = (__bf16)p;
+        sb[g / 2][(g % 2) * 4 + r] = (__bf16)(p * (dP[g * 4 + r] - D4[r]));
       }
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int t = 0; t < DT; ++t) {
-        dv[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(dtile, u, t, lane), pb[u],
+        dv[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(dtile, tbase, u, t), pb[u],
                                                         dv[t], 0, 0, 0);
-        dk[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(qtile, u, t, lane), sb[u],
+        dk[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(qtile, tbase, u, t), sb[u],
                                                         dk[t], 0, 0, 0);
       }
   }
@@ -284,6 +304,7 @@ fa2_bwd_dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ 
   const uint16_t *Kh = Kg + slice, *Vh = Vg + slice;
   const int q0 = m * kRows + 32 * wave;
   const int qrow = q0 + col;
+  const uint32_t rbase = row_base<D>(lane), tbase = tr_base<D>(lane);
 
   bf16x8_t qf[KS], df[KS];
   load_frags<D>(qf, Qg + slice, qrow, N, half);
@@ -313,9 +334,9 @@ fa2_bwd_dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ 
       f32x16_t S = f32x16_t{}, dP = f32x16_t{};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(kt_, 32 * kt, ks, lane), qf[ks], S,
-                                                    0, 0, 0);
-        dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(vt, 32 * kt, ks, lane), df[ks],
+        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(kt_, rbase, 32 * kt, ks), qf[ks],
+                                                    S, 0, 0, 0);
+        dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(vt, rbase, 32 * kt, ks), df[ks],
                                                      dP, 0, 0, 0);
       }
       // This lane's query is qrow; accumulator r holds key
@@ -332,8 +353,8 @@ fa2_bwd_dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ 
     for (int u = 0; u < 4; ++u)
 #pragma unroll
       for (int t = 0; t < DT; ++t)
-        dq[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(kt_, u, t, lane), sb[u], dq[t],
-                                                        0, 0, 0);
+        dq[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(kt_, tbase, u, t), sb[u],
+                                                        dq[t], 0, 0, 0);
   }
   store_rows<D>(dq, scale, dQg + slice, q0, N, lane);
 }

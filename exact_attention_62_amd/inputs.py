@@ -116,3 +116,12 @@ def make_random(B: int, H: int, N: int, d: int, seed: int, dtype: str = "bf16",
     k = (torch.randn(shape, generator=gen) * sigma).to(dt).contiguous()
     v = torch.randn(shape, generator=gen).to(dt).contiguous()
     return q, k, v
+
+
+def make_upstream(B: int, H: int, N: int, d: int, seed: int, dtype: str = "bf16"):
+    """The upstream gradient dO for backward-pass problems: N(0, 1), seeded separately from
+    the inputs (generator seed 0x6D0E0000 + seed)."""
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(0x6D0E0000 + int(seed))
+    dt = {"bf16": torch.bfloat16, "fp32": torch.float32}[dtype]
+    return torch.randn((B, H, N, d), generator=gen).to(dt).contiguous()

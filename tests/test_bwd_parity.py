@@ -21,7 +21,7 @@ import pytest
 import torch
 
 from exact_attention_62_amd import FlashAttention, attention, attention_backward
-from exact_attention_62_amd.inputs import make_random
+from exact_attention_62_amd.inputs import make_random, make_upstream
 from oracle.backward import attention_bwd_fp64
 
 pytestmark = pytest.mark.gpu
@@ -42,9 +42,7 @@ def _say(msg):
 
 def _grad_inputs(B, H, N, d, seed):
     q, k, v = make_random(B, H, N, d, seed=seed)
-    g = torch.Generator().manual_seed(0x5EED0000 + 7 * seed + 1)
-    do = torch.randn(B, H, N, d, generator=g).to(torch.bfloat16)
-    return q, k, v, do
+    return q, k, v, make_upstream(B, H, N, d, seed=seed)
 
 
 def _check(got, ref, what):

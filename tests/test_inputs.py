@@ -30,3 +30,13 @@ def test_make_random_shapes():
     q, k, v = make_random(2, 3, 17, 64, seed=5)
     assert q.shape == (2, 3, 17, 64) and v.dtype == torch.bfloat16
     assert q.is_contiguous() and k.is_contiguous() and v.is_contiguous()
+
+
+def test_make_upstream_is_seeded_and_independent_of_the_inputs():
+    from exact_attention_62_amd.inputs import make_random, make_upstream
+    a = make_upstream(1, 2, 33, 64, seed=3)
+    assert a.shape == (1, 2, 33, 64) and a.dtype == torch.bfloat16
+    assert torch.equal(a, make_upstream(1, 2, 33, 64, seed=3))
+    assert not torch.equal(a, make_upstream(1, 2, 33, 64, seed=4))
+    q, _, _ = make_random(1, 2, 33, 64, seed=3)
+    assert not torch.equal(a, q)
