@@ -251,7 +251,13 @@ fa2_bwd_dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict_
                                                    0, 0, 0);
     }
     // This lane's key is k0 + col; accumulator r holds query
-    // q_base + 8*(r/4) + 4*half + r%4.
+    // q_base + cr + 4*half with cr = 8*(r/4) + r%4 (a constant).  The query is
+    // visible to the key when lo <= cr < hi (at or after the key, before N);
+    // steps that lie wholly after the wavefront's keys and before N need no
+    // test (uniform for the wavefront).
+    const bool clean = q_base + kQStep <= N && (!CAUSAL || q_base >= k0 + 31);
+    const int lo = CAUSAL ? k0 + col - q_base - 4 * half : -1;
+    const int hi = N - q_base - 4 * half;
     bf16x8_t pb[2], sb[2];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
@@ -260,11 +266,9 @@ fa2_bwd_dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict_
       const f32x4_t D4 = *(const f32x4_t*)(dvec + qr);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int q = q_base + qr + r;
-        const bool hide = q >= N || (CAUSAL && k0 + col > q);
-        const float p = hide ? 0.f
-                             : __builtin_amdgcn_exp2f(__builtin_fmaf(S[g * 4 + r], c,
-                                                                     -L4[r] * kLog2e));
+        const int cr = 8 * g + r;
+        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(S[g * 4 + r], c, -L4[r] * kLog2e));
+        if (!clean) p = (cr < lo || cr >= hi) ? 0.f : p;
         pb[g / 2][(g % 2) * 4 + r] = (__bf16)p;
         sb[g / 2][(g % 2) * 4 + r] = (__bf16)(p * (dP[g * 4 + r] - D4[r]));
       }
@@ -285,7 +289,7 @@ fa2_bwd_dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict_
 
 // ---------------------------------------------------------------- dQ
 template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(kThreads, 1)
+__global__ void __launch_bounds__(kThreads, 2)
 fa2_bwd_dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
                   const uint16_t* __restrict__ Vg, const uint16_t* __restrict__ dOg,
                   const float* __restrict__ Lg, const float* __restrict__ Dg,
@@ -328,6 +332,7 @@ fa2_bwd_dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ 
     if (j + 1 < j_end) stage(j + 1);
     const char* kt_ = buf(j);
     const char* vt = buf(j) + TILE;
+    const bool clean = (j + 1) * kStep <= N && (!CAUSAL || (j + 1) * kStep - 1 <= q0);
     bf16x8_t sb[4];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
@@ -340,12 +345,17 @@ fa2_bwd_dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ 
                                                      dP, 0, 0, 0);
       }
       // This lane's query is qrow; accumulator r holds key
-      // j*64 + 32*kt + 8*(r/4) + 4*half + r%4.
+      // j*64 + 32*kt + cr + 4*half with cr = 8*(r/4) + r%4 (a constant),
+      // visible when cr <= th (at or before the query, before N).  Blocks wholly
+      // before the wavefront's first query and before N need no test.
+      const int kb0 = j * kStep + 32 * kt + 4 * half;
+      int th = N - 1 - kb0;
+      if (CAUSAL) th = min(th, qrow - kb0);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = j * kStep + 32 * kt + 8 * (r / 4) + 4 * half + (r % 4);
-        const bool hide = key >= N || (CAUSAL && key > qrow);
-        const float p = hide ? 0.f : __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], c, -l2));
+        const int cr = 8 * (r / 4) + (r % 4);
+        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], c, -l2));
+        if (!clean) p = cr > th ? 0.f : p;
         sb[kt * 2 + r / 8][r % 8] = (__bf16)(p * (dP[r] - dd));
       }
     }
