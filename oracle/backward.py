@@ -43,12 +43,19 @@ def _f64(x) -> np.ndarray:
 
 
 def _probs(q, k, causal, scale):
+    """Row softmax of the masked logits; a row that sees no key has P = 0."""
+    Nq, Nk = q.shape[0], k.shape[0]
     S = scale * (q @ k.T)
     if causal:
-        S = np.where(np.arange(k.shape[0])[None, :] > np.arange(q.shape[0])[:, None], -np.inf, S)
+        S = np.where(np.arange(Nk)[None, :] > np.arange(Nq)[:, None] + (Nk - Nq), -np.inf, S)
+    P = np.zeros_like(S)
+    if Nk == 0:
+        return P
     m = S.max(axis=1, keepdims=True)
-    P = np.exp(S - m)
-    return P / P.sum(axis=1, keepdims=True)
+    seen = np.isfinite(m[:, 0])
+    P[seen] = np.exp(S[seen] - m[seen])
+    P[seen] /= P[seen].sum(axis=1, keepdims=True)
+    return P
 
 
 def delta_fp64(o, do):
@@ -57,7 +64,11 @@ def delta_fp64(o, do):
 
 
 def attention_bwd_fp64(q, k, v, do, causal: bool = False, scale: float | None = None):
-    """(dQ, dK, dV), each [B, H, N, d] float64, for O = attention(q, k, v) and upstream dO."""
+    """(dQ [B,H,Nq,d], dK, dV [B,H,Nk,d]) in float64, for O = attention(q, k, v) and upstream dO.
+
+    q and do are [B, H, Nq, d], k and v [B, H, Nk, d]; the causal mask is aligned
+    bottom-right as in the forward oracle, and rows that see no key (P = 0) add nothing.
+    """
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
     B, H, N, d = q.shape
     if scale is None:

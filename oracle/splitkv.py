@@ -52,27 +52,29 @@ def _f64(x) -> np.ndarray:
 
 def attention_keyrange_fp64(q, k, v, lo: int, hi: int, causal: bool = False,
                             scale: float | None = None):
-    """Partial attention over keys [lo, hi) of every row: (O_s [B,H,N,d], L_s [B,H,N]).
+    """Partial attention over keys [lo, hi) of every row: (O_s [B,H,Nq,d], L_s [B,H,Nq]).
 
-    Plain definition per row (no tiling): S = scale * q k^T over the keys in the
-    range, the causal mask hides keys j > i, then m, P = exp(S - m), l, O = P V / l,
-    L = m + ln l.  Rows with no visible key: O = 0, L = -inf.
+    q is [B, H, Nq, d], k and v [B, H, Nk, d].  Plain definition per row (no
+    tiling): S = scale * q k^T over the keys in the range, the causal mask hides
+    keys j > i + Nk - Nq (bottom-right aligned), then m, P = exp(S - m), l,
+    O = P V / l, L = m + ln l.  Rows with no visible key: O = 0, L = -inf.
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
-    B, H, N, d = q.shape
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    O = np.zeros((B, H, N, d))
-    L = np.full((B, H, N), -np.inf)
-    lo, hi = max(0, lo), min(N, hi)
+    O = np.zeros((B, H, Nq, d))
+    L = np.full((B, H, Nq), -np.inf)
+    lo, hi = max(0, lo), min(Nk, hi)
     if hi <= lo:
         return O, L
     keys = np.arange(lo, hi)
     for b in range(B):
         for h in range(H):
-            S = scale * (q[b, h] @ k[b, h, lo:hi].T)  # [N, hi-lo]
+            S = scale * (q[b, h] @ k[b, h, lo:hi].T)  # [Nq, hi-lo]
             if causal:
-                S = np.where(keys[None, :] > np.arange(N)[:, None], -np.inf, S)
+                S = np.where(keys[None, :] > np.arange(Nq)[:, None] + (Nk - Nq), -np.inf, S)
             m = S.max(axis=1)
             seen = np.isfinite(m)
             P = np.exp(S[seen] - m[seen, None])
@@ -86,15 +88,19 @@ def combine_fp64(O_parts, L_parts):
     """Merge partial results: O_parts [S,...,d], L_parts [S,...] -> (O [...,d], L [...]).
 
     L = ln sum_s exp(L_s) (evaluated as max + ln sum exp(L_s - max)) and
-    O = sum_s exp(L_s - L) O_s.  Every row must have at least one finite L_s.
+    O = sum_s exp(L_s - L) O_s.  A row whose every L_s is -inf saw no key in any
+    range: its sum is empty, L = -inf and O = 0.
     """
     O_parts = np.asarray(O_parts, dtype=np.float64)
     L_parts = np.asarray(L_parts, dtype=np.float64)
     Lmax = L_parts.max(axis=0)
-    w = np.exp(L_parts - Lmax[None])  # exp(-inf) = 0 for empty ranges
+    seen = np.isfinite(Lmax)
+    ref = np.where(seen, Lmax, 0.0)
+    w = np.exp(L_parts - ref[None])  # exp(-inf) = 0 for empty ranges
     tot = w.sum(axis=0)
-    L = Lmax + np.log(tot)
-    O = (w[..., None] * O_parts).sum(axis=0) / tot[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        L = np.where(seen, ref + np.log(tot), -np.inf)
+        O = np.where(seen[..., None], (w[..., None] * O_parts).sum(axis=0) / tot[..., None], 0.0)
     return O, L
 
 

@@ -145,3 +145,42 @@ def test_every_planted_mistake_is_caught(kind):
     got = _broken(kind)(q, k, v, do, True, 0.3)
     ref = _autograd(q, k, v, do, True, 0.3)
     assert max(np.abs(g - r).max() for g, r in zip(got, ref)) > 1e-6
+
+
+# ---- query and key lengths that differ (bottom-right causal alignment) ----------------------
+@pytest.mark.parametrize("Nq,Nk", [(3, 11), (11, 3), (1, 9), (16, 16)])
+def test_noncausal_lengths_against_autograd(Nq, Nk):
+    g = np.random.default_rng(Nq * 31 + Nk)
+    q, do = g.standard_normal((2, 2, 2, Nq, 8))
+    k, v = g.standard_normal((2, 2, 2, Nk, 8))
+    got = attention_bwd_fp64(q, k, v, do, False, 0.35)
+    ref = _autograd(q, k, v, do, False, 0.35)
+    for a, b in zip(got, ref):
+        assert a.shape == b.shape and np.abs(a - b).max() < 1e-12
+
+
+@pytest.mark.parametrize("Nq,Nk", [(1, 9), (4, 13), (12, 13)])
+def test_short_queries_are_the_last_rows_of_the_square_problem(Nq, Nk):
+    # The square causal problem with Nk queries, the first Nk - Nq of which have dO = 0:
+    # those rows add nothing to dK and dV, and the other rows see exactly the keys the
+    # bottom-right mask gives the Nq queries.
+    g = np.random.default_rng(Nq + 7 * Nk)
+    qf, dof, k, v = g.standard_normal((4, 1, 2, Nk, 6))
+    dof[:, :, :Nk - Nq] = 0.0
+    dQf, dKf, dVf = _autograd(qf, k, v, dof, True, 0.45)
+    dQ, dK, dV = attention_bwd_fp64(qf[:, :, Nk - Nq:], k, v, dof[:, :, Nk - Nq:], True, 0.45)
+    assert np.abs(dQ - dQf[:, :, Nk - Nq:]).max() < 1e-12
+    assert np.abs(dK - dKf).max() < 1e-12 and np.abs(dV - dVf).max() < 1e-12
+
+
+@pytest.mark.parametrize("Nq,Nk", [(9, 1), (13, 4)])
+def test_excess_queries_get_zero_gradient(Nq, Nk):
+    g = np.random.default_rng(Nq + 5 * Nk)
+    q, do = g.standard_normal((2, 1, 1, Nq, 6))
+    k, v = g.standard_normal((2, 1, 1, Nk, 6))
+    dQ, dK, dV = attention_bwd_fp64(q, k, v, do, True, 0.45)
+    e = Nq - Nk
+    assert np.all(dQ[:, :, :e] == 0.0)
+    dQs, dKs, dVs = _autograd(q[:, :, e:], k, v, do[:, :, e:], True, 0.45)
+    assert np.abs(dQ[:, :, e:] - dQs).max() < 1e-12
+    assert np.abs(dK - dKs).max() < 1e-12 and np.abs(dV - dVs).max() < 1e-12

@@ -166,3 +166,31 @@ def test_split_ranges_partition(n_blocks, s):
     r = split_ranges(n_blocks, s)
     assert len(r) == s and r[0][0] == 0 and r[-1][1] == n_blocks
     assert all(a <= b for a, b in r) and all(r[i][1] == r[i + 1][0] for i in range(s - 1))
+
+
+# ---- query and key lengths that differ (bottom-right causal alignment) ----------------------
+@pytest.mark.parametrize("Nq,Nk,bounds", [(5, 40, [0, 13, 27, 40]), (40, 12, [0, 5, 12]),
+                                          (1, 64, [0, 32, 64]), (33, 33, [0, 16, 33])])
+@pytest.mark.parametrize("causal", [False, True])
+def test_merge_with_different_lengths_is_the_definition(Nq, Nk, bounds, causal):
+    g = np.random.default_rng(Nq * 100 + Nk)
+    q = g.standard_normal((1, 2, Nq, 8))
+    k, v = g.standard_normal((2, 1, 2, Nk, 8))
+    parts = [attention_keyrange_fp64(q, k, v, lo, hi, causal, 0.5) for lo, hi in zip(bounds, bounds[1:])]
+    O, L = combine_fp64([p[0] for p in parts], [p[1] for p in parts])
+    Oref, Lref = attention_fp64(q, k, v, causal=causal, scale=0.5)
+    np.testing.assert_allclose(O, Oref, rtol=0, atol=1e-13)
+    np.testing.assert_array_equal(np.isfinite(L), np.isfinite(Lref))
+    fin = np.isfinite(Lref)
+    np.testing.assert_allclose(L[fin], Lref[fin], rtol=0, atol=1e-13)
+
+
+def test_rows_that_see_no_key_merge_to_zero_and_minus_infinity():
+    q = np.ones((1, 1, 6, 4))
+    k = v = np.ones((1, 1, 2, 4))
+    parts = [attention_keyrange_fp64(q, k, v, lo, hi, True, 1.0) for lo, hi in ((0, 1), (1, 2))]
+    O, L = combine_fp64([p[0] for p in parts], [p[1] for p in parts])
+    # rows 0..3 see no key (j > i + 2 - 6 for every j); row 4 sees key 0, row 5 both
+    assert np.all(O[0, 0, :4] == 0.0) and np.all(L[0, 0, :4] == -np.inf)
+    np.testing.assert_allclose(L[0, 0, 4:], [4.0, 4.0 + math.log(2.0)], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(O[0, 0, 4:], 1.0, rtol=0, atol=1e-15)
