@@ -1,6 +1,7 @@
 """Benchmark of the FlashAttention-2 forward pass on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload train] [--splits S]
+                    [--dtype bf16|fp16] [--B B] [--H H] [--d D] [--q-len NQ] [--kv-len NK]
 
 A step is one fa2_fwd call (the whole hot path: one kernel launch) over the
 workload's inputs (with --splits: one fa2_fwd_splitkv call, the split kernel and
@@ -15,6 +16,14 @@ Prints one JSON line.  ``value`` is TFLOP/s by the metric's count
 algorithmic flops per launch against MI355X's dense bf16 MFMA peak;
 ``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of the same
 workload on this host's cores.
+
+Variants: --dtype, --B, --H, --d, --q-len and --kv-len override the named
+workload's type and shape (same seeded recipe).  With query and key lengths
+that differ, the flop count is 4*d per visible (query, key) pair (the causal
+mask aligned bottom-right), and a problem whose arithmetic intensity is below
+MI355X's ridge point (peak flops / 8 TB/s) is reported against HBM bandwidth
+instead: algorithmic bytes (Q, K, V read once, O and L written once) per
+launch over the kernel time.
 """
 from __future__ import annotations
 
@@ -33,9 +42,13 @@ METRIC = "attention fwd TFLOP/s (4BHN²d, causal halved) and % of bf16 MFMA peak
 METRIC_BWD = "attention bwd TFLOP/s (2.5 x 4BHN²d, causal halved) and % of bf16 MFMA peak"
 # MI355X published dense peaks (256 CUs at 2.4 GHz): bf16 MFMA 2.5 PFLOP/s
 # (256 * 4096 flop/clk * 2.4 GHz = 2516.6 TFLOP/s); fp32 vector 157.3 TFLOP/s.
-PEAK_TFLOPS = {"bf16": 2516.6, "fp32": 157.3}
-KERNEL_SOURCES = {"bf16": "exact_attention_62_amd/csrc/fa2_fwd_bf16.hip",
-                  "fp32": "exact_attention_62_amd/csrc/fa2_fwd_f32.hip"}
+PEAK_TFLOPS = {"bf16": 2516.6, "fp16": 2516.6, "fp32": 157.3}
+PEAK_HBM_GBS = 8000.0
+_FWD16 = ["exact_attention_62_amd/csrc/fa2_fwd_kernel.h", "exact_attention_62_amd/csrc/fa2_device.h"]
+KERNEL_SOURCES = {"bf16": _FWD16 + ["exact_attention_62_amd/csrc/fa2_fwd_bf16.hip"],
+                  "fp16": _FWD16 + ["exact_attention_62_amd/csrc/fa2_fwd_fp16.hip"],
+                  "fp32": ["exact_attention_62_amd/csrc/fa2_fwd_f32.hip"]}
+KERNEL_TYPE = {"bf16": "__bf16", "fp16": "_Float16"}
 
 
 def parse_args(argv=None):
@@ -47,6 +60,14 @@ def parse_args(argv=None):
     p.add_argument("--causal", type=int, choices=(0, 1), default=None,
                    help="override the workload's first mask setting")
     p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--dtype", choices=("bf16", "fp16", "fp32"), default=None,
+                   help="override the workload's element type")
+    p.add_argument("--B", type=int, default=None, help="override the batch size")
+    p.add_argument("--H", type=int, default=None, help="override the head count")
+    p.add_argument("--d", type=int, default=None, help="override the head dimension")
+    p.add_argument("--q-len", type=int, default=None, help="override the query length")
+    p.add_argument("--kv-len", type=int, default=None,
+                   help="key/value length (default: the query length)")
     p.add_argument("--backward", action="store_true",
                    help="time the backward pass (fa2_bwd) instead; flops = 2.5 x the forward's")
     p.add_argument("--splits", type=int, default=None, metavar="S",
@@ -76,7 +97,7 @@ def copy_calibration(mib: int, steps: int) -> int:
 
 def kernel_source_hash(dtype: str) -> str:
     h = hashlib.sha256()
-    for rel in (KERNEL_SOURCES[dtype], "exact_attention_62_amd/csrc/fa2_internal.h"):
+    for rel in KERNEL_SOURCES[dtype] + ["exact_attention_62_amd/csrc/fa2_internal.h"]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -98,7 +119,19 @@ def measured_traffic(workload: str, causal: bool, dtype: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, q, k, v, causal: bool, target_s: float):
+def metric_flops(B: int, H: int, Nq: int, Nk: int, d: int, causal: bool) -> float:
+    """The metric's flop count: 4*B*H*N^2*d (halved when causal) for equal lengths; otherwise
+    4*d per visible (query, key) pair, the causal mask aligned bottom-right."""
+    if Nq == Nk:
+        return 4.0 * B * H * Nq * Nq * d / (2.0 if causal else 1.0)
+    if not causal:
+        return 4.0 * B * H * Nq * Nk * d
+    off = Nk - Nq
+    pairs = sum(min(Nk, max(0, i + 1 + off)) for i in range(Nq))
+    return 4.0 * B * H * pairs * d
+
+
+def cpu_baseline(w, q, k, v, causal: bool, scale: float, target_s: float):
     """Time the fp64 oracle on whole (batch, head) slices until ~target_s seconds pass.
 
     q, k, v are the CPU copies of the very inputs the GPU run used.
@@ -107,26 +140,28 @@ def cpu_baseline(w, q, k, v, causal: bool, target_s: float):
 
     from oracle import attention_fp64
 
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
     attention_fp64(q[:1, :1, :64], k[:1, :1, :64], v[:1, :1, :64], causal=causal)  # warm-up
     heads = 0
     t0 = time.perf_counter()
     elapsed = 0.0
-    while heads < w.B * w.H and (heads == 0 or elapsed < target_s):
-        b, h = divmod(heads, w.H)
+    while heads < B * H and (heads == 0 or elapsed < target_s):
+        b, h = divmod(heads, H)
         attention_fp64(q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1],
-                       causal=causal, scale=w.scale)
+                       causal=causal, scale=scale)
         heads += 1
         elapsed = time.perf_counter() - t0
-    flops = 4.0 * heads * w.N * w.N * w.d / (2.0 if causal else 1.0)
+    flops = metric_flops(1, heads, Nq, Nk, d, causal)
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     return {
         "value": flops / elapsed / 1e12,
         "unit": "TFLOP/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": (f"{heads} of the {w.B * w.H} (batch, head) slices of the {w.name} workload "
-                   f"(all {w.N} rows each, fp64 numpy, full N^2 work even with the mask), "
-                   f"{elapsed:.1f} s; throughput by the metric's flop count"),
+        "sample": (f"{heads} of the {B * H} (batch, head) slices of the {w.name} workload "
+                   f"(all {Nq} rows each over {Nk} keys, fp64 numpy, full work even with the "
+                   f"mask), {elapsed:.1f} s; throughput by the metric's flop count"),
         "seconds": elapsed,
         "blas_threads": int(threads),
         "host_cpus": len(os.sched_getaffinity(0)),
@@ -146,7 +181,7 @@ def main(argv=None) -> int:
 
     import torch
 
-    from exact_attention_62_amd import (fa2_bwd, fa2_bwd_workspace_size, fa2_fwd,
+    from exact_attention_62_amd import (fa2_bwd, fa2_bwd_workspace_size, fa2_fwd, fa2_fwd_cross,
                                         fa2_fwd_splitkv, fa2_num_splits,
                                         fa2_splitkv_workspace_size, load_library)
     from exact_attention_62_amd.inputs import WORKLOADS, make, make_upstream
@@ -157,42 +192,55 @@ def main(argv=None) -> int:
     load_library()
     w = WORKLOADS[args.workload]
     causal = bool(w.causal[0] if args.causal is None else args.causal)
+    dtype = args.dtype or w.dtype
+    B = w.B if args.B is None else args.B
+    H = w.H if args.H is None else args.H
+    d = w.d if args.d is None else args.d
+    Nq = w.N if args.q_len is None else args.q_len
+    Nk = Nq if args.kv_len is None else args.kv_len
+    scale = 1.0 / d ** 0.5
+    overridden = (dtype, B, H, d, Nq, Nk) != (w.dtype, w.B, w.H, w.d, w.N, w.N)
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
 
-    q_cpu, k_cpu, v_cpu = make(w, args.seed)
+    q_cpu, k_cpu, v_cpu = make(w, args.seed, B=B, H=H, N=Nq, d=d, dtype=dtype, Nk=Nk)
     q, k, v = (t.to(dev) for t in (q_cpu, k_cpu, v_cpu))
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
-    flops = w.flops(causal)
+    flops = metric_flops(B, H, Nq, Nk, d, causal)
+    esize = q.element_size()
+    # Algorithmic bytes per launch: Q, K, V read once, O and L written once.
+    alg_bytes = float(B * H * (2 * Nq * d + 2 * Nk * d) * esize + B * H * Nq * 4)
     splits = None
     if args.backward:
-        if w.dtype != "bf16" or w.d not in (64, 128):
-            print("the backward pass is bf16 with d = 64 or 128", file=sys.stderr)
+        if dtype != "bf16" or d not in (64, 128) or Nq != Nk:
+            print("the backward pass is bf16 with d = 64 or 128 and equal lengths", file=sys.stderr)
             return 1
-        fa2_fwd(q, k, v, o, lse, causal=causal, scale=w.scale)
-        do = make_upstream(w.B, w.H, w.N, w.d, args.seed).to(dev)
+        fa2_fwd(q, k, v, o, lse, causal=causal, scale=scale)
+        do = make_upstream(B, H, Nq, d, args.seed).to(dev)
         dq, dk, dv = (torch.empty_like(q) for _ in range(3))
-        bws = torch.empty(fa2_bwd_workspace_size(w.B, w.H, w.N, w.d), dtype=torch.uint8,
-                          device=dev)
+        bws = torch.empty(fa2_bwd_workspace_size(B, H, Nq, d), dtype=torch.uint8, device=dev)
         flops = 2.5 * flops  # five products to the forward's two
 
         def step():
-            fa2_bwd(q, k, v, o, do, lse, dq, dk, dv, bws, causal=causal, scale=w.scale)
+            fa2_bwd(q, k, v, o, do, lse, dq, dk, dv, bws, causal=causal, scale=scale)
     elif args.splits is not None:
-        if w.dtype != "bf16":
-            print("the split-KV path is bf16 only", file=sys.stderr)
+        if dtype == "fp32":
+            print("the split-KV path is for bf16 and fp16", file=sys.stderr)
             return 1
-        splits = args.splits if args.splits > 0 else fa2_num_splits(w.B, w.H, w.N, w.d)
-        ws = torch.empty(fa2_splitkv_workspace_size(w.B, w.H, w.N, w.d, splits), dtype=torch.uint8,
+        splits = args.splits if args.splits > 0 else fa2_num_splits(B, H, Nq, Nk, d)
+        ws = torch.empty(fa2_splitkv_workspace_size(B, H, Nq, Nk, d, splits), dtype=torch.uint8,
                          device=dev)
 
         def step():
-            fa2_fwd_splitkv(q, k, v, o, lse, ws, num_splits=splits, causal=causal, scale=w.scale)
+            fa2_fwd_splitkv(q, k, v, o, lse, ws, num_splits=splits, causal=causal, scale=scale)
+    elif Nq != Nk:
+        def step():
+            fa2_fwd_cross(q, k, v, o, lse, causal=causal, scale=scale)
     else:
         def step():
-            fa2_fwd(q, k, v, o, lse, causal=causal, scale=w.scale)
+            fa2_fwd(q, k, v, o, lse, causal=causal, scale=scale)
 
     for _ in range(args.warmup):
         step()
@@ -212,18 +260,34 @@ def main(argv=None) -> int:
     ms_per_step = wall * 1e3 / args.steps
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (kernel_ms * 1e-3) / 1e12
-    peak = PEAK_TFLOPS[w.dtype]
+    peak = PEAK_TFLOPS[dtype]
+    # Below the ridge point (peak flops per HBM byte) the roofline is bandwidth.
+    hbm_bound = not args.backward and flops / alg_bytes < peak * 1e12 / (PEAK_HBM_GBS * 1e9)
 
-    traffic = (measured_traffic(w.name, causal, w.dtype)
-               if splits is None and not args.backward else None)
-    kname = f"fa2_fwd_{w.dtype}_kernel<{w.d},{'true' if causal else 'false'}" + (
-        ",false>" if w.dtype == "bf16" else ">")
+    traffic = (measured_traffic(w.name, causal, dtype)
+               if splits is None and not args.backward and not overridden else None)
+    c = "true" if causal else "false"
+    if dtype == "fp32":
+        kname = f"fa2_fwd_f32_kernel<{d}, {c}>"
+    else:
+        kname = f"fa2_fwd_kernel<{KERNEL_TYPE[dtype]}, {d}, {c}, {'true' if splits else 'false'}>"
     if splits is not None:
-        kname = (f"fa2_fwd_bf16_kernel<{w.d},{'true' if causal else 'false'},true> + "
-                 f"fa2_combine_kernel<{w.d}> (both per step; kernel_ms covers the two)")
+        kname += (f" + fa2_combine_kernel<{KERNEL_TYPE[dtype]}, {d}> (both per step; kernel_ms "
+                  f"covers the two)")
     if args.backward:
-        kname = (f"fa2_bwd_prep_kernel<{w.d}> + fa2_bwd_dkdv_kernel<{w.d},{'true' if causal else 'false'}> + "
-                 f"fa2_bwd_dq_kernel<{w.d},{'true' if causal else 'false'}> (all per step; kernel_ms covers the three)")
+        kname = (f"fa2_bwd_prep_kernel<{d}> + fa2_bwd_dkdv_kernel<{d}, {c}> + "
+                 f"fa2_bwd_dq_kernel<{d}, {c}> (all per step; kernel_ms covers the three)")
+    if hbm_bound:
+        gbs = alg_bytes / (kernel_ms * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
+                    "algorithmic_bytes": alg_bytes, "mfma_tflops": round(achieved, 2)}
+    else:
+        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                    "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic}
+    roofline.update({"kernel": kname, "kernel_ms": round(kernel_ms, 5),
+                     "kernel_source_hash": kernel_source_hash(dtype)})
+    name = w.name if not overridden else f"{w.name}-variant"
     out = {
         "metric": METRIC if not args.backward else METRIC_BWD,
         "value": round(tflops, 2),
@@ -235,23 +299,19 @@ def main(argv=None) -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": w.dtype,
+        "dtype": dtype,
         "data": "synthetic (seeded normal Q, K, V; see exact_attention_62_amd/inputs.py)",
-        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
-                   "causal": causal, "scale": w.scale, "kBlockM": 128,
+        "config": {"workload": name, "B": B, "H": H, "N": Nq, "d": d,
+                   **({"Nk": Nk} if Nk != Nq else {}),
+                   "causal": causal, "scale": scale, "kBlockM": 128,
                    "flops_per_step": flops,
                    **({"path": "split-KV", "num_splits": splits} if splits is not None else {}),
                    **({"path": "backward"} if args.backward else {})},
         "pct_of_peak": round(100.0 * tflops / peak, 2),
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": traffic,
-                     "kernel": kname,
-                     "kernel_ms": round(kernel_ms, 5),
-                     "kernel_source_hash": kernel_source_hash(w.dtype)},
+        "roofline": roofline,
     }
     if args.cpu_seconds > 0 and not args.backward:
-        out["cpu_baseline"] = cpu_baseline(w, q_cpu, k_cpu, v_cpu, causal, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(w, q_cpu, k_cpu, v_cpu, causal, scale, args.cpu_seconds)
     print(json.dumps(out), flush=True)
     return 0
 

@@ -13,6 +13,7 @@ import shutil
 import subprocess
 import sys
 import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -20,8 +21,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfa2.so")
 
-SOURCES = ["fa2_api.cpp", "fa2_fwd_bf16.hip", "fa2_fwd_f32.hip", "fa2_combine.hip",
-           "fa2_bwd_bf16.hip"]
+SOURCES = ["fa2_api.cpp", "fa2_fwd_bf16.hip", "fa2_fwd_fp16.hip", "fa2_fwd_f32.hip",
+           "fa2_combine.hip", "fa2_bwd_bf16.hip"]
 ARCH = "gfx950"
 
 
@@ -43,13 +44,18 @@ def build(verbose: bool = False, extra_flags=()) -> str:
     """Compile every source and link libfa2.so; returns its path.  Raises on failure."""
     cc = hipcc()
     with tempfile.TemporaryDirectory(prefix="fa2_build_") as tmp:
-        objs = []
+        cmds, objs = [], []
         for src in SOURCES:
             obj = os.path.join(tmp, os.path.splitext(src)[0] + ".o")
             lang = ["-x", "hip"] if src.endswith(".hip") else []
-            cmd = [cc, *common_flags(extra_flags), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
-            _run(cmd, verbose)
+            cmds.append([cc, *common_flags(extra_flags), *lang, "-c", os.path.join(CSRC, src), "-o", obj])
             objs.append(obj)
+        # The sources compile independently; the two forward instantiation
+        # files dominate, so they run side by side.
+        jobs = max(1, min(len(cmds), int(os.environ.get("MAX_JOBS", "0")) or os.cpu_count() or 1, 8))
+        with ThreadPoolExecutor(jobs) as pool:
+            for f in [pool.submit(_run, cmd, verbose) for cmd in cmds]:
+                f.result()
         tmp_lib = os.path.join(tmp, "libfa2.so")
         _run([cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp_lib], verbose)
         shutil.copyfile(tmp_lib, LIB + ".tmp")

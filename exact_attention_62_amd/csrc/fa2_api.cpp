@@ -6,6 +6,7 @@
 // then the kernel is enqueued and the launch status is read back.
 #include <hip/hip_runtime_api.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -30,26 +31,30 @@ fa2_status_t fail_hip(hipError_t e, const char* what) {
   return fail(FA2_EHIP, "%s: %s (%s)", what, hipGetErrorName(e), hipGetErrorString(e));
 }
 
-int64_t elem_size(fa2_dtype_t t) { return t == FA2_BF16 ? 2 : 4; }
+int64_t elem_size(fa2_dtype_t t) { return t == FA2_FP32 ? 4 : 2; }
 
-// Checks that need no HIP call.  On success fills the element counts.
-fa2_status_t check_shape(int64_t B, int64_t H, int64_t N, int64_t d, fa2_dtype_t dtype,
-                         int64_t* kBlockM) {
-  if (dtype != FA2_BF16 && dtype != FA2_FP32)
-    return fail(FA2_ENOTSUP, "dtype %d is not FA2_BF16 (0) or FA2_FP32 (1)", (int)dtype);
-  if (B < 0 || H < 0 || N < 0)
-    return fail(FA2_EINVAL, "sizes must be >= 0 (B=%lld H=%lld N=%lld)", (long long)B,
-                (long long)H, (long long)N);
-  if (d != 64 && d != 128 && d != 256)
-    return fail(FA2_ENOTSUP, "head dimension d=%lld is not one of 64, 128, 256", (long long)d);
-  // Per-slice offsets are 32-bit inside the kernels; slice counts and the grid too.
-  if (N > (int64_t(1) << 31) / 256)
-    return fail(FA2_EINVAL, "N=%lld exceeds the supported maximum %lld", (long long)N,
-                (long long)((int64_t(1) << 31) / 256));
+constexpr int64_t kMaxLen = (int64_t(1) << 31) / 256;  // per-slice offsets are 32-bit in the kernels
+
+// Checks that need no HIP call, for Nq queries over Nk keys.  On success
+// fills the query block size.
+fa2_status_t check_shape(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                         fa2_dtype_t dtype, int64_t* kBlockM) {
+  if (dtype != FA2_BF16 && dtype != FA2_FP32 && dtype != FA2_FP16)
+    return fail(FA2_ENOTSUP, "dtype %d is not FA2_BF16 (0), FA2_FP32 (1) or FA2_FP16 (2)",
+                (int)dtype);
+  if (B < 0 || H < 0 || Nq < 0 || Nk < 0)
+    return fail(FA2_EINVAL, "sizes must be >= 0 (B=%lld H=%lld Nq=%lld Nk=%lld)", (long long)B,
+                (long long)H, (long long)Nq, (long long)Nk);
+  if (d != 32 && d != 64 && d != 96 && d != 128 && d != 256)
+    return fail(FA2_ENOTSUP, "head dimension d=%lld is not one of 32, 64, 96, 128, 256",
+                (long long)d);
+  if (Nq > kMaxLen || Nk > kMaxLen)
+    return fail(FA2_EINVAL, "sequence length %lld exceeds the supported maximum %lld",
+                (long long)(Nq > Nk ? Nq : Nk), (long long)kMaxLen);
   if (B > 0 && H > (int64_t(1) << 31) / B)
     return fail(FA2_EINVAL, "B*H=%lld*%lld exceeds 2^31", (long long)B, (long long)H);
-  const int64_t bm = dtype == FA2_BF16 ? fa2::kBlockM_bf16 : fa2::kBlockM_f32;
-  const int64_t nmb = (N + bm - 1) / bm;
+  const int64_t bm = dtype == FA2_FP32 ? fa2::kBlockM_f32 : fa2::kBlockM_mfma;
+  const int64_t nmb = (Nq + bm - 1) / bm;
   if (B * H > 0 && nmb > ((int64_t(1) << 31) - 1) / (B * H))
     return fail(FA2_EINVAL, "grid of %lld x %lld workgroups exceeds 2^31 - 1", (long long)nmb,
                 (long long)(B * H));
@@ -82,6 +87,25 @@ fa2_status_t check_device_range(const void* p, int64_t bytes, const char* name) 
 
 }  // namespace
 
+namespace fa2 {
+
+hipError_t cu_count(int* cus) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cache[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < kMaxDevices && (*cus = cache[dev].load(std::memory_order_relaxed)) > 0)
+    return hipSuccess;
+  e = hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  if (*cus < 1) *cus = 1;
+  if (dev >= 0 && dev < kMaxDevices) cache[dev].store(*cus, std::memory_order_relaxed);
+  return hipSuccess;
+}
+
+}  // namespace fa2
+
 extern "C" {
 
 const char* fa2_strerror(fa2_status_t s) {
@@ -100,7 +124,7 @@ fa2_status_t fa2_launch_shape(int64_t B, int64_t H, int64_t N, int64_t d, fa2_dt
                               int64_t* kBlockM, int64_t* num_m_block, int64_t* items) {
   g_last_error[0] = '\0';
   int64_t bm = 0;
-  fa2_status_t s = check_shape(B, H, N, d, dtype, &bm);
+  fa2_status_t s = check_shape(B, H, N, N, d, dtype, &bm);
   if (s != FA2_OK) return s;
   const int64_t nmb = (N + bm - 1) / bm;
   if (kBlockM) *kBlockM = bm;
@@ -115,36 +139,39 @@ namespace {
 
 // Pointer checks shared by the forward entry points: non-NULL, aligned, outputs
 // disjoint from everything else (extra[i] are further buffers, e.g. a
-// workspace, treated as outputs), then device residency of every range.
-// Fills the launch arguments.  Returns FA2_OK with a.BH == 0 for an empty
-// problem (nothing to launch).
+// workspace, treated as outputs), then device residency of every range.  K and
+// V are not read when Nk == 0 and are not checked then.  Fills the launch
+// arguments.  Returns FA2_OK with a.BH == 0 for an empty problem (nothing to
+// launch).
 fa2_status_t prepare(const void* Q, const void* K, const void* V, void* O, float* L, int64_t B,
-                     int64_t H, int64_t N, int64_t d, int causal, float scale, fa2_dtype_t dtype,
-                     void* stream, const void* ws, int64_t ws_bytes, fa2::FwdArgs* a) {
+                     int64_t H, int64_t Nq, int64_t Nk, int64_t d, int causal, float scale,
+                     fa2_dtype_t dtype, void* stream, const void* ws, int64_t ws_bytes,
+                     fa2::FwdArgs* a) {
   int64_t bm = 0;
-  fa2_status_t s = check_shape(B, H, N, d, dtype, &bm);
+  fa2_status_t s = check_shape(B, H, Nq, Nk, d, dtype, &bm);
   if (s != FA2_OK) return s;
   if (causal != 0 && causal != 1) return fail(FA2_EINVAL, "causal=%d must be 0 or 1", causal);
   if (!std::isfinite(scale)) return fail(FA2_EINVAL, "scale must be finite");
   a->BH = 0;
-  if (B * H * N == 0) return FA2_OK;  // empty problem: nothing to read or write
+  if (B * H * Nq == 0) return FA2_OK;  // empty problem: nothing to write
 
-  const int64_t tensor_bytes = B * H * N * d * elem_size(dtype);
-  const int64_t l_bytes = B * H * N * 4;
-  const int n = ws ? 6 : 5;
+  const int64_t q_bytes = B * H * Nq * d * elem_size(dtype);
+  const int64_t k_bytes = B * H * Nk * d * elem_size(dtype);
+  const int64_t l_bytes = B * H * Nq * 4;
   const void* ptrs[6] = {Q, K, V, O, L, ws};
-  const int64_t sizes[6] = {tensor_bytes, tensor_bytes, tensor_bytes, tensor_bytes, l_bytes,
-                            ws_bytes};
+  const int64_t sizes[6] = {q_bytes, k_bytes, k_bytes, q_bytes, l_bytes, ws_bytes};
   const char* names[6] = {"Q", "K", "V", "O", "L", "workspace"};
-  for (int i = 0; i < n; ++i) {
+  bool used[6] = {true, Nk > 0, Nk > 0, true, true, ws != nullptr};
+  for (int i = 0; i < 6; ++i) {
+    if (!used[i]) continue;
     if (ptrs[i] == nullptr) return fail(FA2_EINVAL, "%s is NULL", names[i]);
     const uintptr_t align = i == 4 ? 4 : 16;
     if (reinterpret_cast<uintptr_t>(ptrs[i]) % align != 0)
       return fail(FA2_EINVAL, "%s=%p is not %d-byte aligned", names[i], ptrs[i], (int)align);
   }
-  for (int o = 3; o < n; ++o)
-    for (int i = 0; i < n; ++i)
-      if (i != o && overlaps(ptrs[o], sizes[o], ptrs[i], sizes[i]))
+  for (int o = 3; o < 6; ++o)
+    for (int i = 0; i < 6; ++i)
+      if (used[o] && used[i] && i != o && overlaps(ptrs[o], sizes[o], ptrs[i], sizes[i]))
         return fail(FA2_EINVAL, "%s overlaps %s", names[o], names[i]);
 
   // From here on the HIP runtime is involved.
@@ -154,7 +181,8 @@ fa2_status_t prepare(const void* Q, const void* K, const void* V, void* O, float
     (void)hipGetLastError();
     return fail_hip(e, "hipGetDevice");
   }
-  for (int i = 0; i < n; ++i) {
+  for (int i = 0; i < 6; ++i) {
+    if (!used[i]) continue;
     s = check_device_range(ptrs[i], sizes[i], names[i]);
     if (s != FA2_OK) return s;
   }
@@ -164,13 +192,25 @@ fa2_status_t prepare(const void* Q, const void* K, const void* V, void* O, float
   a->O = O;
   a->L = L;
   a->BH = static_cast<int>(B * H);
-  a->N = static_cast<int>(N);
+  a->Nq = static_cast<int>(Nq);
+  a->Nk = static_cast<int>(Nk);
   a->d = static_cast<int>(d);
   a->causal = causal;
   a->scale = scale;
-  a->num_m_block = static_cast<int>((N + bm - 1) / bm);
+  a->num_m_block = static_cast<int>((Nq + bm - 1) / bm);
+  a->elem = static_cast<int>(dtype);
   a->stream = static_cast<hipStream_t>(stream);
   return FA2_OK;
+}
+
+hipError_t launch_fwd(const fa2::FwdArgs& a) {
+  if (a.Nk == 0) return fa2::launch_fill_no_keys(a);  // every row's sum is empty
+  switch (a.elem) {
+    case fa2::kBF16: return fa2::launch_fwd_bf16(a);
+    case fa2::kFP16: return fa2::launch_fwd_fp16(a);
+    case fa2::kFP32: return fa2::launch_fwd_f32(a);
+  }
+  return hipErrorInvalidValue;
 }
 
 // The pages' rule (page "Flash Attention V2原理解读", the thread-block grid
@@ -192,33 +232,50 @@ int choose_num_splits(int64_t items, int64_t slots, int64_t max_splits) {
   return 1;
 }
 
-int64_t splitkv_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int64_t splits) {
-  return splits * B * H * N * (d + 1) * 4;  // O_s [splits][B*H][N][d] then L_s [splits][B*H][N]
+int64_t splitkv_bytes(int64_t B, int64_t H, int64_t Nq, int64_t d, int64_t splits) {
+  return splits * B * H * Nq * (d + 1) * 4;  // O_s [splits][B*H][Nq][d], L_s [splits][B*H][Nq]
 }
 
-fa2_status_t check_splits(int64_t B, int64_t H, int64_t N, int num_splits) {
+fa2_status_t check_splits(int64_t B, int64_t H, int64_t Nq, int num_splits) {
   if (num_splits < 1 || num_splits > FA2_MAX_SPLITS)
     return fail(FA2_EINVAL, "num_splits=%d is not in 1..%d", num_splits, FA2_MAX_SPLITS);
-  const int64_t nmb = (N + fa2::kBlockM_bf16 - 1) / fa2::kBlockM_bf16;
-  if (B * H * N > 0 && (nmb * num_splits > ((int64_t(1) << 31) - 1) / (B * H) ||
-                        N * num_splits > ((int64_t(1) << 31) - 1) / (B * H)))
-    return fail(FA2_EINVAL, "B*H=%lld with N=%lld and %d splits exceeds 2^31 - 1 items or rows",
-                (long long)(B * H), (long long)N, num_splits);
+  const int64_t nmb = (Nq + fa2::kBlockM_mfma - 1) / fa2::kBlockM_mfma;
+  if (B * H * Nq > 0 && (nmb * num_splits > ((int64_t(1) << 31) - 1) / (B * H) ||
+                         Nq * num_splits > ((int64_t(1) << 31) - 1) / (B * H)))
+    return fail(FA2_EINVAL, "B*H=%lld with Nq=%lld and %d splits exceeds 2^31 - 1 items or rows",
+                (long long)(B * H), (long long)Nq, num_splits);
   return FA2_OK;
 }
 
-fa2_status_t heuristic_splits(int64_t B, int64_t H, int64_t N, int64_t d, int* num_splits) {
-  int slots = 0;
-  const hipError_t e = fa2::bf16_resident_workgroups(static_cast<int>(d), &slots);
+fa2_status_t heuristic_splits(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                              int* num_splits) {
+  int cus = 0;
+  const hipError_t e = fa2::cu_count(&cus);
   if (e != hipSuccess) {
     (void)hipGetLastError();
     return fail_hip(e, "device query");
   }
-  const int64_t nmb = (N + fa2::kBlockM_bf16 - 1) / fa2::kBlockM_bf16;
-  const int64_t kv_blocks = (N + fa2::bf16_block_n(static_cast<int>(d)) - 1) /
-                            fa2::bf16_block_n(static_cast<int>(d));
+  // Workgroups of the 16-bit kernel resident at once: kWavesPerSimd per CU.
+  const int64_t slots = int64_t(cus) * fa2::mfma_waves_per_simd(static_cast<int>(d));
+  const int64_t bn = fa2::mfma_block_n(static_cast<int>(d));
+  const int64_t nmb = (Nq + fa2::kBlockM_mfma - 1) / fa2::kBlockM_mfma;
+  const int64_t kv_blocks = (Nk + bn - 1) / bn;
   const int64_t max_splits = kv_blocks < FA2_MAX_SPLITS ? kv_blocks : FA2_MAX_SPLITS;
   *num_splits = choose_num_splits(nmb * B * H, slots, max_splits);
+  return FA2_OK;
+}
+
+fa2_status_t fwd_common(const void* Q, const void* K, const void* V, void* O, float* L,
+                        int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int causal,
+                        float scale, fa2_dtype_t dtype, void* stream) {
+  fa2::FwdArgs a;
+  fa2_status_t s =
+      prepare(Q, K, V, O, L, B, H, Nq, Nk, d, causal, scale, dtype, stream, nullptr, 0, &a);
+  if (s != FA2_OK || a.BH == 0) return s;
+  (void)hipGetLastError();  // clear a stale error so the status below is this launch's
+  hipError_t e = launch_fwd(a);
+  if (e == hipSuccess) e = hipGetLastError();
+  if (e != hipSuccess) return fail_hip(e, "kernel launch");
   return FA2_OK;
 }
 
@@ -230,71 +287,71 @@ fa2_status_t fa2_fwd(const void* Q, const void* K, const void* V, void* O, float
                      int64_t H, int64_t N, int64_t d, int causal, float scale, fa2_dtype_t dtype,
                      void* stream) {
   g_last_error[0] = '\0';
-  fa2::FwdArgs a;
-  fa2_status_t s =
-      prepare(Q, K, V, O, L, B, H, N, d, causal, scale, dtype, stream, nullptr, 0, &a);
-  if (s != FA2_OK || a.BH == 0) return s;
-  (void)hipGetLastError();  // clear a stale error so the status below is this launch's
-  hipError_t e = dtype == FA2_BF16 ? fa2::launch_fwd_bf16(a) : fa2::launch_fwd_f32(a);
-  if (e == hipSuccess) e = hipGetLastError();
-  if (e != hipSuccess) return fail_hip(e, "kernel launch");
-  return FA2_OK;
+  return fwd_common(Q, K, V, O, L, B, H, N, N, d, causal, scale, dtype, stream);
 }
 
-fa2_status_t fa2_splitkv_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d,
+fa2_status_t fa2_fwd_cross(const void* Q, const void* K, const void* V, void* O, float* L,
+                           int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int causal,
+                           float scale, fa2_dtype_t dtype, void* stream) {
+  g_last_error[0] = '\0';
+  return fwd_common(Q, K, V, O, L, B, H, Nq, Nk, d, causal, scale, dtype, stream);
+}
+
+fa2_status_t fa2_splitkv_workspace_size(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
                                         int num_splits, size_t* bytes) {
   g_last_error[0] = '\0';
   int64_t bm = 0;
-  fa2_status_t s = check_shape(B, H, N, d, FA2_BF16, &bm);
+  fa2_status_t s = check_shape(B, H, Nq, Nk, d, FA2_BF16, &bm);
   if (s != FA2_OK) return s;
-  s = check_splits(B, H, N, num_splits);
+  s = check_splits(B, H, Nq, num_splits);
   if (s != FA2_OK) return s;
   if (!bytes) return fail(FA2_EINVAL, "bytes is NULL");
-  *bytes = static_cast<size_t>(splitkv_bytes(B, H, N, d, num_splits));
+  *bytes = static_cast<size_t>(splitkv_bytes(B, H, Nq, d, num_splits));
   return FA2_OK;
 }
 
-fa2_status_t fa2_num_splits(int64_t B, int64_t H, int64_t N, int64_t d, int* num_splits) {
+fa2_status_t fa2_num_splits(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                            int* num_splits) {
   g_last_error[0] = '\0';
   int64_t bm = 0;
-  fa2_status_t s = check_shape(B, H, N, d, FA2_BF16, &bm);
+  fa2_status_t s = check_shape(B, H, Nq, Nk, d, FA2_BF16, &bm);
   if (s != FA2_OK) return s;
   if (!num_splits) return fail(FA2_EINVAL, "num_splits is NULL");
-  return heuristic_splits(B, H, N, d, num_splits);
+  return heuristic_splits(B, H, Nq, Nk, d, num_splits);
 }
 
 fa2_status_t fa2_fwd_splitkv(const void* Q, const void* K, const void* V, void* O, float* L,
-                             int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
-                             fa2_dtype_t dtype, int num_splits, void* workspace,
+                             int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int causal,
+                             float scale, fa2_dtype_t dtype, int num_splits, void* workspace,
                              size_t workspace_bytes, void* stream) {
   g_last_error[0] = '\0';
-  if (dtype != FA2_BF16)
-    return fail(FA2_ENOTSUP, "split-KV is implemented for FA2_BF16 only (dtype %d)", (int)dtype);
+  if (dtype == FA2_FP32)
+    return fail(FA2_ENOTSUP, "split-KV is implemented for FA2_BF16 and FA2_FP16 only");
   int64_t bm = 0;
-  fa2_status_t s = check_shape(B, H, N, d, dtype, &bm);
+  fa2_status_t s = check_shape(B, H, Nq, Nk, d, dtype, &bm);
   if (s != FA2_OK) return s;
   if (num_splits < 0) return fail(FA2_EINVAL, "num_splits=%d must be >= 0", num_splits);
-  if (B * H * N == 0) return FA2_OK;
+  if (B * H * Nq == 0) return FA2_OK;
   if (num_splits == 0) {
-    s = heuristic_splits(B, H, N, d, &num_splits);
+    s = heuristic_splits(B, H, Nq, Nk, d, &num_splits);
     if (s != FA2_OK) return s;
   }
-  s = check_splits(B, H, N, num_splits);
+  s = check_splits(B, H, Nq, num_splits);
   if (s != FA2_OK) return s;
-  const int64_t need = splitkv_bytes(B, H, N, d, num_splits);
+  const int64_t need = splitkv_bytes(B, H, Nq, d, num_splits);
   if (workspace == nullptr) return fail(FA2_EINVAL, "workspace is NULL");
   if (static_cast<int64_t>(workspace_bytes) < need)
     return fail(FA2_EINVAL, "workspace of %llu bytes is smaller than the %lld bytes needed",
                 (unsigned long long)workspace_bytes, (long long)need);
   fa2::FwdArgs a;
-  s = prepare(Q, K, V, O, L, B, H, N, d, causal, scale, dtype, stream, workspace, need, &a);
+  s = prepare(Q, K, V, O, L, B, H, Nq, Nk, d, causal, scale, dtype, stream, workspace, need, &a);
   if (s != FA2_OK) return s;
   a.num_splits = num_splits;
   a.ws_O = static_cast<float*>(workspace);
-  a.ws_L = a.ws_O + static_cast<size_t>(num_splits) * B * H * N * d;
+  a.ws_L = a.ws_O + static_cast<size_t>(num_splits) * B * H * Nq * d;
   (void)hipGetLastError();
-  hipError_t e = fa2::launch_fwd_bf16(a);
-  if (e == hipSuccess) e = fa2::launch_combine_bf16(a);
+  hipError_t e = launch_fwd(a);
+  if (e == hipSuccess && a.Nk > 0) e = fa2::launch_combine(a);
   if (e == hipSuccess) e = hipGetLastError();
   if (e != hipSuccess) return fail_hip(e, "kernel launch");
   return FA2_OK;
@@ -303,9 +360,10 @@ fa2_status_t fa2_fwd_splitkv(const void* Q, const void* K, const void* V, void* 
 fa2_status_t fa2_bwd_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d, size_t* bytes) {
   g_last_error[0] = '\0';
   int64_t bm = 0;
-  fa2_status_t s = check_shape(B, H, N, d, FA2_BF16, &bm);
+  fa2_status_t s = check_shape(B, H, N, N, d, FA2_BF16, &bm);
   if (s != FA2_OK) return s;
-  if (d == 256) return fail(FA2_ENOTSUP, "the backward pass supports d = 64 and 128 (d=256)");
+  if (d != 64 && d != 128)
+    return fail(FA2_ENOTSUP, "the backward pass supports d = 64 and 128 (d=%lld)", (long long)d);
   if (!bytes) return fail(FA2_EINVAL, "bytes is NULL");
   *bytes = static_cast<size_t>(B * H * N * 4);  // D = rowsum(dO * O), float32 per row
   return FA2_OK;
@@ -320,9 +378,10 @@ fa2_status_t fa2_bwd(const void* Q, const void* K, const void* V, const void* O,
     return fail(FA2_ENOTSUP, "the backward pass is implemented for FA2_BF16 only (dtype %d)",
                 (int)dtype);
   int64_t bm = 0;
-  fa2_status_t s = check_shape(B, H, N, d, dtype, &bm);
+  fa2_status_t s = check_shape(B, H, N, N, d, dtype, &bm);
   if (s != FA2_OK) return s;
-  if (d == 256) return fail(FA2_ENOTSUP, "the backward pass supports d = 64 and 128 (d=256)");
+  if (d != 64 && d != 128)
+    return fail(FA2_ENOTSUP, "the backward pass supports d = 64 and 128 (d=%lld)", (long long)d);
   if (causal != 0 && causal != 1) return fail(FA2_EINVAL, "causal=%d must be 0 or 1", causal);
   if (!std::isfinite(scale)) return fail(FA2_EINVAL, "scale must be finite");
   if (B * H * N == 0) return FA2_OK;

@@ -8,74 +8,103 @@
 // row's softmax denominator:
 //   L = ln sum_s exp(L_s)   (as Lmax + ln sum_s exp(L_s - Lmax)),
 //   O = sum_s exp(L_s - L) O_s.
-// A split that saw no key of the row has L_s = -inf and weight 0; split 0
-// always holds key 0, which every row sees, so Lmax is finite.
+// A split that saw no key of the row has L_s = -inf and weight 0.  A row that
+// saw no key in any split (a causal query before the first key, Nq > Nk) has
+// an empty sum: O = 0 and L = -inf.
 //
-// The merge reads num_splits * d fp32 values per row and writes d bf16 values:
-// it is bound by HBM bandwidth, so it is plain coalesced vector loads.  Each
-// thread owns 4 consecutive dimensions of one row (d/4 threads per row).
+// The merge reads num_splits * d fp32 values per row and writes d 16-bit
+// values: it is bound by HBM bandwidth, so it is plain coalesced vector loads.
+// Each thread owns 4 consecutive dimensions of one row (d/4 threads per row).
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
 
+#include "fa2_device.h"
 #include "fa2_internal.h"
 
 namespace fa2 {
 namespace {
 
+using namespace dev;
+
 constexpr int kThreads = 256;
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
 
-typedef __attribute__((ext_vector_type(4))) float f32x4_t;
-typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
-
-template <int D>
+template <typename T, int D>
 __global__ void __launch_bounds__(kThreads)
 fa2_combine_kernel(const float* __restrict__ Ow, const float* __restrict__ Lw,
                    uint16_t* __restrict__ O, float* __restrict__ L, int rows, int num_splits) {
+  typedef typename Vec16<T>::x4 t4_t;
   constexpr int TPR = D / 4;               // threads per row
   constexpr int RPB = kThreads / TPR;      // rows per workgroup
+  if ((int)threadIdx.x >= RPB * TPR) return;  // d = 96: 240 of the 256 threads have a row
   const int row = blockIdx.x * RPB + threadIdx.x / TPR;
   const int t = threadIdx.x % TPR;
   if (row >= rows) return;
 
-  float lmax = -INFINITY;
+  float lmax = kNegInf;
   for (int s = 0; s < num_splits; ++s) lmax = fmaxf(lmax, Lw[(size_t)s * rows + row]);
+  const float ref = lmax == kNegInf ? 0.f : lmax;  // every weight is 0 for an empty row
   float tot = 0.f;
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
   for (int s = 0; s < num_splits; ++s) {
-    const float w = __builtin_amdgcn_exp2f((Lw[(size_t)s * rows + row] - lmax) * kLog2e);
+    const float w = __builtin_amdgcn_exp2f((Lw[(size_t)s * rows + row] - ref) * kLog2e);
     const f32x4_t o = *(const f32x4_t*)(Ow + ((size_t)s * rows + row) * D + 4 * t);
     tot += w;
     acc += w * o;
   }
-  const float inv = 1.f / tot;
-  bf16x4_t out;
+  const float inv = tot > 0.f ? 1.f / tot : 0.f;
+  t4_t out;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) out[r] = (__bf16)(acc[r] * inv);
-  *(bf16x4_t*)(O + (size_t)row * D + 4 * t) = out;
-  if (t == 0) L[row] = __builtin_fmaf(__builtin_amdgcn_logf(tot), kLn2, lmax);
+  for (int r = 0; r < 4; ++r) out[r] = (T)(acc[r] * inv);
+  *(t4_t*)(O + (size_t)row * D + 4 * t) = out;
+  if (t == 0) L[row] = tot > 0.f ? __builtin_fmaf(__builtin_amdgcn_logf(tot), kLn2, lmax) : kNegInf;
 }
 
-template <int D>
+template <typename T, int D>
 hipError_t launch(const FwdArgs& a) {
   constexpr int RPB = kThreads / (D / 4);
-  const int rows = a.BH * a.N;
+  const int rows = a.BH * a.Nq;
   const int grid = (rows + RPB - 1) / RPB;
-  hipLaunchKernelGGL((fa2_combine_kernel<D>), dim3(grid), dim3(kThreads), 0, a.stream, a.ws_O,
+  hipLaunchKernelGGL((fa2_combine_kernel<T, D>), dim3(grid), dim3(kThreads), 0, a.stream, a.ws_O,
                      a.ws_L, (uint16_t*)a.O, a.L, rows, a.num_splits);
   return hipGetLastError();
 }
 
+template <typename T>
+hipError_t dispatch(const FwdArgs& a) {
+  switch (a.d) {
+    case 32: return launch<T, 32>(a);
+    case 64: return launch<T, 64>(a);
+    case 96: return launch<T, 96>(a);
+    case 128: return launch<T, 128>(a);
+    case 256: return launch<T, 256>(a);
+  }
+  return hipErrorInvalidValue;
+}
+
+// Rows with no key at all (Nk == 0): O = 0, L = -inf.  One thread per 16
+// bytes of O (every row is a multiple of 64 bytes) and per row of L.
+__global__ void __launch_bounds__(kThreads)
+fa2_fill_no_keys_kernel(u32x4_t* __restrict__ O, float* __restrict__ L, int64_t o_chunks, int rows) {
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i < o_chunks) O[i] = u32x4_t{0u, 0u, 0u, 0u};
+  if (i < rows) L[i] = kNegInf;
+}
+
 }  // namespace
 
-hipError_t launch_combine_bf16(const FwdArgs& a) {
-  switch (a.d) {
-    case 64: return launch<64>(a);
-    case 128: return launch<128>(a);
-    case 256: return launch<256>(a);
-  }
+hipError_t launch_fill_no_keys(const FwdArgs& a) {
+  const int rows = a.BH * a.Nq;
+  const int64_t o_chunks = (int64_t)rows * a.d * (a.elem == kFP32 ? 4 : 2) / 16;
+  const int64_t n = o_chunks > rows ? o_chunks : rows;
+  hipLaunchKernelGGL(fa2_fill_no_keys_kernel, dim3((unsigned)((n + kThreads - 1) / kThreads)),
+                     dim3(kThreads), 0, a.stream, (u32x4_t*)a.O, a.L, o_chunks, rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const FwdArgs& a) {
+  if (a.elem == kBF16) return dispatch<__bf16>(a);
+  if (a.elem == kFP16) return dispatch<_Float16>(a);
   return hipErrorInvalidValue;
 }
 

@@ -12,6 +12,8 @@ namespace dev {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
+typedef __attribute__((ext_vector_type(4))) _Float16 f16x4_t;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
@@ -73,9 +75,22 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
 }
 
-// SPLIT: the key/value range of each query block is cut into num_splits
-// contiguous parts, each a work item of its own; an item writes its partial
-// result (O normalised within the part, fp32, and its L) to Ow / Lw, indexed
-// [split][batch*head][row], for a separate merge.
+// The two 16-bit input types: their 8- and 4-element vectors and the 32x32x16
+// MFMA that multiplies them (fp32 accumulation for both).
+template <typename T> struct Vec16;
+template <> struct Vec16<__bf16> {
+  typedef bf16x8_t x8;
+  typedef bf16x4_t x4;
+};
+template <> struct Vec16<_Float16> {
+  typedef f16x8_t x8;
+  typedef f16x4_t x4;
+};
+__device__ __forceinline__ f32x16_t mfma32x32x16(bf16x8_t a, bf16x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16_t mfma32x32x16(f16x8_t a, f16x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
 }  // namespace dev
 }  // namespace fa2

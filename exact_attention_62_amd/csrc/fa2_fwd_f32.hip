@@ -9,7 +9,9 @@
 // precision fp32 matrix path to fall into, and this mode is meant for small
 // problems, so it runs on the vector ALUs: each wavefront owns one query row
 // (its Q block), each lane one key of the current 64-key block, and the lanes
-// share the output row's head dimension for the P~ V_j update.
+// share the output row's head dimension for the P~ V_j update.  Q has Nq rows
+// and K, V Nk; the causal mask is aligned bottom-right (key j hidden from query
+// i when j > i + Nk - Nq), and a query that sees no key gets O = 0, L = -inf.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -38,8 +40,8 @@ template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(kThreads)
 fa2_fwd_f32_kernel(const float* __restrict__ Qg, const float* __restrict__ Kg,
                    const float* __restrict__ Vg, float* __restrict__ Og, float* __restrict__ Lg,
-                   int N, int num_m_block, float scale) {
-  constexpr int R = D / 64;  // output dims per lane
+                   int Nq, int Nk, int num_m_block, float scale) {
+  constexpr int R = (D + 63) / 64;  // output dims per lane (dims lane + 64 r < D)
   __shared__ float qs[kWaves][D];
 
   const int lane = threadIdx.x & 63;
@@ -48,13 +50,14 @@ fa2_fwd_f32_kernel(const float* __restrict__ Qg, const float* __restrict__ Kg,
   const int m = blockIdx.x - bh * num_m_block;
   const int q = m * kWaves + wave;  // this wavefront's query row
 
-  const size_t slice = (size_t)bh * (size_t)N * D;
-  const float* Kh = Kg + slice;
-  const float* Vh = Vg + slice;
+  const size_t qslice = (size_t)bh * (size_t)Nq * D;
+  const size_t kslice = (size_t)bh * (size_t)Nk * D;
+  const float* Kh = Kg + kslice;
+  const float* Vh = Vg + kslice;
 
-  for (int t = lane; t < D; t += 64) qs[wave][t] = q < N ? Qg[slice + (size_t)q * D + t] : 0.f;
+  for (int t = lane; t < D; t += 64) qs[wave][t] = q < Nq ? Qg[qslice + (size_t)q * D + t] : 0.f;
   __syncthreads();
-  if (q >= N) return;
+  if (q >= Nq) return;
 
   float o[R];
 #pragma unroll
@@ -62,7 +65,9 @@ fa2_fwd_f32_kernel(const float* __restrict__ Qg, const float* __restrict__ Kg,
   float m_run = -__builtin_inff();
   float l_run = 0.f;
 
-  const int n_keys = CAUSAL ? q + 1 : N;  // keys past the diagonal are never visited
+  // Keys past the diagonal are never visited; with Nq > Nk the first queries
+  // see none (the loop does not run: O = 0, L = -inf below).
+  const int n_keys = CAUSAL ? min(Nk, q + 1 + (Nk - Nq)) : Nk;
   for (int k0 = 0; k0 < n_keys; k0 += kBN) {
     const int key = k0 + lane;
     float s = -__builtin_inff();
@@ -91,14 +96,17 @@ fa2_fwd_f32_kernel(const float* __restrict__ Qg, const float* __restrict__ Kg,
       const float pk = __shfl(p, kk, 64);
       const float* vrow = Vh + (size_t)(k0 + kk) * D;
 #pragma unroll
-      for (int r = 0; r < R; ++r) o[r] = __builtin_fmaf(pk, vrow[lane + 64 * r], o[r]);
+      for (int r = 0; r < R; ++r)
+        if (lane + 64 * r < D) o[r] = __builtin_fmaf(pk, vrow[lane + 64 * r], o[r]);
     }
   }
 
-  float* orow = Og + slice + (size_t)q * D;
+  float* orow = Og + qslice + (size_t)q * D;
+  const bool seen = n_keys > 0;
 #pragma unroll
-  for (int r = 0; r < R; ++r) orow[lane + 64 * r] = o[r] / l_run;
-  if (lane == 0) Lg[(size_t)bh * N + q] = m_run + logf(l_run);
+  for (int r = 0; r < R; ++r)
+    if (lane + 64 * r < D) orow[lane + 64 * r] = seen ? o[r] / l_run : 0.f;
+  if (lane == 0) Lg[(size_t)bh * Nq + q] = seen ? m_run + logf(l_run) : -__builtin_inff();
 }
 
 template <int D, bool CAUSAL>
@@ -106,7 +114,7 @@ hipError_t launch(const FwdArgs& a) {
   const int total = a.num_m_block * a.BH;
   hipLaunchKernelGGL((fa2_fwd_f32_kernel<D, CAUSAL>), dim3(total), dim3(kThreads), 0, a.stream,
                      (const float*)a.Q, (const float*)a.K, (const float*)a.V, (float*)a.O, a.L,
-                     a.N, a.num_m_block, a.scale);
+                     a.Nq, a.Nk, a.num_m_block, a.scale);
   return hipGetLastError();
 }
 
@@ -114,6 +122,10 @@ hipError_t launch(const FwdArgs& a) {
 
 hipError_t launch_fwd_f32(const FwdArgs& a) {
   switch (a.d * 2 + a.causal) {
+    case 32 * 2 + 0: return launch<32, false>(a);
+    case 32 * 2 + 1: return launch<32, true>(a);
+    case 96 * 2 + 0: return launch<96, false>(a);
+    case 96 * 2 + 1: return launch<96, true>(a);
     case 64 * 2 + 0: return launch<64, false>(a);
     case 64 * 2 + 1: return launch<64, true>(a);
     case 128 * 2 + 0: return launch<128, false>(a);

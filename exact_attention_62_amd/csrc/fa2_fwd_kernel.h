@@ -1,0 +1,760 @@
+// FlashAttention-2 forward pass on 16-bit inputs (bf16 or fp16 in, the same
+// type out, fp32 accumulation), for gfx950 (MI355X).  This header holds the
+// kernel template; fa2_fwd_bf16.hip and fa2_fwd_fp16.hip instantiate it.
+//
+// The algorithm (pages "FlashAttention学习笔记(2)" and "Flash Attention V2原理解读",
+// forward sections; "flash-attention123和ring-attention", 优化1-优化4):
+//   outer loop: one work item per block of kBlockM = 128 query rows of one
+//               (batch, head); items are independent;
+//   inner loop: K_j, V_j blocks of BN keys, staged in LDS and shared by the
+//               workgroup's four wavefronts;
+//   per block:  S = scale * Q_i K_j^T on MFMA, online row max / row sum, the
+//               running O rescaled by exp(m_old - m_new) and P~ V_j added on
+//               MFMA, no division by l inside the loop;
+//   after:      O = O / l once, L = m + ln(l); K/V blocks that the causal mask
+//               covers entirely are neither loaded nor computed.
+//   lengths:    Q has Nq rows, K and V Nk (the grid follows the query length,
+//               page "FlashAttention学习笔记(2)", section "V2中的thread blocks
+//               排布"); the causal mask is aligned bottom-right, key j hidden
+//               from query i when j > i + Nk - Nq, so a query that sees no key
+//               at all (Nq > Nk) gets O = 0 and L = -inf.
+//
+// Persistent grid.  The page's grid has one thread block per (query block,
+// batch, head).  Here as many workgroups run as fit on the chip at once and
+// each walks a fixed sequence of work items: the items of one XCD are the
+// query blocks of a contiguous range of heads (which read the same K/V and so
+// share that XCD's L2), dealt to its workgroups in a snake order so that heavy
+// and light causal blocks balance.  While the last K/V block of an item is
+// processed, the next item's Q rows and first K/V blocks are already loading.
+//
+// Wavefront layout (the pages' split-Q warp scheme, re-derived for 64-wide
+// wavefronts and 32x32 MFMA tiles): each wavefront owns 32 query rows against
+// the shared K/V block and never exchanges partial results with another.
+//
+// MFMA orientation.  v_mfma_f32_32x32x16_{bf16,f16} produces a 32x32 fp32 tile
+// where lane l holds column (l % 32) and rows 8*(r/4) + 4*(l/32) + (r%4),
+// r = 0..15.  The kernel computes S^T = K Q^T, so that a lane holds 16 keys of
+// ONE query row: the row max and row sum are in-lane, plus one exchange with
+// the lane 32 positions away.  The output is accumulated transposed too,
+// O^T += V^T P^T, so each lane's accumulators all belong to its one query row
+// (the rescale and the final 1/l are per-lane scalars).  The P^T operand comes
+// straight from the S^T registers: the contraction index may be permuted
+// freely as long as both operands use the same order, and the V^T operand is
+// read in exactly the order in which S^T's accumulator rows sit in a lane.
+//
+// Memory pipeline.  K and V blocks go from HBM straight into LDS
+// (global_load_lds_dwordx4, no register staging), double-buffered: while
+// block j is consumed, blocks j+1 (V) and j+2 (K) are in flight, with one
+// workgroup barrier per block.  Each direct load writes 1 KB of LDS.  K: whole
+// key rows in 1 KB pieces that sit 1040 bytes apart, with the rows that share
+// a piece chosen so that the K fragment reads (16 rows x 16 bytes per pass)
+// touch every LDS bank once.  V: 128-byte blocks of 4 key rows x 16 dims, so
+// that each 16-lane group of a transposing read (ds_read_b64_tr_b16) reads
+// one contiguous block, the pattern the LDS serves fastest.  Every fragment
+// address is one per-lane base plus a compile-time offset.  The direct loads,
+// and the waits and barriers that order them, are inline assembly, so the
+// compiler does not serialise them against the LDS reads in between.
+//
+// Epilogue.  O and L go straight from registers to global memory through
+// buffer stores whose resource covers only the rows < Nq: rows past the end
+// are dropped by the hardware, and every wavefront issues the same number of
+// stores, which the next item's first wait counts past.
+//
+// Overlap.  The MFMAs of block j+1's S = K Q^T are issued in the same basic
+// block as block j's softmax (vector ALU: exp2, row max/sum, 16-bit packing),
+// so the matrix cores and the vector ALUs work concurrently; the PV MFMAs of
+// block j follow.
+//
+// Rescaling.  The running reference max m only moves when a block's row max
+// exceeds it by more than kTau (in log2 units); otherwise O and l keep their
+// scale and P~ = exp2(c s - c m) stays <= 2^kTau.  O / l and L = m + ln(l) are
+// unchanged by the choice of reference, so this is the same online softmax
+// with fewer rescales of O.
+//
+// Rounding.  P~ is rounded to the input type (nearest even) for the PV
+// product; l sums the unrounded fp32 values.  For fp16, P~ <= 2^kTau stays far
+// below the type's largest value, and a value below its normal range loses at
+// most 2^-25 against l >= 1.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "fa2_device.h"
+#include "fa2_internal.h"
+
+namespace fa2 {
+namespace {
+
+using namespace dev;
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kBM = 32 * kWaves;  // query rows per workgroup
+static_assert(kBM == kBlockM_mfma, "kBlockM mismatch");
+
+constexpr float kTau = 8.0f;  // lazy-rescale threshold, log2 units
+
+// Keys per K/V block and wavefronts per SIMD for each head dimension.
+template <int D> struct Cfg {
+  static constexpr int BN = mfma_block_n(D), kWavesPerSimd = mfma_waves_per_simd(D);
+};
+
+// LDS layout of a K block: key row r lives in 1 KB piece blk(r) at row slot
+// slot(r); pieces are kPiece bytes apart, so piece b starts 16*b bytes further
+// into the 256-byte bank cycle.  Rows 0..15 of any aligned group get 16
+// different bank offsets (for the K reads, 16 lanes x 16 bytes per pass).
+//   D = 32:  4 pieces of 16 rows, blk = r % 4, slot = r / 4 (bank offset
+//            16*blk + 64*(slot % 4));
+//   D = 64:  8 pieces of 8 rows;
+//   D = 96, 128, 256: 16 pieces of 4, 4 and 2 rows (a D = 96 piece holds 768
+//            bytes of rows).
+// piece_row(b) + slot_row(s) inverts blk/slot: it is the row at slot s of
+// piece b, which the direct loads need.
+constexpr int kPiece = 1024 + 16;
+template <int D> __host__ __device__ constexpr int blk(int r) {
+  if constexpr (D == 32) return r & 3;
+  else if constexpr (D == 64) return ((r >> 2) & 3) + 4 * (r & 1);
+  else return 4 * (r & 3) + ((r >> 2) & 3);
+}
+template <int D> __host__ __device__ constexpr int slot(int r) {
+  if constexpr (D == 32) return r >> 2;
+  else if constexpr (D == 64) return 2 * (r >> 4) + ((r >> 1) & 1);
+  else return r >> 4;
+}
+template <int D> __host__ __device__ constexpr int piece_row(int b) {
+  if constexpr (D == 32) return b;
+  else return 4 * (b & 3) + (b >> 2);
+}
+template <int D> __host__ __device__ constexpr int slot_row(int s) {
+  if constexpr (D == 32) return 4 * s;
+  else if constexpr (D == 64) return 16 * (s >> 1) + 2 * (s & 1);
+  else return 16 * s;
+}
+template <int D> __host__ __device__ constexpr int rows_per_piece() {
+  return D == 96 ? 4 : 1024 / (2 * D);
+}
+template <int D> __host__ __device__ constexpr int lds_off(int r) {
+  return blk<D>(r) * kPiece + slot<D>(r) * 2 * D;
+}
+// Every row of a block has one (piece, slot) inside the block, piece_row +
+// slot_row finds it again, and the rows of each aligned group of 16 sit at 16
+// different bank offsets.
+template <int D, int BN> __host__ __device__ constexpr bool k_layout_ok() {
+  constexpr int RPP = rows_per_piece<D>();
+  for (int r = 0; r < BN; ++r) {
+    if (blk<D>(r) < 0 || blk<D>(r) >= BN / RPP || slot<D>(r) < 0 || slot<D>(r) >= RPP) return false;
+    if (piece_row<D>(blk<D>(r)) + slot_row<D>(slot<D>(r)) != r) return false;
+  }
+  for (int g = 0; g < BN; g += 16)
+    for (int a = g; a < g + 16; ++a)
+      for (int b = a + 1; b < g + 16; ++b)
+        if ((lds_off<D>(a) / 16) % 16 == (lds_off<D>(b) / 16) % 16) return false;
+  return true;
+}
+// V layout: element (key row r, dim d) at (r/4)*4*2D + (d/16)*128 + 32*(r%4) + 2*(d%16):
+// 128-byte blocks of 4 key rows x 16 dims.  Direct load n of a V block fills
+// blocks 8n .. 8n+7; lane l writes 16 bytes of block 8n + l/8: row (l%8)/2 of
+// its group of 4, dims 8*(l%2) .. +8 of its 16-dim segment.
+template <int D> __host__ __device__ constexpr int v_row(int n, int l) {
+  return 4 * ((8 * n + l / 8) / (D / 16)) + (l % 8) / 2;
+}
+template <int D> __host__ __device__ constexpr int v_dim(int n, int l) {
+  return 16 * ((8 * n + l / 8) % (D / 16)) + 8 * (l % 2);
+}
+
+template <typename T, int D, bool CAUSAL, bool SPLIT>
+__global__ void __launch_bounds__(kThreads, Cfg<D>::kWavesPerSimd)
+fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
+               const uint16_t* __restrict__ Vg, uint16_t* __restrict__ Og,
+               float* __restrict__ Lg, float* __restrict__ Ow, float* __restrict__ Lw,
+               int Nq, int Nk, int BH, int num_m_block, int num_splits, int total_items,
+               float c, float scale_abs, uint32_t qsign, uint32_t qkeep) {
+  typedef typename Vec16<T>::x8 t8_t;
+  typedef typename Vec16<T>::x4 t4_t;
+  constexpr int BN = Cfg<D>::BN;
+  constexpr int CH = D / 8;                  // 16-byte chunks per key row
+  constexpr int KT = BN / 32;                // 32-key sub-blocks per block
+  constexpr int KS = D / 16;                 // MFMA k-steps over the head dimension
+  constexpr int DT = D / 32;                 // 32-wide tiles of the head dimension
+  constexpr int U = BN / 16;                 // 16-key MFMA k-steps of the PV product
+  constexpr int ROWB = D * 2;                // bytes per key row
+  constexpr int RPP = rows_per_piece<D>();   // key rows per 1 KB piece
+  constexpr int PIECES = BN / RPP;           // pieces per K block
+  constexpr int LOADS = PIECES / kWaves;     // direct loads per thread per block
+  constexpr int TB = PIECES * kPiece;        // bytes per K block buffer
+  constexpr int TBV = BN * ROWB;             // bytes per V block buffer
+  constexpr int LOADS_V = TBV / 1024 / kWaves;  // direct V loads per thread per block
+  constexpr int NSEG = D / 16;               // 16-dim segments per V row
+  // V load addresses split into a per-lane part and a per-load part unless the
+  // 16-dim segments of a row and the 8 blocks of a load do not nest (D = 96).
+  constexpr bool V_SEP = 8 % NSEG == 0 || NSEG % 8 == 0;
+  constexpr int KTSTEP = lds_off<D>(32) - lds_off<D>(0); // 32 keys further in a K block
+  constexpr int NSTORE = DT * 4 + 1;         // O and L stores per wavefront per item
+  static_assert(LOADS >= 1 && PIECES % kWaves == 0, "block must split evenly over wavefronts");
+  static_assert(BN % 32 == 0 && BN % RPP == 0 && RPP * ROWB <= 1024, "piece geometry");
+  static_assert(k_layout_ok<D, BN>(), "K LDS layout: rows, pieces and banks");
+  static_assert(lds_off<D>(BN - 1) + ROWB <= TB, "K rows stay inside their buffer");
+  static_assert(LOADS_V >= 1 && TBV % (1024 * kWaves) == 0, "V block must split evenly");
+  static_assert(TBV + 16 * ROWB * (U - 1) + 8 * ROWB + 256 * (DT - 1) < 65536 &&
+                    2 * TBV + TB + KTSTEP * (KT - 1) + 32 * (KS - 1) < 65536,
+                "LDS offsets fit the 16-bit instruction offset");
+
+  __shared__ __attribute__((aligned(1024))) char smem[2 * TBV + 2 * TB];  // V0 V1 K0 K1
+  char* const Vb0 = smem;
+  char* const Kb0 = smem + 2 * TBV;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps LDS bases scalar
+  const int col = lane & 31;  // this lane's query row within the wavefront's 32
+  const int half = lane >> 5;
+
+  // Causal offset: key j is visible to query i when j <= i + off.
+  const int off = Nk - Nq;
+  const int nkb = (Nk + BN - 1) / BN;  // K/V blocks of a (batch, head)
+
+  // ---- work schedule.  The grid is persistent: each workgroup processes a
+  // sequence of work items (query block, batch*head).  Workgroup ids reach the
+  // 8 XCDs round-robin; XCD x takes a contiguous range of logical items (the
+  // query blocks of the same few heads, which read the same K/V and so share
+  // that XCD's L2), ordered head by head with a head's heaviest causal query
+  // block first.  The workgroups of an XCD walk that range in groups, in a
+  // snake order (group k: slot s takes position s, or P-1-s when k is odd), so
+  // that heavy and light causal blocks alternate per workgroup.
+  // (With fewer than 8 workgroups the ranges are split over that many.)
+  const int nx = gridDim.x < 8 ? (int)gridDim.x : 8;
+  const int xcd = blockIdx.x % nx;
+  const int lslot = blockIdx.x / nx;
+  const int P = ((int)gridDim.x - xcd + nx - 1) / nx;  // workgroups on this XCD
+  const int per = total_items / nx, rem = total_items % nx;
+  const int x_base = xcd * per + (xcd < rem ? xcd : rem);
+  const int x_items = per + (xcd < rem ? 1 : 0);
+  auto logical_of = [&](int k) -> int {  // the k-th item of this workgroup, or -1
+    const int pos = k * P + ((k & 1) ? P - 1 - lslot : lslot);
+    return pos < x_items ? x_base + pos : -1;
+  };
+
+  // ---- per-item state
+  int bh = 0, m = 0, q0 = 0, qrow = 0, j_beg = 0, j_end = 0, j_mask = 0;
+  int g0 = 0;      // running block count of this workgroup at the current item's first block
+  int k_item = 0;  // index of the current item in this workgroup's sequence
+  const uint16_t *Qh = Qg, *Kh = Kg, *Vh = Vg;
+  // O and L of the item's query block as buffer resources whose size covers
+  // only the rows < Nq: the hardware drops stores to rows past the end, so
+  // every wavefront issues the same number of stores for every item.
+  __amdgpu_buffer_rsrc_t o_rsrc, l_rsrc;
+  int gb = 0;  // buffer parity base: block j uses K and V buffers (gb + j) & 1
+  // logical item -> (batch*head, query block, split): splits fastest, then the
+  // query blocks of a head (heaviest causal block first), then the heads.
+  auto decode = [&](int logical, int& bh_, int& m_, int& s_) __attribute__((always_inline)) {
+    int mi = logical;
+    s_ = 0;
+    if constexpr (SPLIT) {
+      mi = logical / num_splits;
+      s_ = logical - mi * num_splits;
+    }
+    bh_ = mi / num_m_block;
+    mi -= bh_ * num_m_block;
+    m_ = CAUSAL ? num_m_block - 1 - mi : mi;
+  };
+  // K/V blocks up to the last key that query block m sees.  A query block
+  // whose last row sees no key (causal, Nq > Nk) has none: with splits its
+  // items are empty; without, it runs block 0 fully masked, which leaves every
+  // row with l = 0 (O = 0, L = -inf) and keeps the empty-item path out of the
+  // plain kernel.  (Nk >= 1 here; the host handles Nk == 0.)
+  auto blocks_of = [&](int m_) __attribute__((always_inline)) -> int {
+    if (CAUSAL) {
+      const int last_key = min(Nq, (m_ + 1) * kBM) - 1 + off;
+      if (last_key < 0) return SPLIT ? 0 : 1;
+      return min(last_key / BN + 1, nkb);
+    }
+    return nkb;
+  };
+  // KV blocks [beg, end) of split s of query block m: ceil(blocks / num_splits)
+  // blocks per split, so split 0 is empty only when the query block sees no
+  // key at all; later splits can be empty (SPLIT only).
+  auto range_of = [&](int m_, int s_, int& beg, int& end) __attribute__((always_inline)) {
+    const int jt = blocks_of(m_);
+    if constexpr (SPLIT) {
+      const int per = (jt + num_splits - 1) / num_splits;
+      beg = min(s_ * per, jt);
+      end = min(beg + per, jt);
+    } else {
+      beg = 0;
+      end = jt;
+    }
+  };
+  auto set_item = [&](int logical) __attribute__((always_inline)) {
+    int sp;
+    decode(logical, bh, m, sp);
+    range_of(m, sp, j_beg, j_end);
+    const size_t qslice = (size_t)bh * (size_t)Nq * D;
+    const size_t kslice = (size_t)bh * (size_t)Nk * D;
+    Qh = Qg + qslice;
+    Kh = Kg + kslice;
+    Vh = Vg + kslice;
+    const int rows = min(kBM, Nq - m * kBM);
+    if constexpr (SPLIT) {
+      const size_t prow = ((size_t)sp * BH + bh) * Nq + (size_t)m * kBM;  // first partial row
+      o_rsrc = __builtin_amdgcn_make_buffer_rsrc(Ow + prow * D, (short)0, rows * D * 4,
+                                                 kBufferFlags);
+      l_rsrc = __builtin_amdgcn_make_buffer_rsrc(Lw + prow, (short)0, rows * 4, kBufferFlags);
+    } else {
+      o_rsrc = __builtin_amdgcn_make_buffer_rsrc(Og + qslice + (size_t)m * kBM * D, (short)0,
+                                                 rows * ROWB, kBufferFlags);
+      l_rsrc = __builtin_amdgcn_make_buffer_rsrc(Lg + (size_t)bh * Nq + (size_t)m * kBM, (short)0,
+                                                 rows * 4, kBufferFlags);
+    }
+    q0 = m * kBM + wave * 32;  // first query row of this wavefront
+    qrow = q0 + col;
+    gb = g0 - j_beg;
+    // Blocks before j_mask need no mask for this wavefront (every key visible
+    // to every one of its rows: below the first row's diagonal, and whole).
+    const int seen = q0 + off + 1;  // keys visible to the wavefront's first row
+    j_mask = CAUSAL ? (seen <= 0 ? 0 : min(seen / BN, Nk / BN)) : Nk / BN;
+  };
+
+  // Q fragments (the B operand of S^T = K Q^T), kept in registers for an item.
+  // A negative scale flips Q's sign (exact); a zero scale zeroes Q, which gives
+  // the same all-zero logits.
+  t8_t qf[KS];
+  auto load_q = [&](const uint16_t* qh, int row) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4_t t = {0u, 0u, 0u, 0u};
+      if (row < Nq) t = *(const u32x4_t*)(qh + (size_t)row * D + ks * 16 + 8 * half);
+      qf[ks] = __builtin_bit_cast(t8_t, t);
+    }
+  };
+  // After the sign/zero fix, the fragments pass through an empty asm
+  // statement: the compiler waits for the Q loads there, once per item, and
+  // from then on sees register values with no load pending (it cannot see the
+  // direct LDS loads, so a pending Q load inside the KV loop would make it
+  // wait for every load in flight).
+  auto fix_q = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4_t t = (__builtin_bit_cast(u32x4_t, qf[ks]) & qkeep) ^ qsign;
+      asm volatile("" : "+v"(t));
+      qf[ks] = __builtin_bit_cast(t8_t, t);
+    }
+  };
+
+  // ---- global -> LDS staging.  K: load i of this thread fills piece
+  // b = wave*LOADS + i, whose lane L writes bytes 16L.. of the piece: row slot
+  // L / CH, 16-byte chunk L % CH of the key row r with blk(r) = b and
+  // slot(r) = L / CH.  That row is piece_row(b) (wave-uniform) plus
+  // slot_row(L / CH) (per lane).  For D = 96 a piece holds 4 rows (lanes
+  // 0..47); lanes 48..63 repeat the loads of lanes 0..15 into the piece's
+  // unread last 256 bytes, so every lane's address stays inside the tensor.
+  auto k_src_lane = [](int l) { return D == 96 && l >= 48 ? l - 48 : l; };
+  auto k_lane_row = [&](int l) { return slot_row<D>(k_src_lane(l) / CH); };
+  auto k_lane_col = [&](int l) { return (k_src_lane(l) % CH) * 8; };
+  const uint32_t lane_bytes = (uint32_t)(k_lane_row(lane) * D + k_lane_col(lane)) * 2;
+  // k0 goes through an empty asm statement: for the constant first blocks of an
+  // item the compiler would otherwise precompute the clamped tail addresses
+  // once, outside the item loop, and keep them in (spilled) registers.
+  auto issue_k = [&](const uint16_t* head, int k0, char* buf) __attribute__((always_inline)) {
+    asm volatile("" : "+s"(k0));
+    if (k0 + BN <= Nk) {
+      // Scalar base (the piece's first row) plus a constant 32-bit per-lane offset.
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        const int b = wave * LOADS + i;
+        lds_dma(head + (size_t)(k0 + piece_row<D>(b)) * D, lane_bytes,
+                lds_addr(buf + b * kPiece));
+      }
+    } else {
+      // Ragged last block: rows past Nk are clamped to row Nk-1 (their keys are masked).
+      const int tl = fresh_lane();
+      const int lane_row = k_lane_row(tl), lane_col = k_lane_col(tl);
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        const int b = wave * LOADS + i;
+        const int r = min(k0 + piece_row<D>(b) + lane_row, Nk - 1);
+        lds_dma(head + (size_t)r * D + lane_col, lds_addr(buf + b * kPiece));
+      }
+    }
+  };
+  // V: load i of this thread fills 1 KB chunk n = wave*LOADS_V + i of the
+  // block (v_row / v_dim above).  Where the geometry nests, the lane's share of
+  // the row and dims is the same for every n and n adds a wave-uniform offset;
+  // otherwise each load keeps its own per-lane offset.
+  uint32_t vlane[V_SEP ? 1 : LOADS_V];
+  if constexpr (V_SEP) {
+    vlane[0] = (uint32_t)(v_row<D>(0, lane) * D + v_dim<D>(0, lane)) * 2;
+  } else {
+#pragma unroll
+    for (int i = 0; i < LOADS_V; ++i)
+      vlane[i] = (uint32_t)(v_row<D>(wave * LOADS_V + i, lane) * D +
+                            v_dim<D>(wave * LOADS_V + i, lane)) * 2;
+  }
+  auto issue_v = [&](const uint16_t* head, int k0, char* buf) __attribute__((always_inline)) {
+    asm volatile("" : "+s"(k0));
+    const char* base = (const char*)(head + (size_t)k0 * D);
+    if (k0 + BN <= Nk) {
+#pragma unroll
+      for (int i = 0; i < LOADS_V; ++i) {
+        const int n = wave * LOADS_V + i;
+        if constexpr (V_SEP)
+          lds_dma(base + (v_row<D>(n, 0) * D + v_dim<D>(n, 0)) * 2, vlane[0],
+                  lds_addr(buf + n * 1024));
+        else
+          lds_dma(base, vlane[i], lds_addr(buf + n * 1024));
+      }
+    } else {
+      // Ragged last block: rows past Nk are clamped to row Nk-1 (P~ is 0 there).
+      const int tl = fresh_lane();
+#pragma unroll
+      for (int i = 0; i < LOADS_V; ++i) {
+        const int n = wave * LOADS_V + i;
+        const int r = min(k0 + v_row<D>(n, tl), Nk - 1);
+        lds_dma(head + (size_t)r * D + v_dim<D>(n, tl), lds_addr(buf + n * 1024));
+      }
+    }
+  };
+  // The first blocks of an item (blocks beg, beg+1, ... of its range): Q rows,
+  // K_beg and V_beg, and K_beg+1 if the range has it.  g is the running block
+  // count of this workgroup: block g of the sequence uses buffers g & 1.
+  auto issue_item_start = [&](const uint16_t* qh, const uint16_t* kh, const uint16_t* vh, int row,
+                              int beg, int blocks, int g) __attribute__((always_inline)) {
+    load_q(qh, row);
+    issue_k(kh, beg * BN, Kb0 + (g & 1) * TB);
+    issue_v(vh, beg * BN, Vb0 + (g & 1) * TBV);
+    if (blocks > 1) issue_k(kh, (beg + 1) * BN, Kb0 + ((g + 1) & 1) * TB);
+  };
+
+  // ---- LDS fragment addresses (bytes within a block buffer).
+  // K (A operand of S^T): key row kt*32 + col, dims 16*ks + 8*half ..+8.
+  const uint32_t kaddr = lds_off<D>(col) + 16 * half;
+  // V^T (A operand of O^T += V^T P^T) through ds_read_b64_tr_b16: within each
+  // group of 16 lanes, lane 4*r + c supplies the address of 4 consecutive dims
+  // (d0 + 4c ..) of key row (kbase + r); the hardware hands lane t of the
+  // group the 4 keys kbase..kbase+3 of dim d0 + t.  kbase = 16u + 4*half (the
+  // first 4 slots of the operand) or 16u + 8 + 4*half (the last 4), matching
+  // the keys 8*(r/4) + 4*half + r%4 that a lane's S^T accumulators hold.  With
+  // the V layout, the 16 lanes of a group read one contiguous 128-byte block:
+  // lane i at byte 8i of the block of rows kbase.. and dims d0..d0+15.
+  const uint32_t vaddr =
+      (uint32_t)(((lane >> 4) >> 1) * 4 * ROWB + ((lane >> 4) & 1) * 128 + 8 * (lane & 15));
+
+  f32x16_t o[DT];
+  float m_ref = kNegInf;  // reference max of the (sign-adjusted) raw logits
+  float l_part = 0.f;     // running sum over this lane's half of the keys
+
+  auto compute_S = [&](const char* kb, f32x16_t (&S)[KT]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+      S[kt] = f32x16_t{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const t8_t a = *(const t8_t*)(kb + kaddr + kt * KTSTEP + ks * 32);
+        S[kt] = mfma32x32x16(a, qf[ks], S[kt]);
+      }
+    }
+  };
+
+  // Block j's step of the online softmax (new running max, rescaled running
+  // sum, unnormalised probabilities) and the rescaled O update;
+  // `during` issues independent MFMA work (the next block's S) alongside.
+  auto consume = [&](auto masked_tag, int j, f32x16_t(&S)[KT],
+                     auto&& during) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    const int k0 = j * BN;
+    if constexpr (MASKED) {
+      // key = k0 + cr + 4*half with cr = kt*32 + 8*(r/4) + r%4 (a constant):
+      // it is hidden when cr + (k0 - q0 - off) > col - 4*half (after the lane's
+      // query row's diagonal) or cr + (k0 - Nk) >= -4*half (past the keys),
+      // i.e. when cr exceeds one per-lane threshold.
+      const int ml = fresh_lane();
+      const int mh = -4 * (ml >> 5);
+      int th = mh - (k0 - Nk) - 1;
+      if (CAUSAL) th = min(th, (ml & 31) + mh - (k0 - q0 - off));
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int cr = kt * 32 + 8 * (r / 4) + (r % 4);
+          S[kt][r] = cr > th ? kNegInf : S[kt][r];
+        }
+    }
+    during();
+    float mx = kNegInf;
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[kt][r]);
+    mx = halves_max(mx);
+    // The first block with a visible key always moves the reference (alpha =
+    // exp2(-inf) = 0 then: O and l are still zero).  A block can hold no key
+    // a row sees (mx = -inf: a split's range, or a row that sees no key at
+    // all): the reference then stays at -inf and the block adds nothing,
+    // without forming exp2(-inf + inf).
+    const bool move = m_ref == kNegInf ? mx != kNegInf : c * (mx - m_ref) > kTau;
+    const float alpha = move ? __builtin_amdgcn_exp2f(c * (m_ref - mx)) : 1.f;
+    m_ref = move ? mx : m_ref;
+    const float mc = m_ref == kNegInf ? 0.f : c * m_ref;
+    float ls = 0.f;
+    t8_t pb[U];
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kt][r], c, -mc));
+        ls += p;
+        pb[kt * 2 + r / 8][r % 8] = (T)p;  // round to nearest even
+      }
+    l_part = alpha * l_part + ls;
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+#pragma unroll
+      for (int t = 0; t < DT; ++t) o[t] *= alpha;
+    }
+    const char* vb = Vb0 + ((gb + j) & 1) * TBV + vaddr;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int t = 0; t < DT; ++t) {
+        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4_ptr_t)(vb + u * 16 * ROWB + t * 256));
+        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4_ptr_t)(vb + 8 * ROWB + u * 16 * ROWB + t * 256));
+        const t8_t a =
+            __builtin_bit_cast(t8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        o[t] = mfma32x32x16(a, pb[u], o[t]);
+      }
+  };
+
+  // One barrier per block: block j's V and block j+1's K have landed in LDS,
+  // and every wavefront is done with the buffers of block j-1, which the loads
+  // for blocks j+2 (K) and j+1 (V) issued right after reuse.
+  auto advance = [&](int j) __attribute__((always_inline)) {
+    // At an item's first block the previous item's O and L stores, issued
+    // last, need not have completed.
+    if (j == j_beg && k_item > 0) wait_vmcnt<NSTORE>();
+    else wait_vmcnt<0>();
+    lds_barrier();
+    if (j + 2 < j_end) issue_k(Kh, (j + 2) * BN, Kb0 + ((gb + j) & 1) * TB);
+    if (j + 1 < j_end) issue_v(Vh, (j + 1) * BN, Vb0 + ((gb + j + 1) & 1) * TBV);
+  };
+
+  // ---- item prologue: wait for Q and K_beg, then S for the first block.
+  // Vector memory operations complete in issue order, and V_beg and K_beg+1
+  // (and, after the first item, the previous item's O and L stores) were
+  // issued after K_beg, so the wait leaves that many operations in flight;
+  // then a barrier.  The first item's prologue is separate from the later
+  // items' (at the end of the loop), so that the compiler's own wait for the
+  // Q registers counts the stores on the later path instead of draining
+  // everything.
+  f32x16_t S_cur[KT];
+  auto prologue = [&](auto later_tag) __attribute__((always_inline)) {
+    fix_q();
+    const bool two = j_end - j_beg > 1;
+    if constexpr (decltype(later_tag)::value) {
+      if (two) wait_vmcnt<LOADS_V + LOADS + NSTORE>();
+      else wait_vmcnt<LOADS_V + NSTORE>();
+    } else {
+      if (two) wait_vmcnt<LOADS_V + LOADS>();
+      else wait_vmcnt<LOADS_V>();
+    }
+    lds_barrier();
+#pragma unroll
+    for (int t = 0; t < DT; ++t) o[t] = f32x16_t{};
+    m_ref = kNegInf;
+    l_part = 0.f;
+    compute_S(Kb0 + (g0 & 1) * TB, S_cur);
+  };
+  // The item after the current one, and its key range.
+  int next = -1, nbh = 0, nm = 0, nsp = 0, nbeg = 0, nend = 0;
+  auto look_ahead = [&]() __attribute__((always_inline)) {
+    next = logical_of(k_item + 1);
+    if (next >= 0) {
+      decode(next, nbh, nm, nsp);
+      range_of(nm, nsp, nbeg, nend);
+    }
+  };
+  // The next item's Q and first K/V blocks; issued while this item's last
+  // block is processed (or at once, for an empty item).
+  auto prefetch_next = [&]() __attribute__((always_inline)) {
+    if (next >= 0 && nend > nbeg) {
+      const size_t nqs = (size_t)nbh * (size_t)Nq * D, nks = (size_t)nbh * (size_t)Nk * D;
+      issue_item_start(Qg + nqs, Kg + nks, Vg + nks, nm * kBM + wave * 32 + col, nbeg,
+                       nend - nbeg, g0 + (j_end - j_beg));
+    }
+  };
+  // ---- item epilogue, after the KV loop: O = O / l once, L = m + ln(l).
+  // (A row that saw no key has l = 0: O = 0 and L = -inf.)
+  auto store_result = [&]() __attribute__((always_inline)) {
+    const float l_tot = halves_sum(l_part);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const int lrow = wave * 32 + col;  // this lane's row in the query block
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int dim = t * 32 + 8 * g + 4 * half;
+        if constexpr (SPLIT) {
+          f32x4_t w;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) w[r] = o[t][g * 4 + r] * inv;
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, w), o_rsrc,
+                                                 (lrow * D + dim) * 4, 0, 0);
+        } else {
+          t4_t w;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) w[r] = (T)(o[t][g * 4 + r] * inv);
+          __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, w), o_rsrc,
+                                                lrow * ROWB + dim * 2, 0, 0);
+        }
+      }
+    // Both halves of a row hold the same l and m: they store the same L.
+    __builtin_amdgcn_raw_buffer_store_b32(
+        __builtin_bit_cast(uint32_t,
+                           __builtin_fmaf(__builtin_amdgcn_logf(l_tot), kLn2, scale_abs * m_ref)),
+        l_rsrc, lrow * 4, 0, 0);
+  };
+  // Split items whose key range is empty (a split past the keys its rows see,
+  // or a query block that sees no key at all) are finished here (O_s = 0,
+  // L_s = -inf), so that the KV loop below is only ever entered through a
+  // prologue.  Returns false when the workgroup's sequence ends.
+  auto finish_empty_items = [&]() __attribute__((always_inline)) -> bool {
+    if constexpr (SPLIT) {
+      while (j_end == j_beg) {
+        look_ahead();
+        prefetch_next();
+#pragma unroll
+        for (int t = 0; t < DT; ++t) o[t] = f32x16_t{};
+        m_ref = kNegInf;
+        l_part = 0.f;
+        store_result();
+        if (next < 0) return false;
+        ++k_item;
+        set_item(next);
+      }
+    }
+    return true;
+  };
+
+  int logical = logical_of(0);
+  if (logical < 0) return;  // uniform for the workgroup
+  set_item(logical);
+  if (!finish_empty_items()) return;
+  if (k_item == 0) {
+    issue_item_start(Qh, Kh, Vh, qrow, j_beg, j_end - j_beg, g0);
+    prologue(std::false_type{});
+  } else {
+    prologue(std::true_type{});  // prefetched by the last empty item, stores after it
+  }
+
+  for (;;) {
+    look_ahead();
+    const int j_unmasked = min(j_mask, j_end - 1);  // unmasked blocks that have a successor
+    f32x16_t SB[KT];
+    int j = j_beg;
+    // Unrolled by two so that the S registers alternate between S_cur and SB
+    // instead of being copied every block.
+    for (; j + 2 <= j_unmasked; j += 2) {
+      advance(j);
+      consume(std::false_type{}, j, S_cur,
+              [&]() { compute_S(Kb0 + ((gb + j + 1) & 1) * TB, SB); });
+      advance(j + 1);
+      consume(std::false_type{}, j + 1, SB,
+              [&]() { compute_S(Kb0 + ((gb + j) & 1) * TB, S_cur); });
+    }
+    if (j < j_unmasked) {
+      advance(j);
+      consume(std::false_type{}, j, S_cur,
+              [&]() { compute_S(Kb0 + ((gb + j + 1) & 1) * TB, SB); });
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) S_cur[kt] = SB[kt];
+      ++j;
+    }
+    for (; j + 2 < j_end; j += 2) {
+      advance(j);
+      consume(std::true_type{}, j, S_cur,
+              [&]() { compute_S(Kb0 + ((gb + j + 1) & 1) * TB, SB); });
+      advance(j + 1);
+      consume(std::true_type{}, j + 1, SB,
+              [&]() { compute_S(Kb0 + ((gb + j) & 1) * TB, S_cur); });
+    }
+    if (j + 1 < j_end) {
+      advance(j);
+      consume(std::true_type{}, j, S_cur,
+              [&]() { compute_S(Kb0 + ((gb + j + 1) & 1) * TB, SB); });
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) S_cur[kt] = SB[kt];
+      ++j;
+    }
+    // Last block of the item.  Both K buffers and the other V buffer are free
+    // now, and so are the Q registers: the next item's Q, K_beg, V_beg,
+    // K_beg+1 go out here and overlap this block's softmax, its PV product and
+    // the O stores.
+    advance(j);
+    prefetch_next();
+    // Always the masked form: one copy of the code, and for an unmasked block
+    // the threshold test hides nothing.
+    consume(std::true_type{}, j, S_cur, [] {});
+    store_result();
+    if (next < 0) break;
+    g0 += j_end - j_beg;
+    ++k_item;
+    set_item(next);
+    if (!finish_empty_items()) break;
+    prologue(std::true_type{});
+  }
+}
+
+template <typename T, int D, bool CAUSAL, bool SPLIT>
+hipError_t launch(const FwdArgs& a) {
+  const int splits = SPLIT ? a.num_splits : 1;
+  const int total = a.num_m_block * a.BH * splits;
+  // Persistent grid: as many workgroups as fit on the chip at once (a 4-wave
+  // workgroup puts one wave on each SIMD of a CU, so kWavesPerSimd workgroups
+  // per CU), each walking its share of the work items.
+  int cus = 0;
+  const hipError_t e = cu_count(&cus);
+  if (e != hipSuccess) return e;
+  const int resident = Cfg<D>::kWavesPerSimd * cus;
+  const int grid = total < resident ? total : resident;
+  // The kernel works with c = |scale| * log2(e) > 0: a negative scale flips the
+  // sign of Q and a zero scale zeroes Q (both exact), with |scale| = 1 then.
+  const bool zero = a.scale == 0.f;
+  const float sa = zero ? 1.f : (a.scale < 0.f ? -a.scale : a.scale);
+  const uint32_t qsign = a.scale < 0.f ? 0x80008000u : 0u;
+  const uint32_t qkeep = zero ? 0u : 0xFFFFFFFFu;
+  hipLaunchKernelGGL((fa2_fwd_kernel<T, D, CAUSAL, SPLIT>), dim3(grid), dim3(kThreads), 0,
+                     a.stream, (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V,
+                     (uint16_t*)a.O, a.L, a.ws_O, a.ws_L, a.Nq, a.Nk, a.BH, a.num_m_block,
+                     splits, total, sa * kLog2e, sa, qsign, qkeep);
+  return hipGetLastError();
+}
+
+// Enqueue the kernel for element type T: one instantiation per head
+// dimension, mask and split setting.
+template <typename T>
+hipError_t dispatch_fwd_mfma(const FwdArgs& a) {
+  const bool split = a.num_splits > 0;
+  switch ((a.d * 2 + a.causal) * 2 + split) {
+#define FA2_CASE(D, C)                                                  \
+  case (D * 2 + C) * 2 + 0: return launch<T, D, (bool)C, false>(a);    \
+  case (D * 2 + C) * 2 + 1: return launch<T, D, (bool)C, true>(a);
+    FA2_CASE(32, 0)
+    FA2_CASE(32, 1)
+    FA2_CASE(64, 0)
+    FA2_CASE(64, 1)
+    FA2_CASE(96, 0)
+    FA2_CASE(96, 1)
+    FA2_CASE(128, 0)
+    FA2_CASE(128, 1)
+    FA2_CASE(256, 0)
+    FA2_CASE(256, 1)
+#undef FA2_CASE
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+}  // namespace fa2

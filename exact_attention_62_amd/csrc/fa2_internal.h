@@ -6,12 +6,18 @@
 
 namespace fa2 {
 
-// Query rows per workgroup (the pages' kBlockM).  bf16: four wavefronts of 32
-// rows each.  fp32 exact mode: four wavefronts of one row each.
-constexpr int kBlockM_bf16 = 128;
+// Query rows per workgroup (the pages' kBlockM).  16-bit types (bf16, fp16):
+// four wavefronts of 32 rows each.  fp32 exact mode: four wavefronts of one
+// row each.
+constexpr int kBlockM_mfma = 128;
 constexpr int kBlockM_f32 = 4;
-// Keys per K/V block of the bf16 kernel.
-constexpr int bf16_block_n(int d) { return d == 256 ? 32 : 64; }
+// Keys per K/V block of the 16-bit kernel, and its wavefronts per SIMD (the
+// workgroups that stay resident on one CU).
+constexpr int mfma_block_n(int d) { return d == 256 ? 32 : 64; }
+constexpr int mfma_waves_per_simd(int d) { return d == 256 ? 1 : 2; }
+
+// Element types, with the values of fa2_dtype_t.
+enum Elem { kBF16 = 0, kFP32 = 1, kFP16 = 2 };
 
 struct FwdArgs {
   const void* Q;
@@ -20,14 +26,17 @@ struct FwdArgs {
   void* O;
   float* L;
   int BH;           // B * H, the number of (batch, head) slices
-  int N;            // sequence length (queries = keys)
+  int Nq;           // query rows per slice (Q, O, L)
+  int Nk;           // key rows per slice (K, V)
   int d;            // head dimension
-  int causal;       // 0 or 1
+  int causal;       // 0 or 1; aligned bottom-right when Nq != Nk
   float scale;      // softmax scale
-  int num_m_block;  // ceil(N / kBlockM)
+  int num_m_block;  // ceil(Nq / kBlockM)
+  int elem;         // Elem of Q, K, V and O
   hipStream_t stream;
-  // Split-KV (bf16 only): num_splits > 0 writes partial results to ws_O
-  // [num_splits][BH][N][d] and ws_L [num_splits][BH][N] (fp32) instead of O/L.
+  // Split-KV (16-bit types only): num_splits > 0 writes partial results to
+  // ws_O [num_splits][BH][Nq][d] and ws_L [num_splits][BH][Nq] (fp32) instead
+  // of O/L.
   int num_splits = 0;
   float* ws_O = nullptr;
   float* ws_L = nullptr;
@@ -49,14 +58,18 @@ struct BwdArgs {
   hipStream_t stream;
 };
 
+// Compute units of the current device (queried once per device).
+hipError_t cu_count(int* cus);
+
 // Enqueue the kernel; returns the launch's hipError_t.
 hipError_t launch_fwd_bf16(const FwdArgs& a);
+hipError_t launch_fwd_fp16(const FwdArgs& a);
 hipError_t launch_fwd_f32(const FwdArgs& a);
-// Merge num_splits partial results (ws_O, ws_L) into O (bf16) and L.
-hipError_t launch_combine_bf16(const FwdArgs& a);
+// Merge num_splits partial results (ws_O, ws_L) into O (a.elem) and L.
+hipError_t launch_combine(const FwdArgs& a);
+// The result when there are no keys (a.Nk == 0): O = 0 and L = -inf.
+hipError_t launch_fill_no_keys(const FwdArgs& a);
 // Enqueue the backward pass (three kernels) on a.stream.
 hipError_t launch_bwd_bf16(const BwdArgs& a);
-// Workgroups of the bf16 kernel resident at once on the current device.
-hipError_t bf16_resident_workgroups(int d, int* slots);
 
 }  // namespace fa2

@@ -17,13 +17,13 @@ import threading
 import torch
 
 __all__ = ["FA2Error", "FlashAttention", "attention", "attention_backward", "fa2_bwd",
-           "fa2_bwd_workspace_size", "fa2_fwd", "fa2_fwd_splitkv", "fa2_launch_shape",
-           "fa2_num_splits", "fa2_splitkv_workspace_size", "fa2_strerror", "fa2_last_error",
-           "library_path", "load_library"]
+           "fa2_bwd_workspace_size", "fa2_fwd", "fa2_fwd_cross", "fa2_fwd_splitkv",
+           "fa2_launch_shape", "fa2_num_splits", "fa2_splitkv_workspace_size", "fa2_strerror",
+           "fa2_last_error", "library_path", "load_library"]
 
 FA2_OK, FA2_EINVAL, FA2_ENOTSUP, FA2_EHIP = 0, -1, -2, -3
-FA2_BF16, FA2_FP32 = 0, 1
-_DTYPES = {torch.bfloat16: FA2_BF16, torch.float32: FA2_FP32}
+FA2_BF16, FA2_FP32, FA2_FP16 = 0, 1, 2
+_DTYPES = {torch.bfloat16: FA2_BF16, torch.float32: FA2_FP32, torch.float16: FA2_FP16}
 
 _lib = None
 _lock = threading.Lock()
@@ -59,18 +59,21 @@ def load_library() -> ctypes.CDLL:
         lib.fa2_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int,
                                 ctypes.c_float, ctypes.c_int, vp]
         lib.fa2_fwd.restype = ctypes.c_int
+        lib.fa2_fwd_cross.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_int,
+                                      ctypes.c_float, ctypes.c_int, vp]
+        lib.fa2_fwd_cross.restype = ctypes.c_int
         lib.fa2_launch_shape.argtypes = [i64, i64, i64, i64, ctypes.c_int,
                                          ctypes.POINTER(i64), ctypes.POINTER(i64),
                                          ctypes.POINTER(i64)]
         lib.fa2_launch_shape.restype = ctypes.c_int
-        lib.fa2_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int,
-                                        ctypes.c_float, ctypes.c_int, ctypes.c_int, vp,
-                                        ctypes.c_size_t, vp]
+        lib.fa2_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                                        ctypes.c_int, ctypes.c_float, ctypes.c_int, ctypes.c_int,
+                                        vp, ctypes.c_size_t, vp]
         lib.fa2_fwd_splitkv.restype = ctypes.c_int
-        lib.fa2_splitkv_workspace_size.argtypes = [i64, i64, i64, i64, ctypes.c_int,
+        lib.fa2_splitkv_workspace_size.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int,
                                                    ctypes.POINTER(ctypes.c_size_t)]
         lib.fa2_splitkv_workspace_size.restype = ctypes.c_int
-        lib.fa2_num_splits.argtypes = [i64, i64, i64, i64, ctypes.POINTER(ctypes.c_int)]
+        lib.fa2_num_splits.argtypes = [i64, i64, i64, i64, i64, ctypes.POINTER(ctypes.c_int)]
         lib.fa2_num_splits.restype = ctypes.c_int
         lib.fa2_bwd.argtypes = [vp] * 9 + [i64, i64, i64, i64, ctypes.c_int, ctypes.c_float,
                                            ctypes.c_int, vp, ctypes.c_size_t, vp]
@@ -107,16 +110,18 @@ def fa2_launch_shape(B: int, H: int, N: int, d: int, dtype: torch.dtype = torch.
 
 
 def _check_tensors(q, k, v, o, lse):
-    if q.dim() != 4:
-        raise ValueError(f"q must be [B, H, N, d], got shape {tuple(q.shape)}")
-    B, H, N, d = q.shape
-    for name, t in (("k", k), ("v", v), ("o", o)):
-        if t.shape != q.shape:
-            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(q.shape)}")
+    """q, o [B, H, Nq, d]; k, v [B, H, Nk, d]; lse float32 [B, H, Nq].  Returns B, H, Nq, Nk, d."""
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError(f"q, k, v must be [B, H, N, d], got {tuple(q.shape)}, {tuple(k.shape)}")
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    for name, t, shape in (("k", k, (B, H, Nk, d)), ("v", v, (B, H, Nk, d)), ("o", o, q.shape)):
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
         if t.dtype != q.dtype:
             raise ValueError(f"{name} has dtype {t.dtype}, expected {q.dtype}")
-    if lse.shape != (B, H, N) or lse.dtype != torch.float32:
-        raise ValueError(f"lse must be float32 [{B}, {H}, {N}], got {lse.dtype} {tuple(lse.shape)}")
+    if lse.shape != (B, H, Nq) or lse.dtype != torch.float32:
+        raise ValueError(f"lse must be float32 [{B}, {H}, {Nq}], got {lse.dtype} {tuple(lse.shape)}")
     if q.dtype not in _DTYPES:
         raise ValueError(f"unsupported dtype {q.dtype}")
     tensors = (q, k, v, o, lse)
@@ -127,7 +132,12 @@ def _check_tensors(q, k, v, o, lse):
             raise ValueError("every tensor must be contiguous")
     if any(t.device != q.device for t in tensors):
         raise ValueError("every tensor must be on the same device")
-    return B, H, N, d
+    return B, H, Nq, Nk, d
+
+
+def _ptr(t: torch.Tensor):
+    """Device address of t, or NULL for an empty tensor (the library does not read it)."""
+    return t.data_ptr() if t.numel() else None
 
 
 def fa2_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
@@ -135,11 +145,13 @@ def fa2_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
             stream: torch.cuda.Stream | None = None) -> None:
     """Enqueue the forward pass on ``stream`` (default: the current stream).
 
-    q, k, v, o: contiguous [B, H, N, d] tensors of one dtype (bfloat16 or
-    float32) on the current GPU; lse: contiguous float32 [B, H, N].  Writes
-    o and lse in place.
+    q, k, v, o: contiguous [B, H, N, d] tensors of one dtype (bfloat16,
+    float16 or float32) on the current GPU; lse: contiguous float32 [B, H, N].
+    Writes o and lse in place.
     """
-    B, H, N, d = _check_tensors(q, k, v, o, lse)
+    B, H, N, Nk, d = _check_tensors(q, k, v, o, lse)
+    if Nk != N:
+        raise ValueError(f"fa2_fwd needs equal query and key lengths ({N} != {Nk}): use fa2_fwd_cross")
     dev = q.device
     if scale is None:
         scale = 1.0 / math.sqrt(d)
@@ -153,18 +165,42 @@ def fa2_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
     _check(st)
 
 
-def fa2_splitkv_workspace_size(B: int, H: int, N: int, d: int, num_splits: int) -> int:
+def fa2_fwd_cross(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+                  lse: torch.Tensor, causal: bool = False, scale: float | None = None,
+                  stream: torch.cuda.Stream | None = None) -> None:
+    """Enqueue the forward pass of Nq queries over Nk keys.
+
+    q, o: [B, H, Nq, d]; k, v: [B, H, Nk, d]; lse: float32 [B, H, Nq].  With
+    causal, key j is visible to query i iff j <= i + Nk - Nq; a query that sees
+    no key gets o = 0 and lse = -inf.  Writes o and lse in place.
+    """
+    B, H, Nq, Nk, d = _check_tensors(q, k, v, o, lse)
+    dev = q.device
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    lib = load_library()
+    with torch.cuda.device(dev):
+        st = lib.fa2_fwd_cross(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nk, d,
+                               1 if causal else 0, float(scale), _DTYPES[q.dtype],
+                               ctypes.c_void_p(stream.cuda_stream))
+    _check(st)
+
+
+def fa2_splitkv_workspace_size(B: int, H: int, Nq: int, Nk: int, d: int, num_splits: int) -> int:
     """Bytes of workspace fa2_fwd_splitkv needs with ``num_splits`` splits (no GPU call)."""
     out = ctypes.c_size_t(0)
-    _check(load_library().fa2_splitkv_workspace_size(B, H, N, d, int(num_splits), ctypes.byref(out)))
+    _check(load_library().fa2_splitkv_workspace_size(B, H, Nq, Nk, d, int(num_splits),
+                                                      ctypes.byref(out)))
     return out.value
 
 
-def fa2_num_splits(B: int, H: int, N: int, d: int, device=None) -> int:
+def fa2_num_splits(B: int, H: int, Nq: int, Nk: int, d: int, device=None) -> int:
     """The pages' num_splits rule for this problem on ``device`` (default: the current GPU)."""
     out = ctypes.c_int(0)
     with torch.cuda.device(device if device is not None else torch.cuda.current_device()):
-        _check(load_library().fa2_num_splits(B, H, N, d, ctypes.byref(out)))
+        _check(load_library().fa2_num_splits(B, H, Nq, Nk, d, ctypes.byref(out)))
     return out.value
 
 
@@ -172,10 +208,11 @@ def fa2_fwd_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.
                     lse: torch.Tensor, workspace: torch.Tensor, num_splits: int = 0,
                     causal: bool = False, scale: float | None = None,
                     stream: torch.cuda.Stream | None = None) -> None:
-    """Enqueue the split-KV forward pass (bfloat16).  ``workspace`` is a contiguous GPU
-    tensor of at least fa2_splitkv_workspace_size(...) bytes; num_splits = 0 takes
-    fa2_num_splits's choice.  Writes o and lse in place."""
-    B, H, N, d = _check_tensors(q, k, v, o, lse)
+    """Enqueue the split-KV forward pass (bfloat16 or float16; q [B, H, Nq, d] over k, v
+    [B, H, Nk, d]).  ``workspace`` is a contiguous GPU tensor of at least
+    fa2_splitkv_workspace_size(...) bytes; num_splits = 0 takes fa2_num_splits's choice.
+    Writes o and lse in place."""
+    B, H, Nq, Nk, d = _check_tensors(q, k, v, o, lse)
     dev = q.device
     if not workspace.is_cuda or not workspace.is_contiguous() or workspace.device != dev:
         raise ValueError("workspace must be a contiguous tensor on the inputs' GPU")
@@ -185,9 +222,9 @@ def fa2_fwd_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.
         stream = torch.cuda.current_stream(dev)
     lib = load_library()
     with torch.cuda.device(dev):
-        st = lib.fa2_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-                                 lse.data_ptr(), B, H, N, d, 1 if causal else 0, float(scale),
-                                 _DTYPES[q.dtype], int(num_splits), workspace.data_ptr(),
+        st = lib.fa2_fwd_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nk, d,
+                                 1 if causal else 0, float(scale), _DTYPES[q.dtype],
+                                 int(num_splits), _ptr(workspace),
                                  workspace.numel() * workspace.element_size(),
                                  ctypes.c_void_p(stream.cuda_stream))
     _check(st)
@@ -197,16 +234,23 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = 
               scale: float | None = None, num_splits: int | None = None):
     """Allocate O and L and run the forward pass.  Returns (o, lse).
 
-    num_splits=None runs fa2_fwd; an integer runs fa2_fwd_splitkv with that many
-    splits (0: the pages' rule), with a workspace allocated here."""
+    q is [B, H, Nq, d] and k, v [B, H, Nk, d] (Nq != Nk runs fa2_fwd_cross, causal
+    aligned bottom-right).  num_splits=None runs the plain pass; an integer runs
+    fa2_fwd_splitkv with that many splits (0: the pages' rule), with a workspace
+    allocated here."""
     o = torch.empty_like(q, memory_format=torch.contiguous_format)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
     if num_splits is None:
-        fa2_fwd(q, k, v, o, lse, causal=causal, scale=scale)
+        if Nq == Nk:
+            fa2_fwd(q, k, v, o, lse, causal=causal, scale=scale)
+        else:
+            fa2_fwd_cross(q, k, v, o, lse, causal=causal, scale=scale)
         return o, lse
-    B, H, N, d = q.shape
-    s = num_splits if num_splits > 0 else fa2_num_splits(B, H, N, d, q.device)
-    ws = torch.empty(fa2_splitkv_workspace_size(B, H, N, d, s), dtype=torch.uint8, device=q.device)
+    s = num_splits if num_splits > 0 else fa2_num_splits(B, H, Nq, Nk, d, q.device)
+    ws = torch.empty(fa2_splitkv_workspace_size(B, H, Nq, Nk, d, s), dtype=torch.uint8,
+                     device=q.device)
     fa2_fwd_splitkv(q, k, v, o, lse, ws, num_splits=s, causal=causal, scale=scale)
     return o, lse
 
@@ -224,7 +268,9 @@ def fa2_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
             scale: float | None = None, stream: torch.cuda.Stream | None = None) -> None:
     """Enqueue the backward pass (bfloat16): writes dq, dk, dv in place.  o and lse are
     fa2_fwd's outputs for q, k, v; workspace holds at least fa2_bwd_workspace_size bytes."""
-    B, H, N, d = _check_tensors(q, k, v, o, lse)
+    B, H, N, Nk, d = _check_tensors(q, k, v, o, lse)
+    if Nk != N:
+        raise ValueError(f"fa2_bwd needs equal query and key lengths ({N} != {Nk})")
     for name, t in (("do", do), ("dq", dq), ("dk", dk), ("dv", dv)):
         if t.shape != q.shape or t.dtype != q.dtype:
             raise ValueError(f"{name} must be {q.dtype} {tuple(q.shape)}")

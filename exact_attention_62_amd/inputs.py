@@ -35,7 +35,7 @@ class Workload:
     H: int
     N: int
     d: int
-    dtype: str  # "bf16" or "fp32"
+    dtype: str  # "bf16", "fp16" or "fp32"
     causal: Tuple[bool, ...]  # the mask settings this workload is run with
     qk: Tuple[str, float]  # ("normal", sigma) for Q and K
     v: Tuple[str, float]  # ("normal", sigma) or ("uniform", half-width) for V
@@ -47,13 +47,15 @@ class Workload:
 
     @property
     def torch_dtype(self) -> torch.dtype:
-        return {"bf16": torch.bfloat16, "fp32": torch.float32}[self.dtype]
+        return _DT[self.dtype]
 
     def flops(self, causal: bool) -> float:
         """Metric flop count: 4*B*H*N^2*d, halved when the causal mask is on."""
         f = 4.0 * self.B * self.H * self.N * self.N * self.d
         return f / 2.0 if causal else f
 
+
+_DT = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}
 
 WORKLOADS: Dict[str, Workload] = {
     w.name: w
@@ -83,38 +85,41 @@ def _draw(gen: torch.Generator, shape, dist: Tuple[str, float]) -> torch.Tensor:
 
 def make(workload: Workload | str, seed: int = 0, *, qk_sigma: float | None = None,
          B: int | None = None, H: int | None = None, N: int | None = None,
-         d: int | None = None, dtype: str | None = None):
+         d: int | None = None, dtype: str | None = None, Nk: int | None = None):
     """Draw (q, k, v) on the CPU for a named workload.
 
     Keyword overrides change the shape, dtype or Q/K sigma while keeping the
-    recipe (used for small parity cases).  Returns contiguous CPU tensors.
+    recipe (used for small parity cases and benchmark variants); Nk gives K
+    and V a length of their own (default: N).  Returns contiguous CPU tensors.
     """
     w = WORKLOADS[workload] if isinstance(workload, str) else workload
     B = w.B if B is None else B
     H = w.H if H is None else H
     N = w.N if N is None else N
     d = w.d if d is None else d
-    dt = {"bf16": torch.bfloat16, "fp32": torch.float32}[dtype or w.dtype]
+    Nk = N if Nk is None else Nk
+    dt = _DT[dtype or w.dtype]
     qk = w.qk if qk_sigma is None else ("normal", float(qk_sigma))
     gen = torch.Generator(device="cpu")
     gen.manual_seed(1000 * w.index + int(seed))
-    shape = (B, H, N, d)
-    q = _draw(gen, shape, qk).to(dt).contiguous()
-    k = _draw(gen, shape, qk).to(dt).contiguous()
-    v = _draw(gen, shape, w.v).to(dt).contiguous()
+    q = _draw(gen, (B, H, N, d), qk).to(dt).contiguous()
+    k = _draw(gen, (B, H, Nk, d), qk).to(dt).contiguous()
+    v = _draw(gen, (B, H, Nk, d), w.v).to(dt).contiguous()
     return q, k, v
 
 
 def make_random(B: int, H: int, N: int, d: int, seed: int, dtype: str = "bf16",
-                sigma: float = 1.0):
-    """Small ad-hoc problems for parity sweeps: N(0, sigma) Q and K, N(0, 1) V."""
+                sigma: float = 1.0, Nk: int | None = None):
+    """Small ad-hoc problems for parity sweeps: N(0, sigma) Q and K, N(0, 1) V.
+
+    Q has N rows; K and V have Nk rows (default N)."""
     gen = torch.Generator(device="cpu")
     gen.manual_seed(0x5EED0000 + int(seed))
-    dt = {"bf16": torch.bfloat16, "fp32": torch.float32}[dtype]
-    shape = (B, H, N, d)
-    q = (torch.randn(shape, generator=gen) * sigma).to(dt).contiguous()
-    k = (torch.randn(shape, generator=gen) * sigma).to(dt).contiguous()
-    v = torch.randn(shape, generator=gen).to(dt).contiguous()
+    dt = _DT[dtype]
+    Nk = N if Nk is None else Nk
+    q = (torch.randn((B, H, N, d), generator=gen) * sigma).to(dt).contiguous()
+    k = (torch.randn((B, H, Nk, d), generator=gen) * sigma).to(dt).contiguous()
+    v = torch.randn((B, H, Nk, d), generator=gen).to(dt).contiguous()
     return q, k, v
 
 
@@ -123,5 +128,4 @@ def make_upstream(B: int, H: int, N: int, d: int, seed: int, dtype: str = "bf16"
     the inputs (generator seed 0x6D0E0000 + seed)."""
     gen = torch.Generator(device="cpu")
     gen.manual_seed(0x6D0E0000 + int(seed))
-    dt = {"bf16": torch.bfloat16, "fp32": torch.float32}[dtype]
-    return torch.randn((B, H, N, d), generator=gen).to(dt).contiguous()
+    return torch.randn((B, H, N, d), generator=gen).to(_DT[dtype]).contiguous()

@@ -6,9 +6,9 @@
  * pseudo-code commentary and the thread-block grid section;
  * "flash-attention123和ring-attention", 优化1-优化4):
  *
- *   for every batch b < B, head h < H and query row i < N:
- *     S[i][j] = scale * sum_k Q[b][h][i][k] * K[b][h][j][k]       (j < N)
- *     S[i][j] = -inf where causal != 0 and j > i                   (top-left aligned)
+ *   for every batch b < B, head h < H and query row i < Nq:
+ *     S[i][j] = scale * sum_k Q[b][h][i][k] * K[b][h][j][k]       (j < Nk)
+ *     S[i][j] = -inf where causal != 0 and j > i + Nk - Nq        (bottom-right aligned)
  *     O[b][h][i][:] = sum_j softmax_j(S[i][:]) * V[b][h][j][:]
  *     L[b][h][i]    = m_i + ln(l_i),  m_i = max_j S[i][j],  l_i = sum_j exp(S[i][j] - m_i)
  *
@@ -18,10 +18,16 @@
  * blocks that the causal mask covers entirely skipped, and only O and the
  * per-row logsumexp L written to memory.
  *
+ * With Nq == Nk == N (fa2_fwd) the mask is the usual j > i.  The grid follows
+ * the query length alone (page "FlashAttention学习笔记(2)", section "V2中的thread
+ * blocks排布"), so the key length may differ (fa2_fwd_cross).  A query that sees
+ * no key (causal with Nq > Nk, its first Nq - Nk rows, or Nk == 0) has an empty
+ * sum: L = -inf and O = 0.
+ *
  * Conventions shared by every entry point:
- *   - Layout: Q, K, V and O are contiguous row-major [B][H][N][d] arrays of the
- *     element type given by `dtype`; L is a contiguous [B][H][N] float32 array.
- *     Queries and keys have the same length N.
+ *   - Layout: Q and O are contiguous row-major [B][H][Nq][d] arrays and K, V
+ *     [B][H][Nk][d] arrays of the element type given by `dtype`; L is a
+ *     contiguous [B][H][Nq] float32 array.
  *   - Ownership: every array pointer is device memory of the current HIP device,
  *     allocated and owned by the caller.  The library allocates nothing, frees
  *     nothing and keeps no pointer after the call returns.  O and L (and a
@@ -53,7 +59,8 @@ typedef enum {
 
 typedef enum {
   FA2_BF16 = 0, /* bfloat16 Q/K/V/O; QK^T and PV on bf16 MFMA with float32 accumulation      */
-  FA2_FP32 = 1  /* float32 Q/K/V/O; every step in float32 (exact mode, meant for small sizes) */
+  FA2_FP32 = 1, /* float32 Q/K/V/O; every step in float32 (exact mode, meant for small sizes) */
+  FA2_FP16 = 2  /* float16 Q/K/V/O; QK^T and PV on fp16 MFMA with float32 accumulation       */
 } fa2_dtype_t;
 
 /*
@@ -63,12 +70,13 @@ typedef enum {
  *   O        [B][H][N][d] output (same dtype), device memory, 16-byte aligned.
  *   L        [B][H][N] float32 output, the natural-log logsumexp of the scaled,
  *            masked logits of each row, device memory, 4-byte aligned.
- *   B, H, N  batch size, head count, sequence length; each >= 0.  A call with
- *            B*H*N == 0 does nothing and returns FA2_OK (pointers may be NULL).
- *   d        head dimension: 64, 128 or 256 (other values: FA2_ENOTSUP).
+ *   B, H, N  batch size, head count, sequence length (queries = keys); each
+ *            >= 0.  A call with B*H*N == 0 does nothing and returns FA2_OK
+ *            (pointers may be NULL).
+ *   d        head dimension: 32, 64, 96, 128 or 256 (other values: FA2_ENOTSUP).
  *   causal   0: every key is visible; 1: key j is visible to row i iff j <= i.
  *   scale    softmax scale applied to Q K^T; any finite value (0 included).
- *   dtype    FA2_BF16 or FA2_FP32.
+ *   dtype    FA2_BF16, FA2_FP16 or FA2_FP32.
  *   stream   hipStream_t to enqueue on, or NULL for the default stream.
  *
  * Every element of O and L is written.  Results are deterministic: the same
@@ -77,6 +85,26 @@ typedef enum {
 fa2_status_t fa2_fwd(const void* Q, const void* K, const void* V, void* O, float* L,
                      int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
                      fa2_dtype_t dtype, void* stream);
+
+/*
+ * fa2_fwd_cross - the forward pass with Nq queries over Nk keys (cross
+ * attention; with causal, a block of queries appended after Nk - Nq earlier
+ * positions, as in decoding).
+ *
+ *   Q, O     [B][H][Nq][d]; K, V [B][H][Nk][d]; L [B][H][Nq]; alignment and
+ *            memory as for fa2_fwd.
+ *   Nq, Nk   query and key lengths, each >= 0.  B*H*Nq == 0 does nothing and
+ *            returns FA2_OK.  Nk == 0 writes O = 0 and L = -inf (K and V are
+ *            not read and may be NULL then).
+ *   causal   1: key j is visible to query i iff j <= i + Nk - Nq (the last
+ *            query sees every key); rows that see no key get O = 0, L = -inf.
+ *   B, H, d, scale, dtype, stream: as for fa2_fwd.
+ *
+ * fa2_fwd(..., N, ...) is fa2_fwd_cross(..., N, N, ...).
+ */
+fa2_status_t fa2_fwd_cross(const void* Q, const void* K, const void* V, void* O, float* L,
+                           int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int causal,
+                           float scale, fa2_dtype_t dtype, void* stream);
 
 /* Largest number of key/value splits fa2_fwd_splitkv accepts. */
 #define FA2_MAX_SPLITS 128
@@ -89,17 +117,19 @@ fa2_status_t fa2_fwd(const void* Q, const void* K, const void* V, void* O, float
  * allow splitting the key/value sequence as well as the queries when the
  * (query block, batch, head) grid leaves the GPU partly idle, at the price of
  * one more combine step: each row of O then gets one part from every split.
- * Here the K/V blocks a query block visits (all of them, or those up to the
+ * It is the decoding shape's path: few queries (Nq) over a long key sequence
+ * (Nk).  The K/V blocks a query block visits (all of them, or those up to the
  * diagonal when causal) are cut into num_splits contiguous parts of
  * ceil(blocks / num_splits) blocks.  Each (query block, batch, head, part) is a
  * work item that writes its partial result to the workspace: O_s, normalised
  * within its keys, and L_s = m_s + ln(l_s) (-inf for a row that sees none of
  * its keys).  A second kernel on the same stream merges them:
- *   L = ln sum_s exp(L_s),   O = sum_s exp(L_s - L) O_s.
- * The result is the operation fa2_fwd computes, up to rounding.
+ *   L = ln sum_s exp(L_s),   O = sum_s exp(L_s - L) O_s
+ * (a row that sees no key in any split: O = 0, L = -inf).  The result is the
+ * operation fa2_fwd_cross computes, up to rounding.
  *
- *   Q, K, V, O, L, B, H, N, d, causal, scale, stream: as for fa2_fwd.
- *   dtype            FA2_BF16 only (FA2_FP32 gives FA2_ENOTSUP).
+ *   Q, K, V, O, L, B, H, Nq, Nk, d, causal, scale, stream: as for fa2_fwd_cross.
+ *   dtype            FA2_BF16 or FA2_FP16 (FA2_FP32 gives FA2_ENOTSUP).
  *   num_splits       1..FA2_MAX_SPLITS, or 0 for the value fa2_num_splits gives.
  *   workspace        device memory owned by the caller, 16-byte aligned, of at
  *                    least fa2_splitkv_workspace_size() bytes for the number of
@@ -111,30 +141,32 @@ fa2_status_t fa2_fwd(const void* Q, const void* K, const void* V, void* O, float
  * Every element of O and L is written; results are deterministic.
  */
 fa2_status_t fa2_fwd_splitkv(const void* Q, const void* K, const void* V, void* O, float* L,
-                             int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
-                             fa2_dtype_t dtype, int num_splits, void* workspace,
+                             int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int causal,
+                             float scale, fa2_dtype_t dtype, int num_splits, void* workspace,
                              size_t workspace_bytes, void* stream);
 
 /*
  * fa2_splitkv_workspace_size - bytes of workspace fa2_fwd_splitkv needs with
- * num_splits splits: num_splits * B*H*N * (d + 1) * 4 (the float32 partial O_s
- * and L_s of every split).  Host-only: makes no HIP call.  Returns the
+ * num_splits splits: num_splits * B*H*Nq * (d + 1) * 4 (the float32 partial
+ * O_s and L_s of every split).  Host-only: makes no HIP call.  Returns the
  * argument errors fa2_fwd_splitkv would (sizes, d, num_splits out of range).
  */
-fa2_status_t fa2_splitkv_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d,
+fa2_status_t fa2_splitkv_workspace_size(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
                                         int num_splits, size_t* bytes);
 
 /*
  * fa2_num_splits - the number of splits the pages' rule chooses for this
  * problem on the current device (page "Flash Attention V2原理解读", the
- * thread-block grid section): for every candidate s in 1..min(K/V blocks,
- * FA2_MAX_SPLITS), the utilisation of the GPU by items * s work items, items
- * = B*H*ceil(N / kBlockM), over the device's concurrently resident workgroups
- * (the busy fraction of the last round: (n / slots) / ceil(n / slots)); then
- * the smallest s whose utilisation is at least 0.95 of the best.  Queries the
- * current device's compute-unit count (a HIP call; FA2_EHIP if that fails).
+ * thread-block grid section): for every candidate s in 1..min(K/V blocks of
+ * the Nk keys, FA2_MAX_SPLITS), the utilisation of the GPU by items * s work
+ * items, items = B*H*ceil(Nq / kBlockM), over the device's concurrently
+ * resident workgroups (the busy fraction of the last round:
+ * (n / slots) / ceil(n / slots)); then the smallest s whose utilisation is at
+ * least 0.95 of the best.  Queries the current device's compute-unit count (a
+ * HIP call; FA2_EHIP if that fails).
  */
-fa2_status_t fa2_num_splits(int64_t B, int64_t H, int64_t N, int64_t d, int* num_splits);
+fa2_status_t fa2_num_splits(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                            int* num_splits);
 
 /*
  * fa2_launch_shape - the work decomposition fa2_fwd uses, as a host-only query.
@@ -144,9 +176,9 @@ fa2_status_t fa2_num_splits(int64_t B, int64_t H, int64_t N, int64_t d, int* num
  * blocks (page "FlashAttention学习笔记(2)", section "V2中的thread blocks排布";
  * "Flash Attention V2原理解读", the thread-block grid section).  Writes
  * kBlockM, num_m_block and the item count B*H*num_m_block through the
- * non-NULL out pointers.  The bf16 kernel runs the items on a persistent grid
- * of min(items, resident workgroups) workgroups; the fp32 kernel launches one
- * workgroup per item.  Makes no HIP call.  Returns FA2_EINVAL / FA2_ENOTSUP
+ * non-NULL out pointers (N is the query length).  The 16-bit kernel runs the
+ * items on a persistent grid of min(items, resident workgroups) workgroups;
+ * the fp32 kernel launches one workgroup per item.  Makes no HIP call.  Returns FA2_EINVAL / FA2_ENOTSUP
  * for arguments fa2_fwd would reject on those grounds.
  */
 fa2_status_t fa2_launch_shape(int64_t B, int64_t H, int64_t N, int64_t d, fa2_dtype_t dtype,

@@ -33,9 +33,9 @@ def _declared_functions():
 
 def test_header_declares_the_boundary():
     assert _declared_functions() == ["fa2_bwd", "fa2_bwd_workspace_size", "fa2_fwd",
-                                     "fa2_fwd_splitkv", "fa2_last_error", "fa2_launch_shape",
-                                     "fa2_num_splits", "fa2_splitkv_workspace_size",
-                                     "fa2_strerror"]
+                                     "fa2_fwd_cross", "fa2_fwd_splitkv", "fa2_last_error",
+                                     "fa2_launch_shape", "fa2_num_splits",
+                                     "fa2_splitkv_workspace_size", "fa2_strerror"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -73,7 +73,7 @@ def test_invalid_arguments_are_rejected_before_any_hip_call(kw, needle):
     assert needle in F.fa2_last_error()
 
 
-@pytest.mark.parametrize("kw", [dict(d=96), dict(d=32), dict(d=512), dict(dtype=7)])
+@pytest.mark.parametrize("kw", [dict(d=48), dict(d=16), dict(d=512), dict(d=0), dict(dtype=7)])
 def test_unsupported_requests(kw):
     assert _fwd(**kw) == F.FA2_ENOTSUP
     assert F.fa2_last_error()
@@ -93,9 +93,44 @@ def test_strerror_covers_every_status():
 
 
 @pytest.mark.skipif(torch.cuda.is_available(), reason="needs a host without a visible GPU")
-def test_valid_call_without_a_device_reports_the_hip_error():
-    assert _fwd() == F.FA2_EHIP
+@pytest.mark.parametrize("kw", [dict(), dict(dtype=F.FA2_FP16), dict(dtype=F.FA2_FP32),
+                                dict(d=32), dict(d=96)])
+def test_valid_call_without_a_device_reports_the_hip_error(kw):
+    assert _fwd(**kw) == F.FA2_EHIP
     assert "hip" in F.fa2_last_error().lower()
+
+
+# ---- query and key lengths that differ -------------------------------------------------
+def _cross(q=FAKE, k=FAKE + 0x100000, v=FAKE + 0x200000, o=FAKE + 0x300000, L=FAKE + 0x400000,
+           B=1, H=1, Nq=16, Nk=40, d=64, causal=1, scale=0.125, dtype=F.FA2_BF16):
+    lib = F.load_library()
+    return lib.fa2_fwd_cross(q, k, v, o, L, B, H, Nq, Nk, d, causal, scale, dtype, None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(Nq=-1), F.FA2_EINVAL, "sizes must be >= 0"),
+    (dict(Nk=-2), F.FA2_EINVAL, "sizes must be >= 0"),
+    (dict(Nk=(1 << 31) // 256 + 1), F.FA2_EINVAL, "maximum"),
+    (dict(k=None), F.FA2_EINVAL, "K is NULL"),
+    # K and V hold 40 rows of 128 bytes: O placed 1 KB after K's start overlaps K
+    (dict(o=FAKE + 0x100000 + 1024), F.FA2_EINVAL, "O overlaps K"),
+    (dict(d=80), F.FA2_ENOTSUP, "d=80"),
+])
+def test_cross_invalid_arguments_before_any_hip_call(kw, status, needle):
+    assert _cross(**kw) == status
+    assert needle in F.fa2_last_error()
+
+
+def test_cross_empty_query_side_is_a_no_op():
+    assert _cross(q=None, k=None, v=None, o=None, L=None, Nq=0) == F.FA2_OK
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="needs a host without a visible GPU")
+def test_cross_without_keys_does_not_need_k_or_v():
+    # Nk == 0 passes the argument checks with K = V = NULL (they are not read); the call then
+    # needs the device.
+    assert _cross(k=None, v=None, Nk=0) == F.FA2_EHIP
+    assert "K is NULL" not in F.fa2_last_error()
 
 
 def test_grid_matches_the_pages_worked_example():
@@ -144,7 +179,7 @@ def test_last_error_is_thread_local():
 
     def other():
         seen["msg"] = F.fa2_last_error()
-        _fwd(d=96)
+        _fwd(d=48)
 
     t = threading.Thread(target=other)
     t.start()
@@ -156,31 +191,34 @@ def test_last_error_is_thread_local():
 # ---- split-KV entry points ---------------------------------------------------------------
 def _split(ws=FAKE + 0x500000, ws_bytes=1 << 24, num_splits=2, dtype=F.FA2_BF16, **kw):
     args = dict(q=FAKE, k=FAKE + 0x100000, v=FAKE + 0x200000, o=FAKE + 0x300000,
-                L=FAKE + 0x400000, B=1, H=1, N=16, d=64, causal=0, scale=0.125)
+                L=FAKE + 0x400000, B=1, H=1, Nq=16, Nk=16, d=64, causal=0, scale=0.125)
     args.update(kw)
     lib = F.load_library()
     return lib.fa2_fwd_splitkv(args["q"], args["k"], args["v"], args["o"], args["L"], args["B"],
-                               args["H"], args["N"], args["d"], args["causal"], args["scale"],
-                               dtype, num_splits, ws, ws_bytes, None)
+                               args["H"], args["Nq"], args["Nk"], args["d"], args["causal"],
+                               args["scale"], dtype, num_splits, ws, ws_bytes, None)
 
 
 def test_workspace_size_formula():
-    # num_splits * B*H*N * (d + 1) float32 values: O_s and L_s of every split
-    assert F.fa2_splitkv_workspace_size(2, 4, 1024, 64, 8) == 8 * 2 * 4 * 1024 * 65 * 4
-    assert F.fa2_splitkv_workspace_size(1, 1, 1, 256, 1) == 257 * 4
-    assert F.fa2_splitkv_workspace_size(0, 4, 1024, 64, 3) == 0
+    # num_splits * B*H*Nq * (d + 1) float32 values: O_s and L_s of every split
+    assert F.fa2_splitkv_workspace_size(2, 4, 1024, 1024, 64, 8) == 8 * 2 * 4 * 1024 * 65 * 4
+    assert F.fa2_splitkv_workspace_size(1, 1, 1, 1, 256, 1) == 257 * 4
+    assert F.fa2_splitkv_workspace_size(0, 4, 1024, 1024, 64, 3) == 0
+    assert F.fa2_splitkv_workspace_size(1, 2, 5, 4096, 128, 3) == 3 * 2 * 5 * 129 * 4
+    assert F.fa2_splitkv_workspace_size(1, 1, 8, 8, 96, 2) == 2 * 8 * 97 * 4
 
 
 @pytest.mark.parametrize("s", [0, -1, 129])
 def test_workspace_size_rejects_split_counts(s):
     with pytest.raises(F.FA2Error) as e:
-        F.fa2_splitkv_workspace_size(1, 1, 64, 64, s)
+        F.fa2_splitkv_workspace_size(1, 1, 64, 64, 64, s)
     assert e.value.status == F.FA2_EINVAL and "num_splits" in str(e.value)
 
 
 @pytest.mark.parametrize("kw,status,needle", [
-    (dict(dtype=F.FA2_FP32), F.FA2_ENOTSUP, "FA2_BF16 only"),
-    (dict(d=96), F.FA2_ENOTSUP, "d=96"),
+    (dict(dtype=F.FA2_FP32), F.FA2_ENOTSUP, "FA2_BF16 and FA2_FP16 only"),
+    (dict(d=48), F.FA2_ENOTSUP, "d=48"),
+    (dict(Nk=-1), F.FA2_EINVAL, "sizes must be >= 0"),
     (dict(num_splits=-1), F.FA2_EINVAL, "num_splits=-1"),
     (dict(num_splits=200), F.FA2_EINVAL, "num_splits=200"),
     (dict(ws=None), F.FA2_EINVAL, "workspace is NULL"),
@@ -197,12 +235,13 @@ def test_splitkv_invalid_arguments_before_any_hip_call(kw, status, needle):
 
 def test_splitkv_empty_problem_is_a_no_op():
     assert _split(q=None, k=None, v=None, o=None, L=None, ws=None, ws_bytes=0, B=0) == F.FA2_OK
+    assert _split(q=None, k=None, v=None, o=None, L=None, ws=None, ws_bytes=0, Nq=0) == F.FA2_OK
 
 
 @pytest.mark.skipif(torch.cuda.is_available(), reason="needs a host without a visible GPU")
 def test_num_splits_without_a_device_reports_the_hip_error():
     out = ctypes.c_int(0)
-    assert F.load_library().fa2_num_splits(1, 1, 1024, 64, ctypes.byref(out)) == F.FA2_EHIP
+    assert F.load_library().fa2_num_splits(1, 1, 1024, 1024, 64, ctypes.byref(out)) == F.FA2_EHIP
     assert _split(num_splits=0) == F.FA2_EHIP  # the rule needs the device's CU count
 
 

@@ -43,8 +43,8 @@ def _run_split(q, k, v, causal, num_splits, scale=None):
     qd, kd, vd = (t.cuda() for t in (q, k, v))
     o = torch.full_like(qd, float("nan"))
     lse = torch.full((B, H, N), float("nan"), dtype=torch.float32, device="cuda")
-    s = num_splits if num_splits > 0 else fa2_num_splits(B, H, N, d)
-    ws = torch.full((fa2_splitkv_workspace_size(B, H, N, d, s) // 4,), float("nan"),
+    s = num_splits if num_splits > 0 else fa2_num_splits(B, H, N, N, d)
+    ws = torch.full((fa2_splitkv_workspace_size(B, H, N, N, d, s) // 4,), float("nan"),
                     dtype=torch.float32, device="cuda")
     fa2_fwd_splitkv(qd, kd, vd, o, lse, ws, num_splits=num_splits, causal=causal, scale=scale)
     torch.cuda.synchronize()
@@ -111,4 +111,4 @@ def test_device_num_splits_follows_the_pages_rule(shape):
     bn = 32 if d == 256 else 64            # keys per K/V block
     items = B * H * -(-N // 128)
     expected = num_splits_heuristic(items, slots, min(-(-N // bn), 128))
-    assert fa2_num_splits(B, H, N, d) == expected
+    assert fa2_num_splits(B, H, N, N, d) == expected

@@ -1,0 +1,228 @@
+"""Parity of the variants of the forward pass (through the C ABI) with the fp64 oracle:
+fp16 inputs, head dimensions 32 and 96, and query/key lengths that differ.
+
+Tolerances (max-abs): bf16 O 2e-2, L 1e-3; float32 1e-5 on both; fp16 O 1e-2, L 1e-3.  The
+fp16 bound: O is rounded once to fp16 (half an ulp is <= 2^-9 for |O| < 8) and P~ once
+(relative 2^-11, so at most 2^-11 * max|V| ~ 3e-3 for N(0, 1) values), about half of the
+bf16 figures; L comes from fp32 sums in both cases.
+
+Rows that see no key (causal with Nq > Nk, or Nk = 0) must give O = 0 exactly and L = -inf,
+as the oracle does; every other output must be finite.  Outputs are pre-filled with NaN, so
+an element that is not written shows up.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from exact_attention_62_amd import (attention, fa2_fwd_cross, fa2_fwd_splitkv, fa2_num_splits,
+                                    fa2_splitkv_workspace_size)
+from exact_attention_62_amd.inputs import make, make_random
+from oracle import attention_fp64, attention_rows_fp64
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": (2e-2, 1e-3), "fp16": (1e-2, 1e-3), "fp32": (1e-5, 1e-5)}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+
+
+def _say(msg):
+    print(f"\n[variants] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def _cmp(o, lse, O_ref, L_ref, dtype, what):
+    otol, ltol = TOL[dtype]
+    o64 = o.double().cpu().numpy()
+    l64 = lse.double().cpu().numpy()
+    assert np.all(np.isfinite(o64)), f"{what}: non-finite O"
+    none = np.isneginf(L_ref)  # rows that see no key
+    assert np.array_equal(np.isneginf(l64), none), f"{what}: L = -inf on the wrong rows"
+    assert np.all(np.isfinite(l64[~none])), f"{what}: non-finite L"
+    assert np.all(o64[none] == 0.0), f"{what}: O != 0 on a row that sees no key"
+    eo = np.abs(o64 - O_ref).max() if O_ref.size else 0.0
+    el = np.abs(l64[~none] - L_ref[~none]).max() if (~none).any() else 0.0
+    assert eo <= otol, f"{what}: max |O - O_ref| = {eo:.3e} > {otol}"
+    assert el <= ltol, f"{what}: max |L - L_ref| = {el:.3e} > {ltol}"
+    return eo, el
+
+
+def _cross(q, k, v, causal, scale=None):
+    """fa2_fwd_cross on NaN-filled outputs."""
+    qd, kd, vd = (t.cuda() for t in (q, k, v))
+    o = torch.full_like(qd, float("nan"))
+    lse = torch.full(q.shape[:3], float("nan"), dtype=torch.float32, device="cuda")
+    fa2_fwd_cross(qd, kd, vd, o, lse, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def _split(q, k, v, causal, num_splits, scale=None):
+    """fa2_fwd_splitkv on NaN-filled outputs and workspace."""
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    qd, kd, vd = (t.cuda() for t in (q, k, v))
+    o = torch.full_like(qd, float("nan"))
+    lse = torch.full((B, H, Nq), float("nan"), dtype=torch.float32, device="cuda")
+    s = num_splits if num_splits > 0 else fa2_num_splits(B, H, Nq, Nk, d)
+    ws = torch.full((fa2_splitkv_workspace_size(B, H, Nq, Nk, d, s) // 4,), float("nan"),
+                    dtype=torch.float32, device="cuda")
+    fa2_fwd_splitkv(qd, kd, vd, o, lse, ws, num_splits=num_splits, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+# ------------------------------------------------------------------- fp16, square problems
+
+FP16_SQUARE = [
+    (1, 1, 1, 64), (2, 3, 257, 32), (1, 2, 300, 96), (2, 2, 513, 128), (1, 2, 300, 256),
+    (1, 1, 1000, 64), (1, 3, 129, 96), (3, 1, 200, 32),
+]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", FP16_SQUARE, ids=lambda s: "x".join(map(str, s)))
+def test_fp16_square(shape, causal):
+    B, H, N, d = shape
+    _say(f"fp16 B={B} H={H} N={N} d={d} causal={causal}")
+    q, k, v = make_random(B, H, N, d, seed=11 * N + d + causal, dtype="fp16")
+    O, L = attention_fp64(q, k, v, causal=causal)
+    o, lse = _cross(q, k, v, causal)
+    _cmp(o, lse, O, L, "fp16", f"fp16 {shape} causal={causal}")
+
+
+def test_fp16_large_logits():
+    # Q, K ~ N(0, 4^2): logits near 100 (the stress workload's distribution) in fp16 inputs.
+    q, k, v = make("ragged", seed=0, B=1, H=2, N=700, dtype="fp16")
+    for causal in (False, True):
+        _say(f"fp16 ragged-shaped sigma=4 causal={causal}")
+        O, L = attention_fp64(q, k, v, causal=causal)
+        o, lse = _cross(q, k, v, causal)
+        _cmp(o, lse, O, L, "fp16", f"fp16 sigma=4 causal={causal}")
+
+
+# ------------------------------------------------------- head dimensions 32 and 96, bf16 / fp32
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", [(1, 1, 1, 32), (2, 2, 190, 32), (1, 3, 333, 96),
+                                   (2, 1, 64, 96), (1, 1, 1031, 96)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_head_dims_32_and_96(shape, causal, dtype):
+    B, H, N, d = shape
+    if dtype == "fp32" and N > 400:
+        pytest.skip("the fp32 mode is for small problems")
+    _say(f"{dtype} B={B} H={H} N={N} d={d} causal={causal}")
+    q, k, v = make_random(B, H, N, d, seed=5 * N + d + causal, dtype=dtype)
+    O, L = attention_fp64(q, k, v, causal=causal)
+    qd, kd, vd = (t.cuda() for t in (q, k, v))
+    o, lse = attention(qd, kd, vd, causal=causal)
+    torch.cuda.synchronize()
+    _cmp(o, lse, O, L, dtype, f"{dtype} {shape} causal={causal}")
+
+
+# ------------------------------------------------------------- query and key lengths differ
+
+CROSS = [
+    # (B, H, Nq, Nk, d): decoding (one query), short query blocks over long keys, ragged both
+    # ways, more queries than keys (the first Nq - Nk rows see nothing under the causal mask),
+    # one key, no key at all
+    (2, 3, 1, 4097, 128), (1, 2, 7, 300, 64), (1, 2, 128, 1000, 128), (2, 1, 129, 64, 64),
+    (1, 2, 300, 100, 128), (1, 1, 1000, 1, 64), (1, 2, 200, 0, 64), (1, 1, 65, 65, 96),
+    (1, 2, 50, 700, 32), (1, 2, 40, 300, 256), (1, 1, 1, 1, 64),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("case", CROSS, ids=lambda c: "x".join(map(str, c)))
+def test_cross_lengths(case, causal, dtype):
+    B, H, Nq, Nk, d = case
+    if dtype == "fp32" and Nq * Nk > 200_000:
+        pytest.skip("the fp32 mode is for small problems")
+    _say(f"{dtype} B={B} H={H} Nq={Nq} Nk={Nk} d={d} causal={causal}")
+    q, k, v = make_random(B, H, Nq, d, seed=Nq * 13 + Nk + causal, dtype=dtype, Nk=Nk)
+    O, L = attention_fp64(q, k, v, causal=causal)
+    o, lse = _cross(q, k, v, causal)
+    _cmp(o, lse, O, L, dtype, f"{dtype} {case} causal={causal}")
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.25])
+def test_cross_zero_and_negative_scale(scale):
+    q, k, v = make_random(1, 2, 70, 64, seed=77, dtype="fp16", Nk=333)
+    O, L = attention_fp64(q, k, v, causal=True, scale=scale)
+    o, lse = _cross(q, k, v, True, scale=scale)
+    _cmp(o, lse, O, L, "fp16", f"scale={scale}")
+
+
+def test_attention_picks_the_cross_entry_point_and_repeats_bitwise():
+    q, k, v = make_random(2, 2, 96, 128, seed=5, dtype="bf16", Nk=1500)
+    qd, kd, vd = (t.cuda() for t in (q, k, v))
+    o1, l1 = attention(qd, kd, vd, causal=True)
+    o2, l2 = attention(qd, kd, vd, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    O, L = attention_fp64(q, k, v, causal=True)
+    _cmp(o1, l1, O, L, "bf16", "attention() with Nq != Nk")
+
+
+# ---------------------------------------------------- split-KV with fp16 and differing lengths
+
+SPLIT_CASES = [
+    # (B, H, Nq, Nk, d, num_splits): decoding with the pages' rule, several splits over a
+    # causal prefix, more queries than keys (empty splits and rows), no keys
+    (2, 4, 1, 8192, 128, 0), (1, 2, 16, 3000, 64, 7), (1, 2, 300, 100, 128, 3),
+    (1, 1, 5, 0, 64, 2), (1, 3, 1, 513, 96, 5), (2, 2, 33, 1000, 32, 0), (1, 1, 1, 64, 256, 4),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_splitkv_variants(case, causal, dtype):
+    B, H, Nq, Nk, d, s = case
+    _say(f"split {dtype} B={B} H={H} Nq={Nq} Nk={Nk} d={d} splits={s} causal={causal}")
+    q, k, v = make_random(B, H, Nq, d, seed=Nq + 3 * Nk + s + causal, dtype=dtype, Nk=Nk)
+    O, L = attention_fp64(q, k, v, causal=causal)
+    o, lse = _split(q, k, v, causal, s)
+    _cmp(o, lse, O, L, dtype, f"split {dtype} {case} causal={causal}")
+
+
+# ----------------------------------------------------------------- full size, sampled rows
+
+def test_fp16_training_shape_sampled():
+    # The training-shaped workload (16 x 16 x 2048 x 128, causal) in fp16, in the launch
+    # configuration of the bf16 benchmark; rows sampled around block edges and at random.
+    q, k, v = make("train", seed=0, dtype="fp16")
+    _say("fp16 train workload, sampled rows")
+    qd, kd, vd = (t.cuda() for t in (q, k, v))
+    o, lse = attention(qd, kd, vd, causal=True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(3)
+    rows = sorted(set([0, 1, 127, 128, 129, 1023, 1024, 2046, 2047] +
+                      list(rng.integers(0, 2048, 24))))
+    for b, h in [(0, 0), (7, 9), (15, 15)]:
+        O, L = attention_rows_fp64(q, k, v, b, h, rows, causal=True, scale=128 ** -0.5)
+        _cmp(o[b, h, rows], lse[b, h, rows], O, L, "fp16", f"fp16 train (b={b}, h={h})")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_decode_shape_full(dtype):
+    # Decoding: 4 x 32 heads, one query over 32768 cached keys, through the split-KV path with
+    # the pages' rule and through the plain path; every row checked.
+    B, H, Nq, Nk, d = 4, 32, 1, 32768, 128
+    q, k, v = make_random(B, H, Nq, d, seed=2024, dtype=dtype, Nk=Nk)
+    _say(f"decode {dtype} {B}x{H} one query over {Nk} keys")
+    O, L = attention_fp64(q, k, v, causal=True)
+    o, lse = _split(q, k, v, True, 0)
+    _cmp(o, lse, O, L, dtype, f"decode split {dtype}")
+    o2, lse2 = _cross(q, k, v, True)
+    _cmp(o2, lse2, O, L, dtype, f"decode plain {dtype}")
