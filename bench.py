@@ -70,6 +70,11 @@ def parse_args(argv=None):
                    help="key/value length (default: the query length)")
     p.add_argument("--backward", action="store_true",
                    help="time the backward pass (fa2_bwd) instead; flops = 2.5 x the forward's")
+    p.add_argument("--ring", type=int, default=None, metavar="G",
+                   help="time one GPU's share of attention with the key/value sequence in G shards "
+                        "(the last query shard: G fa2_fwd_partial calls and one fa2_merge)")
+    p.add_argument("--ring-streams", type=int, default=1, metavar="K",
+                   help="with --ring: spread the partial-result launches over K streams")
     p.add_argument("--splits", type=int, default=None, metavar="S",
                    help="time the split-KV path (fa2_fwd_splitkv) with S splits; 0 = the pages' rule")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -182,8 +187,8 @@ def main(argv=None) -> int:
     import torch
 
     from exact_attention_62_amd import (fa2_bwd, fa2_bwd_workspace_size, fa2_fwd, fa2_fwd_cross,
-                                        fa2_fwd_splitkv, fa2_num_splits,
-                                        fa2_splitkv_workspace_size, load_library)
+                                        fa2_fwd_partial, fa2_fwd_splitkv, fa2_merge,
+                                        fa2_num_splits, fa2_splitkv_workspace_size, load_library)
     from exact_attention_62_amd.inputs import WORKLOADS, make, make_upstream
 
     if not torch.cuda.is_available():
@@ -225,6 +230,41 @@ def main(argv=None) -> int:
 
         def step():
             fa2_bwd(q, k, v, o, do, lse, dq, dk, dv, bws, causal=causal, scale=scale)
+    elif args.ring is not None:
+        G = args.ring
+        if dtype == "fp32" or Nq != Nk or Nq % G:
+            print("--ring needs a 16-bit type and equal lengths divisible by G", file=sys.stderr)
+            return 1
+        S = Nq // G
+        r = G - 1  # the last query shard: the heaviest share under the causal mask
+        qs = q[:, :, r * S:].contiguous()
+        shards = [(k[:, :, s * S:(s + 1) * S].contiguous(), v[:, :, s * S:(s + 1) * S].contiguous())
+                  for s in range(G if not causal else r + 1)]
+        o_parts = torch.empty((len(shards),) + tuple(qs.shape), dtype=torch.float32, device=dev)
+        l_parts = torch.empty((len(shards),) + tuple(qs.shape[:3]), dtype=torch.float32, device=dev)
+        o = torch.empty_like(qs)
+        lse = torch.empty(qs.shape[:3], dtype=torch.float32, device=dev)
+        flops = sum(metric_flops(B, H, S, S, d, causal and s == r) for s in range(len(shards)))
+        alg_bytes = float(B * H * (2 * S * d + 2 * S * d * len(shards)) * esize + B * H * S * 4)
+
+        # Partials of different shards are independent: with K streams they run side by side
+        # (default stream priority), and the merge waits for all of them.
+        side = [torch.cuda.Stream(device=dev) for _ in range(max(0, args.ring_streams - 1))]
+
+        def step():
+            start = torch.cuda.Event()
+            start.record(stream)
+            for st in side:
+                st.wait_event(start)
+            for s, (ks, vs) in enumerate(shards):
+                st = ([stream] + side)[s % (len(side) + 1)]
+                fa2_fwd_partial(qs, ks, vs, o_parts[s], l_parts[s], causal=causal and s == r,
+                                scale=scale, stream=st)
+            for st in side:
+                done = torch.cuda.Event()
+                done.record(st)
+                stream.wait_event(done)
+            fa2_merge(o_parts, l_parts, o, lse, stream=stream)
     elif args.splits is not None:
         if dtype == "fp32":
             print("the split-KV path is for bf16 and fp16", file=sys.stderr)
@@ -274,6 +314,9 @@ def main(argv=None) -> int:
     if splits is not None:
         kname += (f" + fa2_combine_kernel<{KERNEL_TYPE[dtype]}, {d}> (both per step; kernel_ms "
                   f"covers the two)")
+    if args.ring is not None:
+        kname = (f"{G} x fa2_fwd_kernel<{KERNEL_TYPE[dtype]}, {d}, *, true> + "
+                 f"fa2_combine_kernel<{KERNEL_TYPE[dtype]}, {d}> (all per step; kernel_ms covers them)")
     if args.backward:
         kname = (f"fa2_bwd_prep_kernel<{d}> + fa2_bwd_dkdv_kernel<{d}, {c}> + "
                  f"fa2_bwd_dq_kernel<{d}, {c}> (all per step; kernel_ms covers the three)")
@@ -306,11 +349,14 @@ def main(argv=None) -> int:
                    "causal": causal, "scale": scale, "kBlockM": 128,
                    "flops_per_step": flops,
                    **({"path": "split-KV", "num_splits": splits} if splits is not None else {}),
+                   **({"path": f"one GPU's share of {args.ring} key/value shards (the last query "
+                               f"shard)", "shard_len": Nq // args.ring,
+                       "streams": args.ring_streams} if args.ring else {}),
                    **({"path": "backward"} if args.backward else {})},
         "pct_of_peak": round(100.0 * tflops / peak, 2),
         "roofline": roofline,
     }
-    if args.cpu_seconds > 0 and not args.backward:
+    if args.cpu_seconds > 0 and not args.backward and not args.ring:
         out["cpu_baseline"] = cpu_baseline(w, q_cpu, k_cpu, v_cpu, causal, scale, args.cpu_seconds)
     print(json.dumps(out), flush=True)
     return 0

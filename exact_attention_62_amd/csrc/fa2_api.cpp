@@ -146,7 +146,7 @@ namespace {
 fa2_status_t prepare(const void* Q, const void* K, const void* V, void* O, float* L, int64_t B,
                      int64_t H, int64_t Nq, int64_t Nk, int64_t d, int causal, float scale,
                      fa2_dtype_t dtype, void* stream, const void* ws, int64_t ws_bytes,
-                     fa2::FwdArgs* a) {
+                     fa2::FwdArgs* a, int64_t o_elem_size = 0) {
   int64_t bm = 0;
   fa2_status_t s = check_shape(B, H, Nq, Nk, d, dtype, &bm);
   if (s != FA2_OK) return s;
@@ -157,9 +157,10 @@ fa2_status_t prepare(const void* Q, const void* K, const void* V, void* O, float
 
   const int64_t q_bytes = B * H * Nq * d * elem_size(dtype);
   const int64_t k_bytes = B * H * Nk * d * elem_size(dtype);
+  const int64_t o_bytes = B * H * Nq * d * (o_elem_size ? o_elem_size : elem_size(dtype));
   const int64_t l_bytes = B * H * Nq * 4;
   const void* ptrs[6] = {Q, K, V, O, L, ws};
-  const int64_t sizes[6] = {q_bytes, k_bytes, k_bytes, q_bytes, l_bytes, ws_bytes};
+  const int64_t sizes[6] = {q_bytes, k_bytes, k_bytes, o_bytes, l_bytes, ws_bytes};
   const char* names[6] = {"Q", "K", "V", "O", "L", "workspace"};
   bool used[6] = {true, Nk > 0, Nk > 0, true, true, ws != nullptr};
   for (int i = 0; i < 6; ++i) {
@@ -352,6 +353,98 @@ fa2_status_t fa2_fwd_splitkv(const void* Q, const void* K, const void* V, void* 
   (void)hipGetLastError();
   hipError_t e = launch_fwd(a);
   if (e == hipSuccess && a.Nk > 0) e = fa2::launch_combine(a);
+  if (e == hipSuccess) e = hipGetLastError();
+  if (e != hipSuccess) return fail_hip(e, "kernel launch");
+  return FA2_OK;
+}
+
+fa2_status_t fa2_fwd_partial(const void* Q, const void* K, const void* V, float* O_part,
+                             float* L_part, int64_t B, int64_t H, int64_t Nq, int64_t Nk,
+                             int64_t d, int causal, float scale, fa2_dtype_t dtype, void* stream) {
+  g_last_error[0] = '\0';
+  if (dtype == FA2_FP32)
+    return fail(FA2_ENOTSUP, "partial results are implemented for FA2_BF16 and FA2_FP16 only");
+  fa2::FwdArgs a;
+  fa2_status_t s = prepare(Q, K, V, O_part, L_part, B, H, Nq, Nk, d, causal, scale, dtype, stream,
+                           nullptr, 0, &a, /*o_elem_size=*/4);
+  if (s != FA2_OK || a.BH == 0) return s;
+  (void)hipGetLastError();
+  hipError_t e;
+  if (Nk == 0) {  // no key: O_part = 0, L_part = -inf, written as float32
+    a.elem = fa2::kFP32;
+    e = fa2::launch_fill_no_keys(a);
+  } else {
+    // The split kernel with one split writes exactly the float32 partial result.
+    a.num_splits = 1;
+    a.ws_O = O_part;
+    a.ws_L = L_part;
+    e = launch_fwd(a);
+  }
+  if (e == hipSuccess) e = hipGetLastError();
+  if (e != hipSuccess) return fail_hip(e, "kernel launch");
+  return FA2_OK;
+}
+
+fa2_status_t fa2_merge(const float* O_parts, const float* L_parts, int num_parts, void* O,
+                       float* L, int64_t rows, int64_t d, fa2_dtype_t dtype, void* stream) {
+  g_last_error[0] = '\0';
+  if (dtype != FA2_BF16 && dtype != FA2_FP32 && dtype != FA2_FP16)
+    return fail(FA2_ENOTSUP, "dtype %d is not FA2_BF16 (0), FA2_FP32 (1) or FA2_FP16 (2)",
+                (int)dtype);
+  if (d != 32 && d != 64 && d != 96 && d != 128 && d != 256)
+    return fail(FA2_ENOTSUP, "head dimension d=%lld is not one of 32, 64, 96, 128, 256",
+                (long long)d);
+  if (rows < 0) return fail(FA2_EINVAL, "rows=%lld must be >= 0", (long long)rows);
+  if (num_parts < 1 || num_parts > FA2_MAX_SPLITS)
+    return fail(FA2_EINVAL, "num_parts=%d is not in 1..%d", num_parts, FA2_MAX_SPLITS);
+  if (rows > ((int64_t(1) << 31) - 1) / num_parts)
+    return fail(FA2_EINVAL, "rows=%lld with %d parts exceeds 2^31 - 1 rows", (long long)rows,
+                num_parts);
+  if (rows == 0) return FA2_OK;
+  const int64_t op = int64_t(num_parts) * rows * d * 4, lp = int64_t(num_parts) * rows * 4;
+  const int64_t ob = rows * d * elem_size(dtype), lb = rows * 4;
+  constexpr int n = 4;
+  const void* ptrs[n] = {O_parts, L_parts, O, L};
+  const int64_t sizes[n] = {op, lp, ob, lb};
+  const char* names[n] = {"O_parts", "L_parts", "O", "L"};
+  for (int i = 0; i < n; ++i) {
+    if (ptrs[i] == nullptr) return fail(FA2_EINVAL, "%s is NULL", names[i]);
+    const uintptr_t align = (i == 1 || i == 3) ? 4 : 16;
+    if (reinterpret_cast<uintptr_t>(ptrs[i]) % align != 0)
+      return fail(FA2_EINVAL, "%s=%p is not %d-byte aligned", names[i], ptrs[i], (int)align);
+  }
+  for (int o = 2; o < n; ++o)
+    for (int i = 0; i < n; ++i)
+      if (i != o && overlaps(ptrs[o], sizes[o], ptrs[i], sizes[i]))
+        return fail(FA2_EINVAL, "%s overlaps %s", names[o], names[i]);
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail_hip(e, "hipGetDevice");
+  }
+  for (int i = 0; i < n; ++i) {
+    fa2_status_t s = check_device_range(ptrs[i], sizes[i], names[i]);
+    if (s != FA2_OK) return s;
+  }
+  fa2::FwdArgs a;
+  a.Q = a.K = a.V = nullptr;
+  a.O = O;
+  a.L = L;
+  a.BH = 1;  // the merge sees `rows` independent rows
+  a.Nq = static_cast<int>(rows);
+  a.Nk = 0;
+  a.d = static_cast<int>(d);
+  a.causal = 0;
+  a.scale = 1.f;
+  a.num_m_block = 0;
+  a.elem = static_cast<int>(dtype);
+  a.stream = static_cast<hipStream_t>(stream);
+  a.num_splits = num_parts;
+  a.ws_O = const_cast<float*>(O_parts);
+  a.ws_L = const_cast<float*>(L_parts);
+  (void)hipGetLastError();
+  e = fa2::launch_combine(a);
   if (e == hipSuccess) e = hipGetLastError();
   if (e != hipSuccess) return fail_hip(e, "kernel launch");
   return FA2_OK;

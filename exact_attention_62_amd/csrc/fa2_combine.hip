@@ -12,12 +12,15 @@
 // saw no key in any split (a causal query before the first key, Nq > Nk) has
 // an empty sum: O = 0 and L = -inf.
 //
-// The merge reads num_splits * d fp32 values per row and writes d 16-bit
-// values: it is bound by HBM bandwidth, so it is plain coalesced vector loads.
-// Each thread owns 4 consecutive dimensions of one row (d/4 threads per row).
+// The merge reads num_splits * d fp32 values per row and writes d values
+// (bf16, fp16, or fp32 for fa2_merge): it is bound by HBM bandwidth, so it is
+// plain coalesced vector loads.  Each thread owns 4 consecutive dimensions of
+// one row (d/4 threads per row).
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "fa2_device.h"
 #include "fa2_internal.h"
@@ -32,8 +35,7 @@ constexpr int kThreads = 256;
 template <typename T, int D>
 __global__ void __launch_bounds__(kThreads)
 fa2_combine_kernel(const float* __restrict__ Ow, const float* __restrict__ Lw,
-                   uint16_t* __restrict__ O, float* __restrict__ L, int rows, int num_splits) {
-  typedef typename Vec16<T>::x4 t4_t;
+                   void* __restrict__ O, float* __restrict__ L, int rows, int num_splits) {
   constexpr int TPR = D / 4;               // threads per row
   constexpr int RPB = kThreads / TPR;      // rows per workgroup
   if ((int)threadIdx.x >= RPB * TPR) return;  // d = 96: 240 of the 256 threads have a row
@@ -53,10 +55,15 @@ fa2_combine_kernel(const float* __restrict__ Ow, const float* __restrict__ Lw,
     acc += w * o;
   }
   const float inv = tot > 0.f ? 1.f / tot : 0.f;
-  t4_t out;
+  if constexpr (std::is_same<T, float>::value) {
+    *((f32x4_t*)O + ((size_t)row * D / 4 + t)) = acc * inv;
+  } else {
+    typedef typename Vec16<T>::x4 t4_t;
+    t4_t out;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) out[r] = (T)(acc[r] * inv);
-  *(t4_t*)(O + (size_t)row * D + 4 * t) = out;
+    for (int r = 0; r < 4; ++r) out[r] = (T)(acc[r] * inv);
+    *((t4_t*)O + ((size_t)row * D / 4 + t)) = out;
+  }
   if (t == 0) L[row] = tot > 0.f ? __builtin_fmaf(__builtin_amdgcn_logf(tot), kLn2, lmax) : kNegInf;
 }
 
@@ -66,7 +73,7 @@ hipError_t launch(const FwdArgs& a) {
   const int rows = a.BH * a.Nq;
   const int grid = (rows + RPB - 1) / RPB;
   hipLaunchKernelGGL((fa2_combine_kernel<T, D>), dim3(grid), dim3(kThreads), 0, a.stream, a.ws_O,
-                     a.ws_L, (uint16_t*)a.O, a.L, rows, a.num_splits);
+                     a.ws_L, a.O, a.L, rows, a.num_splits);
   return hipGetLastError();
 }
 
@@ -105,6 +112,7 @@ hipError_t launch_fill_no_keys(const FwdArgs& a) {
 hipError_t launch_combine(const FwdArgs& a) {
   if (a.elem == kBF16) return dispatch<__bf16>(a);
   if (a.elem == kFP16) return dispatch<_Float16>(a);
+  if (a.elem == kFP32) return dispatch<float>(a);
   return hipErrorInvalidValue;
 }
 

@@ -65,7 +65,8 @@ hipError_t cu_count(int* cus);
 hipError_t launch_fwd_bf16(const FwdArgs& a);
 hipError_t launch_fwd_fp16(const FwdArgs& a);
 hipError_t launch_fwd_f32(const FwdArgs& a);
-// Merge num_splits partial results (ws_O, ws_L) into O (a.elem) and L.
+// Merge num_splits partial results (ws_O, ws_L: [num_splits][BH*Nq] rows) into
+// O (a.elem: bf16, fp16 or fp32) and L.
 hipError_t launch_combine(const FwdArgs& a);
 // The result when there are no keys (a.Nk == 0): O = 0 and L = -inf.
 hipError_t launch_fill_no_keys(const FwdArgs& a);

@@ -16,10 +16,11 @@ import threading
 
 import torch
 
-__all__ = ["FA2Error", "FlashAttention", "attention", "attention_backward", "fa2_bwd",
-           "fa2_bwd_workspace_size", "fa2_fwd", "fa2_fwd_cross", "fa2_fwd_splitkv",
-           "fa2_launch_shape", "fa2_num_splits", "fa2_splitkv_workspace_size", "fa2_strerror",
-           "fa2_last_error", "library_path", "load_library"]
+__all__ = ["FA2Error", "FlashAttention", "attention", "attention_backward", "attention_partial",
+           "fa2_bwd", "fa2_bwd_workspace_size", "fa2_fwd", "fa2_fwd_cross", "fa2_fwd_partial",
+           "fa2_fwd_splitkv", "fa2_launch_shape", "fa2_merge", "fa2_num_splits",
+           "fa2_splitkv_workspace_size", "fa2_strerror", "fa2_last_error", "library_path",
+           "load_library", "merge_partials"]
 
 FA2_OK, FA2_EINVAL, FA2_ENOTSUP, FA2_EHIP = 0, -1, -2, -3
 FA2_BF16, FA2_FP32, FA2_FP16 = 0, 1, 2
@@ -75,6 +76,11 @@ def load_library() -> ctypes.CDLL:
         lib.fa2_splitkv_workspace_size.restype = ctypes.c_int
         lib.fa2_num_splits.argtypes = [i64, i64, i64, i64, i64, ctypes.POINTER(ctypes.c_int)]
         lib.fa2_num_splits.restype = ctypes.c_int
+        lib.fa2_fwd_partial.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_int,
+                                        ctypes.c_float, ctypes.c_int, vp]
+        lib.fa2_fwd_partial.restype = ctypes.c_int
+        lib.fa2_merge.argtypes = [vp, vp, ctypes.c_int, vp, vp, i64, i64, ctypes.c_int, vp]
+        lib.fa2_merge.restype = ctypes.c_int
         lib.fa2_bwd.argtypes = [vp] * 9 + [i64, i64, i64, i64, ctypes.c_int, ctypes.c_float,
                                            ctypes.c_int, vp, ctypes.c_size_t, vp]
         lib.fa2_bwd.restype = ctypes.c_int
@@ -116,6 +122,8 @@ def _check_tensors(q, k, v, o, lse):
     B, H, Nq, d = q.shape
     Nk = k.shape[2]
     for name, t, shape in (("k", k, (B, H, Nk, d)), ("v", v, (B, H, Nk, d)), ("o", o, q.shape)):
+        if t is None:  # an output checked by the caller (a float32 partial result)
+            continue
         if tuple(t.shape) != tuple(shape):
             raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
         if t.dtype != q.dtype:
@@ -124,7 +132,7 @@ def _check_tensors(q, k, v, o, lse):
         raise ValueError(f"lse must be float32 [{B}, {H}, {Nq}], got {lse.dtype} {tuple(lse.shape)}")
     if q.dtype not in _DTYPES:
         raise ValueError(f"unsupported dtype {q.dtype}")
-    tensors = (q, k, v, o, lse)
+    tensors = tuple(t for t in (q, k, v, o, lse) if t is not None)
     for t in tensors:
         if not t.is_cuda:
             raise ValueError("every tensor must be on the GPU")
@@ -252,6 +260,75 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = 
     ws = torch.empty(fa2_splitkv_workspace_size(B, H, Nq, Nk, d, s), dtype=torch.uint8,
                      device=q.device)
     fa2_fwd_splitkv(q, k, v, o, lse, ws, num_splits=s, causal=causal, scale=scale)
+    return o, lse
+
+
+def fa2_fwd_partial(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o_part: torch.Tensor,
+                    l_part: torch.Tensor, causal: bool = False, scale: float | None = None,
+                    stream: torch.cuda.Stream | None = None) -> None:
+    """Enqueue attention of q [B, H, Nq, d] over one key/value shard k, v [B, H, Nk, d]
+    (bfloat16 or float16), kept as a mergeable partial result: o_part float32
+    [B, H, Nq, d] (normalised over this shard) and l_part float32 [B, H, Nq]
+    (the shard's logsumexp, -inf for a row that sees none of its keys)."""
+    if o_part.dtype != torch.float32 or tuple(o_part.shape) != tuple(q.shape):
+        raise ValueError(f"o_part must be float32 {tuple(q.shape)}")
+    B, H, Nq, Nk, d = _check_tensors(q, k, v, None, l_part)
+    if not o_part.is_cuda or not o_part.is_contiguous() or o_part.device != q.device:
+        raise ValueError("o_part must be a contiguous tensor on the inputs' GPU")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    lib = load_library()
+    with torch.cuda.device(q.device):
+        st = lib.fa2_fwd_partial(_ptr(q), _ptr(k), _ptr(v), _ptr(o_part), _ptr(l_part), B, H, Nq,
+                                 Nk, d, 1 if causal else 0, float(scale), _DTYPES[q.dtype],
+                                 ctypes.c_void_p(stream.cuda_stream))
+    _check(st)
+
+
+def fa2_merge(o_parts: torch.Tensor, l_parts: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
+              stream: torch.cuda.Stream | None = None) -> None:
+    """Enqueue the merge of S partial results: o_parts float32 [S, ..., d], l_parts float32
+    [S, ...] -> o [..., d] (bfloat16, float16 or float32) and lse float32 [...]."""
+    S = o_parts.shape[0]
+    if (o_parts.dtype != torch.float32 or l_parts.dtype != torch.float32
+            or lse.dtype != torch.float32):
+        raise ValueError("o_parts, l_parts and lse must be float32")
+    if tuple(o_parts.shape[1:]) != tuple(o.shape) or tuple(l_parts.shape) != (S, *o.shape[:-1]) \
+            or tuple(lse.shape) != tuple(o.shape[:-1]):
+        raise ValueError(f"shapes do not match: o_parts {tuple(o_parts.shape)}, l_parts "
+                         f"{tuple(l_parts.shape)}, o {tuple(o.shape)}, lse {tuple(lse.shape)}")
+    if o.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {o.dtype}")
+    for t in (o_parts, l_parts, o, lse):
+        if not t.is_cuda or not t.is_contiguous() or t.device != o.device:
+            raise ValueError("every tensor must be contiguous and on the same GPU")
+    rows = lse.numel()
+    if stream is None:
+        stream = torch.cuda.current_stream(o.device)
+    with torch.cuda.device(o.device):
+        st = load_library().fa2_merge(_ptr(o_parts), _ptr(l_parts), int(S), _ptr(o), _ptr(lse),
+                                      rows, o.shape[-1], _DTYPES[o.dtype],
+                                      ctypes.c_void_p(stream.cuda_stream))
+    _check(st)
+
+
+def attention_partial(q, k, v, causal: bool = False, scale: float | None = None):
+    """Allocate and return (o_part float32, l_part float32) from fa2_fwd_partial."""
+    o_part = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    l_part = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    fa2_fwd_partial(q, k, v, o_part, l_part, causal=causal, scale=scale)
+    return o_part, l_part
+
+
+def merge_partials(parts, dtype: torch.dtype = torch.bfloat16):
+    """Merge a list of (o_part, l_part) pairs (as attention_partial returns) into (o, lse)."""
+    o_parts = torch.stack([p[0] for p in parts])
+    l_parts = torch.stack([p[1] for p in parts])
+    o = torch.empty(o_parts.shape[1:], dtype=dtype, device=o_parts.device)
+    lse = torch.empty(l_parts.shape[1:], dtype=torch.float32, device=o_parts.device)
+    fa2_merge(o_parts, l_parts, o, lse)
     return o, lse
 
 

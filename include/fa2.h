@@ -169,6 +169,52 @@ fa2_status_t fa2_num_splits(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_
                             int* num_splits);
 
 /*
+ * fa2_fwd_partial - attention of Q over one part of the key/value sequence,
+ * kept as a partial result that fa2_merge can combine with the other parts.
+ *
+ * When the key/value sequence is split, each row of O gets one part from
+ * every split, and the parts must be combined once more to reach the global
+ * softmax result (page "Flash Attention V2原理解读", the thread-block grid
+ * section).  This is the building block of that: with K and V one contiguous
+ * shard of the keys (for example the shard another GPU holds, in a ring of
+ * GPUs over a long sequence), it writes
+ *   O_part[b][h][i][:] = sum_j softmax_j(S[i][:]) V[j][:]   over this shard only,
+ *   L_part[b][h][i]    = ln sum_j exp(S[i][j])              (-inf: no visible key)
+ * in float32, O_part = 0 for a row with no visible key.
+ *
+ *   Q        [B][H][Nq][d]; K, V [B][H][Nk][d] (the shard); dtype FA2_BF16 or
+ *            FA2_FP16 (FA2_FP32: FA2_ENOTSUP); 16-byte aligned device memory.
+ *   O_part   [B][H][Nq][d] float32 output, 16-byte aligned.
+ *   L_part   [B][H][Nq] float32 output, 4-byte aligned.
+ *   causal   as for fa2_fwd_cross (bottom-right: the shard that ends where the
+ *            queries end); 0 for a shard entirely before the queries.
+ *   B, H, Nq, Nk, d, scale, stream: as for fa2_fwd_cross.  Nk == 0 writes
+ *            O_part = 0, L_part = -inf.
+ */
+fa2_status_t fa2_fwd_partial(const void* Q, const void* K, const void* V, float* O_part,
+                             float* L_part, int64_t B, int64_t H, int64_t Nq, int64_t Nk,
+                             int64_t d, int causal, float scale, fa2_dtype_t dtype, void* stream);
+
+/*
+ * fa2_merge - combine num_parts partial results over disjoint key sets into
+ * the attention over all of them (page "Flash Attention V2原理解读", the
+ * thread-block grid section: the extra combine step split keys need):
+ *   L = ln sum_s exp(L_s),   O = sum_s exp(L_s - L) O_s
+ * (a row whose every L_s is -inf: O = 0, L = -inf).
+ *
+ *   O_parts  [num_parts][rows][d] float32, 16-byte aligned (fa2_fwd_partial's
+ *            outputs, one after another).
+ *   L_parts  [num_parts][rows] float32, 4-byte aligned.
+ *   O        [rows][d] output of type dtype (FA2_BF16, FA2_FP16 or FA2_FP32),
+ *            16-byte aligned; L [rows] float32 output.  rows = B*H*Nq for
+ *            the [B][H][Nq] layout.
+ *   num_parts 1..FA2_MAX_SPLITS; d as for fa2_fwd.  rows == 0 does nothing.
+ * The outputs must not overlap the parts.
+ */
+fa2_status_t fa2_merge(const float* O_parts, const float* L_parts, int num_parts, void* O,
+                       float* L, int64_t rows, int64_t d, fa2_dtype_t dtype, void* stream);
+
+/*
  * fa2_launch_shape - the work decomposition fa2_fwd uses, as a host-only query.
  *
  * The work is one independent item per (query block, batch, head), with

@@ -33,9 +33,10 @@ def _declared_functions():
 
 def test_header_declares_the_boundary():
     assert _declared_functions() == ["fa2_bwd", "fa2_bwd_workspace_size", "fa2_fwd",
-                                     "fa2_fwd_cross", "fa2_fwd_splitkv", "fa2_last_error",
-                                     "fa2_launch_shape", "fa2_num_splits",
-                                     "fa2_splitkv_workspace_size", "fa2_strerror"]
+                                     "fa2_fwd_cross", "fa2_fwd_partial", "fa2_fwd_splitkv",
+                                     "fa2_last_error", "fa2_launch_shape", "fa2_merge",
+                                     "fa2_num_splits", "fa2_splitkv_workspace_size",
+                                     "fa2_strerror"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -291,3 +292,58 @@ def test_bwd_empty_problem_is_a_no_op():
 @pytest.mark.skipif(torch.cuda.is_available(), reason="needs a host without a visible GPU")
 def test_bwd_without_a_device_reports_the_hip_error():
     assert _bwd() == F.FA2_EHIP
+
+
+# ---- partial results and their merge -----------------------------------------------------
+def _partial(dtype=F.FA2_BF16, **kw):
+    a = dict(q=FAKE, k=FAKE + 0x100000, v=FAKE + 0x200000, o=FAKE + 0x300000, L=FAKE + 0x400000,
+             B=1, H=1, Nq=16, Nk=64, d=64, causal=0, scale=0.125)
+    a.update(kw)
+    return F.load_library().fa2_fwd_partial(a["q"], a["k"], a["v"], a["o"], a["L"], a["B"], a["H"],
+                                            a["Nq"], a["Nk"], a["d"], a["causal"], a["scale"],
+                                            dtype, None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(dtype=F.FA2_FP32), F.FA2_ENOTSUP, "FA2_BF16 and FA2_FP16 only"),
+    (dict(o=None), F.FA2_EINVAL, "O is NULL"),
+    # O_part is float32: 16 rows x 64 dims x 4 bytes = 4 KB, so L placed 2 KB in overlaps it
+    (dict(L=FAKE + 0x300000 + 2048), F.FA2_EINVAL, "O overlaps L"),
+    (dict(Nk=-1), F.FA2_EINVAL, "sizes must be >= 0"),
+    (dict(d=40), F.FA2_ENOTSUP, "d=40"),
+])
+def test_partial_invalid_arguments_before_any_hip_call(kw, status, needle):
+    assert _partial(**kw) == status
+    assert needle in F.fa2_last_error()
+
+
+def _merge(dtype=F.FA2_BF16, **kw):
+    a = dict(op=FAKE, lp=FAKE + 0x400000, o=FAKE + 0x500000, L=FAKE + 0x600000, S=3, rows=64, d=64)
+    a.update(kw)
+    return F.load_library().fa2_merge(a["op"], a["lp"], a["S"], a["o"], a["L"], a["rows"], a["d"],
+                                      dtype, None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(S=0), F.FA2_EINVAL, "num_parts=0"),
+    (dict(S=129), F.FA2_EINVAL, "num_parts=129"),
+    (dict(rows=-1), F.FA2_EINVAL, "rows=-1"),
+    (dict(d=100), F.FA2_ENOTSUP, "d=100"),
+    (dict(dtype=9), F.FA2_ENOTSUP, "dtype 9"),
+    (dict(op=None), F.FA2_EINVAL, "O_parts is NULL"),
+    (dict(lp=FAKE + 0x400002), F.FA2_EINVAL, "4-byte aligned"),
+    (dict(o=FAKE + 0x100), F.FA2_EINVAL, "O overlaps O_parts"),
+])
+def test_merge_invalid_arguments_before_any_hip_call(kw, status, needle):
+    assert _merge(**kw) == status
+    assert needle in F.fa2_last_error()
+
+
+def test_merge_of_no_rows_is_a_no_op():
+    assert _merge(op=None, lp=None, o=None, L=None, rows=0) == F.FA2_OK
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="needs a host without a visible GPU")
+def test_partial_and_merge_without_a_device_report_the_hip_error():
+    assert _partial() == F.FA2_EHIP
+    assert _merge() == F.FA2_EHIP
