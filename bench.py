@@ -219,12 +219,15 @@ def main(argv=None) -> int:
     alg_bytes = float(B * H * (2 * Nq * d + 2 * Nk * d) * esize + B * H * Nq * 4)
     splits = None
     if args.backward:
-        if dtype != "bf16" or d not in (64, 128) or Nq != Nk:
-            print("the backward pass is bf16 with d = 64 or 128 and equal lengths", file=sys.stderr)
+        if dtype == "fp32" or d not in (64, 128):
+            print("the backward pass is bf16 or fp16 with d = 64 or 128", file=sys.stderr)
             return 1
-        fa2_fwd(q, k, v, o, lse, causal=causal, scale=scale)
-        do = make_upstream(B, H, Nq, d, args.seed).to(dev)
-        dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+        if Nq == Nk:
+            fa2_fwd(q, k, v, o, lse, causal=causal, scale=scale)
+        else:
+            fa2_fwd_cross(q, k, v, o, lse, causal=causal, scale=scale)
+        do = make_upstream(B, H, Nq, d, args.seed, dtype=dtype).to(dev)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
         bws = torch.empty(fa2_bwd_workspace_size(B, H, Nq, d), dtype=torch.uint8, device=dev)
         flops = 2.5 * flops  # five products to the forward's two
 
@@ -318,8 +321,9 @@ def main(argv=None) -> int:
         kname = (f"{G} x fa2_fwd_kernel<{KERNEL_TYPE[dtype]}, {d}, *, true> + "
                  f"fa2_combine_kernel<{KERNEL_TYPE[dtype]}, {d}> (all per step; kernel_ms covers them)")
     if args.backward:
-        kname = (f"fa2_bwd_prep_kernel<{d}> + fa2_bwd_dkdv_kernel<{d}, {c}> + "
-                 f"fa2_bwd_dq_kernel<{d}, {c}> (all per step; kernel_ms covers the three)")
+        T = KERNEL_TYPE[dtype]
+        kname = (f"fa2_bwd_prep_kernel<{T}, {d}> + fa2_bwd_dkdv_kernel<{T}, {d}, {c}> + "
+                 f"fa2_bwd_dq_kernel<{T}, {d}, {c}> (all per step; kernel_ms covers the three)")
     if hbm_bound:
         gbs = alg_bytes / (kernel_ms * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",

@@ -462,29 +462,37 @@ fa2_status_t fa2_bwd_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d, 
   return FA2_OK;
 }
 
-fa2_status_t fa2_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
-                     const float* L, void* dQ, void* dK, void* dV, int64_t B, int64_t H,
-                     int64_t N, int64_t d, int causal, float scale, fa2_dtype_t dtype,
-                     void* workspace, size_t workspace_bytes, void* stream) {
-  g_last_error[0] = '\0';
-  if (dtype != FA2_BF16)
-    return fail(FA2_ENOTSUP, "the backward pass is implemented for FA2_BF16 only (dtype %d)",
+}  // extern "C"
+
+namespace {
+
+// Shared by fa2_bwd and fa2_bwd_cross: argument checks (none of which needs a
+// HIP call), pointer and device checks, then the three kernels.  Arrays of
+// zero size (no queries, or no keys) may be NULL and are not checked.
+fa2_status_t bwd_common(const void* Q, const void* K, const void* V, const void* O,
+                        const void* dO, const float* L, void* dQ, void* dK, void* dV, int64_t B,
+                        int64_t H, int64_t Nq, int64_t Nk, int64_t d, int causal, float scale,
+                        fa2_dtype_t dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (dtype != FA2_BF16 && dtype != FA2_FP16)
+    return fail(FA2_ENOTSUP,
+                "the backward pass is implemented for FA2_BF16 and FA2_FP16 only (dtype %d)",
                 (int)dtype);
   int64_t bm = 0;
-  fa2_status_t s = check_shape(B, H, N, N, d, dtype, &bm);
+  fa2_status_t s = check_shape(B, H, Nq, Nk, d, dtype, &bm);
   if (s != FA2_OK) return s;
   if (d != 64 && d != 128)
     return fail(FA2_ENOTSUP, "the backward pass supports d = 64 and 128 (d=%lld)", (long long)d);
   if (causal != 0 && causal != 1) return fail(FA2_EINVAL, "causal=%d must be 0 or 1", causal);
   if (!std::isfinite(scale)) return fail(FA2_EINVAL, "scale must be finite");
-  if (B * H * N == 0) return FA2_OK;
+  if (B * H * (Nq + Nk) == 0) return FA2_OK;  // no element of dQ, dK or dV
 
-  const int64_t tb = B * H * N * d * 2, lb = B * H * N * 4;
+  const int64_t qb = B * H * Nq * d * 2, kb = B * H * Nk * d * 2, lb = B * H * Nq * 4;
   constexpr int n = 10;
   const void* ptrs[n] = {Q, K, V, O, dO, L, dQ, dK, dV, workspace};
-  const int64_t sizes[n] = {tb, tb, tb, tb, tb, lb, tb, tb, tb, lb};
+  const int64_t sizes[n] = {qb, kb, kb, qb, qb, lb, qb, kb, kb, lb};
   const char* names[n] = {"Q", "K", "V", "O", "dO", "L", "dQ", "dK", "dV", "workspace"};
   for (int i = 0; i < n; ++i) {
+    if (sizes[i] == 0) continue;
     if (ptrs[i] == nullptr) return fail(FA2_EINVAL, "%s is NULL", names[i]);
     const uintptr_t align = (i == 5 || i == 9) ? 4 : 16;
     if (reinterpret_cast<uintptr_t>(ptrs[i]) % align != 0)
@@ -495,7 +503,8 @@ fa2_status_t fa2_bwd(const void* Q, const void* K, const void* V, const void* O,
                 (unsigned long long)workspace_bytes, (long long)lb);
   for (int o = 6; o < n; ++o)  // outputs and workspace: disjoint from everything else
     for (int i = 0; i < n; ++i)
-      if (i != o && overlaps(ptrs[o], sizes[o], ptrs[i], sizes[i]))
+      if (i != o && sizes[o] > 0 && sizes[i] > 0 &&
+          overlaps(ptrs[o], sizes[o], ptrs[i], sizes[i]))
         return fail(FA2_EINVAL, "%s overlaps %s", names[o], names[i]);
 
   int dev = -1;
@@ -505,6 +514,7 @@ fa2_status_t fa2_bwd(const void* Q, const void* K, const void* V, const void* O,
     return fail_hip(e, "hipGetDevice");
   }
   for (int i = 0; i < n; ++i) {
+    if (sizes[i] == 0) continue;
     s = check_device_range(ptrs[i], sizes[i], names[i]);
     if (s != FA2_OK) return s;
   }
@@ -520,16 +530,41 @@ fa2_status_t fa2_bwd(const void* Q, const void* K, const void* V, const void* O,
   a.dV = dV;
   a.Dvec = static_cast<float*>(workspace);
   a.BH = static_cast<int>(B * H);
-  a.N = static_cast<int>(N);
+  a.Nq = static_cast<int>(Nq);
+  a.Nk = static_cast<int>(Nk);
   a.d = static_cast<int>(d);
   a.causal = causal;
   a.scale = scale;
+  a.elem = static_cast<int>(dtype);
   a.stream = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  e = fa2::launch_bwd_bf16(a);
+  e = fa2::launch_bwd(a);
   if (e == hipSuccess) e = hipGetLastError();
   if (e != hipSuccess) return fail_hip(e, "kernel launch");
   return FA2_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fa2_status_t fa2_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                     const float* L, void* dQ, void* dK, void* dV, int64_t B, int64_t H,
+                     int64_t N, int64_t d, int causal, float scale, fa2_dtype_t dtype,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error[0] = '\0';
+  return bwd_common(Q, K, V, O, dO, L, dQ, dK, dV, B, H, N, N, d, causal, scale, dtype, workspace,
+                    workspace_bytes, stream);
+}
+
+fa2_status_t fa2_bwd_cross(const void* Q, const void* K, const void* V, const void* O,
+                           const void* dO, const float* L, void* dQ, void* dK, void* dV,
+                           int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int causal,
+                           float scale, fa2_dtype_t dtype, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  g_last_error[0] = '\0';
+  return bwd_common(Q, K, V, O, dO, L, dQ, dK, dV, B, H, Nq, Nk, d, causal, scale, dtype,
+                    workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -1,4 +1,5 @@
-// FlashAttention-2 backward pass, bf16 in / bf16 out, for gfx950 (MI355X).
+// FlashAttention-2 backward pass, bf16 or fp16 in / the same type out, fp32
+// accumulation, for gfx950 (MI355X).
 //
 // The pages fix the structure (page "FlashAttention学习笔记(2)", sections on the
 // forward and on the forward/backward thread-block split; page "Flash Attention
@@ -10,6 +11,11 @@
 // chain rule of softmax attention:
 //   P = exp(scale * Q K^T - L),  dV = P^T dO,  dP = dO V^T,
 //   D = rowsum(dO * O),  dS = P * (dP - D),  dQ = scale * dS K,  dK = scale * dS^T Q.
+//
+// Q, O, dO, L and dQ have Nq rows, K, V, dK and dV Nk; the causal mask is
+// aligned bottom-right as in the forward pass (key j visible to query i when
+// j <= i + Nk - Nq), and a query that sees no key (L = -inf) contributes
+// nothing (its P is masked to 0).
 //
 // Three kernels:
 //   fa2_bwd_prep     D per row (bandwidth-bound).
@@ -24,7 +30,7 @@
 //                    and dP once more instead of accumulating dQ with atomics
 //                    across workgroups, so the result is deterministic.
 //
-// Every product is a 32x32x16 bf16 MFMA with fp32 accumulation.  As in the
+// Every product is a 32x32x16 bf16 or fp16 MFMA with fp32 accumulation.  As in the
 // forward pass, accumulators are kept transposed where that puts one output
 // row in one lane: lane l of a 32x32 tile holds column l % 32 and rows
 // 8*(r/4) + 4*(l/32) + r%4.  Tiles staged in LDS use one layout (128-byte
@@ -48,13 +54,13 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kRows = 32 * kWaves;  // keys (dK/dV) or queries (dQ) per workgroup
 constexpr int kStep = 64;           // queries (dK/dV) or keys (dQ) per inner step
 
-// Byte offset of element (row r, dim c) of a staged [rows][D] bf16 tile.
+// Byte offset of element (row r, dim c) of a staged [rows][D] 16-bit tile.
 template <int D>
 __device__ __forceinline__ constexpr int toff(int r, int c) {
   return (r >> 2) * (8 * D) + (c >> 4) * 128 + 32 * (r & 3) + 2 * (c & 15);
 }
 
-// Stage rows [r0, r0 + ROWS) of a [N][D] bf16 slice into LDS in the tile layout
+// Stage rows [r0, r0 + ROWS) of a [N][D] 16-bit slice into LDS in the tile layout
 // (rows past N are clamped to row N - 1; callers mask them).  Load i of this
 // thread fills 1 KB chunk n = wave*LOADS + i: its lane L writes 16 bytes, row
 // 4*(bk / NSEG) + (L%8)/2 and dims 16*(bk % NSEG) + 8*(L%2) of 128-byte block
@@ -95,9 +101,10 @@ template <int D>
 __device__ __forceinline__ uint32_t row_base(int lane) {
   return (uint32_t)(((lane & 31) >> 2) * (8 * D) + 32 * (lane & 3) + 16 * (lane >> 5));
 }
-template <int D>
-__device__ __forceinline__ bf16x8_t row_frag(const char* tile, uint32_t rbase, int row0, int ks) {
-  return *(const bf16x8_t*)(tile + rbase + (row0 / 4) * (8 * D) + 128 * ks);
+template <typename T, int D>
+__device__ __forceinline__ typename Vec16<T>::x8 row_frag(const char* tile, uint32_t rbase, int row0,
+                                                          int ks) {
+  return *(const typename Vec16<T>::x8*)(tile + rbase + (row0 / 4) * (8 * D) + 128 * ks);
 }
 // Transposed fragment: the A operand (dims x rows) for rows 16u .. 16u+15 of
 // the tile and dims 32t .. 32t+31, in the permuted row order that matches a B
@@ -113,32 +120,34 @@ template <int D>
 __device__ __forceinline__ uint32_t tr_base(int lane) {
   return (uint32_t)((lane >> 5) * (8 * D) + 128 * ((lane >> 4) & 1) + 8 * (lane & 15));
 }
-template <int D>
-__device__ __forceinline__ bf16x8_t tr_frag(const char* tile, uint32_t tbase, int u, int t) {
+template <typename T, int D>
+__device__ __forceinline__ typename Vec16<T>::x8 tr_frag(const char* tile, uint32_t tbase, int u,
+                                                         int t) {
   const char* p = tile + tbase + 32 * D * u + 256 * t;
   const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr_t)p);
   const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr_t)(p + 16 * D));
-  return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  return __builtin_bit_cast(typename Vec16<T>::x8,
+                            __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 static_assert(toff<128>(5, 40) == 1 * 1024 + 2 * 128 + 32 * 1 + 2 * 8, "tile layout");
 
-// B operand fragments of a [N][D] bf16 slice held in registers: for k-step ks,
+// B operand fragments of a [N][D] 16-bit slice held in registers: for k-step ks,
 // lane l holds row r0 + l%32, dims 16*ks + 8*(l/32) .. +8 (zero past N).
-template <int D>
-__device__ __forceinline__ void load_frags(bf16x8_t (&f)[D / 16], const uint16_t* head, int row,
-                                           int N, int half) {
+template <typename T, int D>
+__device__ __forceinline__ void load_frags(typename Vec16<T>::x8 (&f)[D / 16], const uint16_t* head,
+                                           int row, int N, int half) {
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
     u32x4_t t = {0u, 0u, 0u, 0u};
     if (row < N) t = *(const u32x4_t*)(head + (size_t)row * D + 16 * ks + 8 * half);
-    f[ks] = __builtin_bit_cast(bf16x8_t, t);
+    f[ks] = __builtin_bit_cast(typename Vec16<T>::x8, t);
   }
 }
 
 // Store a transposed accumulator (DT tiles of 32 dims x 32 rows; lane = row)
-// times `mul` as bf16 rows [row0, row0+32) of a [N][D] slice, through a buffer
-// resource bounded to rows < N.
-template <int D>
+// times `mul` as rows [row0, row0+32) of a [N][D] slice of type T, through a
+// buffer resource bounded to rows < N.
+template <typename T, int D>
 __device__ __forceinline__ void store_rows(const f32x16_t (&acc)[D / 32], float mul,
                                            uint16_t* head, int row0, int N, int lane) {
   // 0 rows for a wavefront past the end: no store lands.  Both values are
@@ -155,26 +164,27 @@ __device__ __forceinline__ void store_rows(const f32x16_t (&acc)[D / 32], float 
   for (int t = 0; t < D / 32; ++t)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      bf16x4_t w;
+      typename Vec16<T>::x4 w;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) w[r] = (__bf16)(acc[t][g * 4 + r] * mul);
+      for (int r = 0; r < 4; ++r) w[r] = (T)(acc[t][g * 4 + r] * mul);
       __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, w), rs,
                                             (col * D + t * 32 + 8 * g + 4 * half) * 2, 0, 0);
     }
 }
 
 // ---------------------------------------------------------------- D = rowsum(dO * O)
-template <int D>
+template <typename T, int D>
 __global__ void __launch_bounds__(kThreads)
 fa2_bwd_prep_kernel(const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO,
                     float* __restrict__ Dv, int rows) {
+  typedef typename Vec16<T>::x8 t8_t;
   constexpr int TPR = D / 8;  // threads per row, 8 dims each
   const int row = blockIdx.x * (kThreads / TPR) + threadIdx.x / TPR;
   const int t = threadIdx.x % TPR;
   float acc = 0.f;
   if (row < rows) {
-    const bf16x8_t o = *(const bf16x8_t*)(O + (size_t)row * D + 8 * t);
-    const bf16x8_t g = *(const bf16x8_t*)(dO + (size_t)row * D + 8 * t);
+    const t8_t o = *(const t8_t*)(O + (size_t)row * D + 8 * t);
+    const t8_t g = *(const t8_t*)(dO + (size_t)row * D + 8 * t);
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc += (float)o[i] * (float)g[i];
   }
@@ -189,13 +199,14 @@ fa2_bwd_prep_kernel(const uint16_t* __restrict__ O, const uint16_t* __restrict__
 // tile) within 256 so that two wavefronts share each SIMD.
 constexpr int kQStep = 32;
 
-template <int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL>
 __global__ void __launch_bounds__(kThreads, 2)
 fa2_bwd_dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
                     const uint16_t* __restrict__ Vg, const uint16_t* __restrict__ dOg,
                     const float* __restrict__ Lg, const float* __restrict__ Dg,
-                    uint16_t* __restrict__ dKg, uint16_t* __restrict__ dVg, int N,
+                    uint16_t* __restrict__ dKg, uint16_t* __restrict__ dVg, int Nq, int Nk,
                     int num_k_block, float c, float scale) {
+  typedef typename Vec16<T>::x8 t8_t;
   constexpr int KS = D / 16, DT = D / 32;
   constexpr int TILE = kQStep * D * 2;  // bytes of one staged [32][D] tile
   // Q, dO tiles, then 64 L and 64 D values (32 used), for two steps.
@@ -207,29 +218,31 @@ fa2_bwd_dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict_
   // With the causal mask the first key blocks are the heaviest; they go out first.
   const int kb = (int)blockIdx.x % num_k_block;
   const int bh = blockIdx.x / num_k_block;
-  const size_t slice = (size_t)bh * N * D;
-  const uint16_t *Qh = Qg + slice, *dOh = dOg + slice;
-  const float *Lh = Lg + (size_t)bh * N, *Dh = Dg + (size_t)bh * N;
+  const size_t qslice = (size_t)bh * Nq * D, kslice = (size_t)bh * Nk * D;
+  const uint16_t *Qh = Qg + qslice, *dOh = dOg + qslice;
+  const float *Lh = Lg + (size_t)bh * Nq, *Dh = Dg + (size_t)bh * Nq;
+  const int off = Nk - Nq;                // key j visible to query i when j <= i + off
   const int k0 = kb * kRows + 32 * wave;  // this wavefront's first key
   const uint32_t rbase = row_base<D>(lane), tbase = tr_base<D>(lane);
 
-  bf16x8_t kf[KS], vf[KS];
-  load_frags<D>(kf, Kg + slice, k0 + col, N, half);
-  load_frags<D>(vf, Vg + slice, k0 + col, N, half);
+  t8_t kf[KS], vf[KS];
+  load_frags<T, D>(kf, Kg + kslice, k0 + col, Nk, half);
+  load_frags<T, D>(vf, Vg + kslice, k0 + col, Nk, half);
   f32x16_t dk[DT], dv[DT];
 #pragma unroll
   for (int t = 0; t < DT; ++t) dk[t] = dv[t] = f32x16_t{};
 
   // Query steps: from the first that can see the block's keys to the end.
-  const int i_beg = CAUSAL ? (kb * kRows) / kQStep : 0;
-  const int i_end = (N + kQStep - 1) / kQStep;
+  const int first_q = kb * kRows - off;  // the first query that sees the block's first key
+  const int i_beg = CAUSAL ? (first_q > 0 ? first_q / kQStep : 0) : 0;
+  const int i_end = (Nq + kQStep - 1) / kQStep;
   auto buf = [&](int i) { return smem + (i & 1) * (2 * TILE + 512); };
   auto stage = [&](int i) {
     char* b = buf(i);
-    stage_tile<D, kQStep>(Qh, i * kQStep, N, b, wave, lane);
-    stage_tile<D, kQStep>(dOh, i * kQStep, N, b + TILE, wave, lane);
-    if (wave == 0) stage_vec(Lh, i * kQStep, N, b + 2 * TILE, lane);
-    if (wave == 1) stage_vec(Dh, i * kQStep, N, b + 2 * TILE + 256, lane);
+    stage_tile<D, kQStep>(Qh, i * kQStep, Nq, b, wave, lane);
+    stage_tile<D, kQStep>(dOh, i * kQStep, Nq, b + TILE, wave, lane);
+    if (wave == 0) stage_vec(Lh, i * kQStep, Nq, b + 2 * TILE, lane);
+    if (wave == 1) stage_vec(Dh, i * kQStep, Nq, b + 2 * TILE + 256, lane);
   };
   if (i_beg < i_end) stage(i_beg);
   for (int i = i_beg; i < i_end; ++i) {
@@ -245,20 +258,19 @@ fa2_bwd_dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict_
     f32x16_t S = f32x16_t{}, dP = f32x16_t{};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(qtile, rbase, 0, ks), kf[ks], S, 0,
-                                                  0, 0);
-      dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(dtile, rbase, 0, ks), vf[ks], dP,
-                                                   0, 0, 0);
+      S = mfma32x32x16(row_frag<T, D>(qtile, rbase, 0, ks), kf[ks], S);
+      dP = mfma32x32x16(row_frag<T, D>(dtile, rbase, 0, ks), vf[ks], dP);
     }
     // This lane's key is k0 + col; accumulator r holds query
     // q_base + cr + 4*half with cr = 8*(r/4) + r%4 (a constant).  The query is
-    // visible to the key when lo <= cr < hi (at or after the key, before N);
-    // steps that lie wholly after the wavefront's keys and before N need no
-    // test (uniform for the wavefront).
-    const bool clean = q_base + kQStep <= N && (!CAUSAL || q_base >= k0 + 31);
-    const int lo = CAUSAL ? k0 + col - q_base - 4 * half : -1;
-    const int hi = N - q_base - 4 * half;
-    bf16x8_t pb[2], sb[2];
+    // visible to the key when lo <= cr < hi (key <= query + off, query < Nq);
+    // steps whose queries all see every key of the wavefront and lie before
+    // Nq need no test (uniform for the wavefront).  A query that sees no key
+    // at all has L = -inf; every one of its entries is masked.
+    const bool clean = q_base + kQStep <= Nq && (!CAUSAL || q_base + off >= k0 + 31);
+    const int lo = CAUSAL ? k0 + col - off - q_base - 4 * half : -1;
+    const int hi = Nq - q_base - 4 * half;
+    t8_t pb[2], sb[2];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int qr = 8 * g + 4 * half;  // first of 4 consecutive queries
@@ -269,31 +281,31 @@ fa2_bwd_dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict_
         const int cr = 8 * g + r;
         float p = __builtin_amdgcn_exp2f(__builtin_fmaf(S[g * 4 + r], c, -L4[r] * kLog2e));
         if (!clean) p = (cr < lo || cr >= hi) ? 0.f : p;
-        pb[g / 2][(g % 2) * 4 + r] = (__bf16)p;
-        sb[g / 2][(g % 2) * 4 + r] = (__bf16)(p * (dP[g * 4 + r] - D4[r]));
+        pb[g / 2][(g % 2) * 4 + r] = (T)p;
+        sb[g / 2][(g % 2) * 4 + r] = (T)(p * (dP[g * 4 + r] - D4[r]));
       }
     }
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int t = 0; t < DT; ++t) {
-        dv[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(dtile, tbase, u, t), pb[u],
-                                                        dv[t], 0, 0, 0);
-        dk[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(qtile, tbase, u, t), sb[u],
-                                                        dk[t], 0, 0, 0);
+        dv[t] = mfma32x32x16(tr_frag<T, D>(dtile, tbase, u, t), pb[u], dv[t]);
+        dk[t] = mfma32x32x16(tr_frag<T, D>(qtile, tbase, u, t), sb[u], dk[t]);
       }
   }
-  store_rows<D>(dv, 1.f, dVg + slice, k0, N, lane);
-  store_rows<D>(dk, scale, dKg + slice, k0, N, lane);
+  store_rows<T, D>(dv, 1.f, dVg + kslice, k0, Nk, lane);
+  store_rows<T, D>(dk, scale, dKg + kslice, k0, Nk, lane);
 }
 
 // ---------------------------------------------------------------- dQ
-template <int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL>
 __global__ void __launch_bounds__(kThreads, 2)
 fa2_bwd_dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
                   const uint16_t* __restrict__ Vg, const uint16_t* __restrict__ dOg,
                   const float* __restrict__ Lg, const float* __restrict__ Dg,
-                  uint16_t* __restrict__ dQg, int N, int num_m_block, float c, float scale) {
+                  uint16_t* __restrict__ dQg, int Nq, int Nk, int num_m_block, float c,
+                  float scale) {
+  typedef typename Vec16<T>::x8 t8_t;
   constexpr int KS = D / 16, DT = D / 32;
   constexpr int TILE = kStep * D * 2;
   __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * TILE];  // K, V tiles, two steps
@@ -304,98 +316,116 @@ fa2_bwd_dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ 
   const int mi = (int)blockIdx.x % num_m_block;
   const int m = CAUSAL ? num_m_block - 1 - mi : mi;  // heaviest query blocks first
   const int bh = blockIdx.x / num_m_block;
-  const size_t slice = (size_t)bh * N * D;
-  const uint16_t *Kh = Kg + slice, *Vh = Vg + slice;
+  const size_t qslice = (size_t)bh * Nq * D, kslice = (size_t)bh * Nk * D;
+  const uint16_t *Kh = Kg + kslice, *Vh = Vg + kslice;
+  const int off = Nk - Nq;  // key j visible to query i when j <= i + off
   const int q0 = m * kRows + 32 * wave;
   const int qrow = q0 + col;
   const uint32_t rbase = row_base<D>(lane), tbase = tr_base<D>(lane);
 
-  bf16x8_t qf[KS], df[KS];
-  load_frags<D>(qf, Qg + slice, qrow, N, half);
-  load_frags<D>(df, dOg + slice, qrow, N, half);
-  const float l2 = qrow < N ? Lg[(size_t)bh * N + qrow] * kLog2e : 0.f;
-  const float dd = qrow < N ? Dg[(size_t)bh * N + qrow] : 0.f;
+  t8_t qf[KS], df[KS];
+  load_frags<T, D>(qf, Qg + qslice, qrow, Nq, half);
+  load_frags<T, D>(df, dOg + qslice, qrow, Nq, half);
+  const float l2 = qrow < Nq ? Lg[(size_t)bh * Nq + qrow] * kLog2e : 0.f;
+  const float dd = qrow < Nq ? Dg[(size_t)bh * Nq + qrow] : 0.f;
   f32x16_t dq[DT];
 #pragma unroll
   for (int t = 0; t < DT; ++t) dq[t] = f32x16_t{};
 
-  const int j_end = CAUSAL ? (min(N, (m + 1) * kRows) - 1) / kStep + 1 : (N + kStep - 1) / kStep;
+  // K/V blocks up to the last key the workgroup's last query sees (none when
+  // it sees no key: dQ = 0).
+  const int nkb = (Nk + kStep - 1) / kStep;
+  const int last_key = min(Nq, (m + 1) * kRows) - 1 + off;
+  const int j_end = CAUSAL ? (last_key < 0 ? 0 : min(last_key / kStep + 1, nkb)) : nkb;
   auto buf = [&](int j) { return smem + (j & 1) * (2 * TILE); };
   auto stage = [&](int j) {
-    stage_tile<D>(Kh, j * kStep, N, buf(j), wave, lane);
-    stage_tile<D>(Vh, j * kStep, N, buf(j) + TILE, wave, lane);
+    stage_tile<D>(Kh, j * kStep, Nk, buf(j), wave, lane);
+    stage_tile<D>(Vh, j * kStep, Nk, buf(j) + TILE, wave, lane);
   };
-  stage(0);
+  if (j_end > 0) stage(0);
   for (int j = 0; j < j_end; ++j) {
     wait_vmcnt<0>();
     lds_barrier();
     if (j + 1 < j_end) stage(j + 1);
     const char* kt_ = buf(j);
     const char* vt = buf(j) + TILE;
-    const bool clean = (j + 1) * kStep <= N && (!CAUSAL || (j + 1) * kStep - 1 <= q0);
-    bf16x8_t sb[4];
+    const bool clean = (j + 1) * kStep <= Nk && (!CAUSAL || (j + 1) * kStep - 1 <= q0 + off);
+    t8_t sb[4];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       f32x16_t S = f32x16_t{}, dP = f32x16_t{};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(kt_, rbase, 32 * kt, ks), qf[ks],
-                                                    S, 0, 0, 0);
-        dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(vt, rbase, 32 * kt, ks), df[ks],
-                                                     dP, 0, 0, 0);
+        S = mfma32x32x16(row_frag<T, D>(kt_, rbase, 32 * kt, ks), qf[ks], S);
+        dP = mfma32x32x16(row_frag<T, D>(vt, rbase, 32 * kt, ks), df[ks], dP);
       }
       // This lane's query is qrow; accumulator r holds key
       // j*64 + 32*kt + cr + 4*half with cr = 8*(r/4) + r%4 (a constant),
-      // visible when cr <= th (at or before the query, before N).  Blocks wholly
-      // before the wavefront's first query and before N need no test.
+      // visible when cr <= th (key <= query + off, key < Nk).  Blocks whose keys
+      // every query of the wavefront sees, before Nk, need no test; a query
+      // that sees no key (L = -inf) has every entry masked.
       const int kb0 = j * kStep + 32 * kt + 4 * half;
-      int th = N - 1 - kb0;
-      if (CAUSAL) th = min(th, qrow - kb0);
+      int th = Nk - 1 - kb0;
+      if (CAUSAL) th = min(th, qrow + off - kb0);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int cr = 8 * (r / 4) + (r % 4);
         float p = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], c, -l2));
         if (!clean) p = cr > th ? 0.f : p;
-        sb[kt * 2 + r / 8][r % 8] = (__bf16)(p * (dP[r] - dd));
+        sb[kt * 2 + r / 8][r % 8] = (T)(p * (dP[r] - dd));
       }
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
       for (int t = 0; t < DT; ++t)
-        dq[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(kt_, tbase, u, t), sb[u],
-                                                        dq[t], 0, 0, 0);
+        dq[t] = mfma32x32x16(tr_frag<T, D>(kt_, tbase, u, t), sb[u], dq[t]);
   }
-  store_rows<D>(dq, scale, dQg + slice, q0, N, lane);
+  store_rows<T, D>(dq, scale, dQg + qslice, q0, Nq, lane);
 }
 
-template <int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL>
 hipError_t launch(const BwdArgs& a) {
   const float c = a.scale * kLog2e;
-  const int rows = a.BH * a.N;
+  const int qrows = a.BH * a.Nq;
   constexpr int RPB = kThreads / (D / 8);
-  hipLaunchKernelGGL((fa2_bwd_prep_kernel<D>), dim3((rows + RPB - 1) / RPB), dim3(kThreads), 0,
-                     a.stream, (const uint16_t*)a.O, (const uint16_t*)a.dO, a.Dvec, rows);
-  const int nkb = (a.N + kRows - 1) / kRows;
-  hipLaunchKernelGGL((fa2_bwd_dkdv_kernel<D, CAUSAL>), dim3(nkb * a.BH), dim3(kThreads), 0,
-                     a.stream, (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V,
-                     (const uint16_t*)a.dO, a.L, a.Dvec, (uint16_t*)a.dK, (uint16_t*)a.dV, a.N,
-                     nkb, c, a.scale);
-  hipLaunchKernelGGL((fa2_bwd_dq_kernel<D, CAUSAL>), dim3(nkb * a.BH), dim3(kThreads), 0,
-                     a.stream, (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V,
-                     (const uint16_t*)a.dO, a.L, a.Dvec, (uint16_t*)a.dQ, a.N, nkb, c, a.scale);
+  // Kernels with nothing to do are not launched: no queries leaves dK = dV = 0
+  // (written by the dK/dV kernel, which then walks no query step); no keys
+  // leaves dQ = 0 (written by the dQ kernel, which then walks no key block).
+  if (qrows > 0)
+    hipLaunchKernelGGL((fa2_bwd_prep_kernel<T, D>), dim3((qrows + RPB - 1) / RPB), dim3(kThreads),
+                       0, a.stream, (const uint16_t*)a.O, (const uint16_t*)a.dO, a.Dvec, qrows);
+  const int nkb = (a.Nk + kRows - 1) / kRows;
+  if (nkb * a.BH > 0)
+    hipLaunchKernelGGL((fa2_bwd_dkdv_kernel<T, D, CAUSAL>), dim3(nkb * a.BH), dim3(kThreads), 0,
+                       a.stream, (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V,
+                       (const uint16_t*)a.dO, a.L, a.Dvec, (uint16_t*)a.dK, (uint16_t*)a.dV, a.Nq,
+                       a.Nk, nkb, c, a.scale);
+  const int nmb = (a.Nq + kRows - 1) / kRows;
+  if (nmb * a.BH > 0)
+    hipLaunchKernelGGL((fa2_bwd_dq_kernel<T, D, CAUSAL>), dim3(nmb * a.BH), dim3(kThreads), 0,
+                       a.stream, (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V,
+                       (const uint16_t*)a.dO, a.L, a.Dvec, (uint16_t*)a.dQ, a.Nq, a.Nk, nmb, c,
+                       a.scale);
   return hipGetLastError();
+}
+
+template <typename T>
+hipError_t dispatch(const BwdArgs& a) {
+  switch (a.d * 2 + a.causal) {
+    case 64 * 2 + 0: return launch<T, 64, false>(a);
+    case 64 * 2 + 1: return launch<T, 64, true>(a);
+    case 128 * 2 + 0: return launch<T, 128, false>(a);
+    case 128 * 2 + 1: return launch<T, 128, true>(a);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_bwd_bf16(const BwdArgs& a) {
-  switch (a.d * 2 + a.causal) {
-    case 64 * 2 + 0: return launch<64, false>(a);
-    case 64 * 2 + 1: return launch<64, true>(a);
-    case 128 * 2 + 0: return launch<128, false>(a);
-    case 128 * 2 + 1: return launch<128, true>(a);
-  }
+hipError_t launch_bwd(const BwdArgs& a) {
+  if (a.elem == kBF16) return dispatch<__bf16>(a);
+  if (a.elem == kFP16) return dispatch<_Float16>(a);
   return hipErrorInvalidValue;
 }
 

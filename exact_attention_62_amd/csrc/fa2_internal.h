@@ -52,9 +52,10 @@ struct BwdArgs {
   void* dQ;
   void* dK;
   void* dV;
-  float* Dvec;  // workspace: rowsum(dO * O), [BH][N]
-  int BH, N, d, causal;
+  float* Dvec;  // workspace: rowsum(dO * O), [BH][Nq]
+  int BH, Nq, Nk, d, causal;  // causal aligned bottom-right when Nq != Nk
   float scale;
+  int elem;  // Elem of Q, K, V, O, dO and the gradients (bf16 or fp16)
   hipStream_t stream;
 };
 
@@ -71,6 +72,6 @@ hipError_t launch_combine(const FwdArgs& a);
 // The result when there are no keys (a.Nk == 0): O = 0 and L = -inf.
 hipError_t launch_fill_no_keys(const FwdArgs& a);
 // Enqueue the backward pass (three kernels) on a.stream.
-hipError_t launch_bwd_bf16(const BwdArgs& a);
+hipError_t launch_bwd(const BwdArgs& a);
 
 }  // namespace fa2

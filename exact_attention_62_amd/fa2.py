@@ -84,6 +84,10 @@ def load_library() -> ctypes.CDLL:
         lib.fa2_bwd.argtypes = [vp] * 9 + [i64, i64, i64, i64, ctypes.c_int, ctypes.c_float,
                                            ctypes.c_int, vp, ctypes.c_size_t, vp]
         lib.fa2_bwd.restype = ctypes.c_int
+        lib.fa2_bwd_cross.argtypes = [vp] * 9 + [i64, i64, i64, i64, i64, ctypes.c_int,
+                                                 ctypes.c_float, ctypes.c_int, vp, ctypes.c_size_t,
+                                                 vp]
+        lib.fa2_bwd_cross.restype = ctypes.c_int
         lib.fa2_bwd_workspace_size.argtypes = [i64, i64, i64, i64, ctypes.POINTER(ctypes.c_size_t)]
         lib.fa2_bwd_workspace_size.restype = ctypes.c_int
         lib.fa2_strerror.argtypes = [ctypes.c_int]
@@ -333,7 +337,7 @@ def merge_partials(parts, dtype: torch.dtype = torch.bfloat16):
 
 
 def fa2_bwd_workspace_size(B: int, H: int, N: int, d: int) -> int:
-    """Bytes of workspace fa2_bwd needs (no GPU call)."""
+    """Bytes of workspace fa2_bwd needs, N the query length (no GPU call)."""
     out = ctypes.c_size_t(0)
     _check(load_library().fa2_bwd_workspace_size(B, H, N, d, ctypes.byref(out)))
     return out.value
@@ -343,14 +347,14 @@ def fa2_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
             do: torch.Tensor, lse: torch.Tensor, dq: torch.Tensor, dk: torch.Tensor,
             dv: torch.Tensor, workspace: torch.Tensor, causal: bool = False,
             scale: float | None = None, stream: torch.cuda.Stream | None = None) -> None:
-    """Enqueue the backward pass (bfloat16): writes dq, dk, dv in place.  o and lse are
-    fa2_fwd's outputs for q, k, v; workspace holds at least fa2_bwd_workspace_size bytes."""
+    """Enqueue the backward pass (bfloat16 or float16): writes dq, dk, dv in place.  o and lse
+    are the forward's outputs for q [B, H, Nq, d], k, v [B, H, Nk, d] (Nq != Nk runs
+    fa2_bwd_cross, causal aligned bottom-right); workspace holds at least
+    fa2_bwd_workspace_size(B, H, Nq, d) bytes."""
     B, H, N, Nk, d = _check_tensors(q, k, v, o, lse)
-    if Nk != N:
-        raise ValueError(f"fa2_bwd needs equal query and key lengths ({N} != {Nk})")
-    for name, t in (("do", do), ("dq", dq), ("dk", dk), ("dv", dv)):
-        if t.shape != q.shape or t.dtype != q.dtype:
-            raise ValueError(f"{name} must be {q.dtype} {tuple(q.shape)}")
+    for name, t, like in (("do", do, q), ("dq", dq, q), ("dk", dk, k), ("dv", dv, k)):
+        if t.shape != like.shape or t.dtype != q.dtype:
+            raise ValueError(f"{name} must be {q.dtype} {tuple(like.shape)}")
         if not t.is_cuda or not t.is_contiguous() or t.device != q.device:
             raise ValueError(f"{name} must be a contiguous tensor on the inputs' GPU")
     if not workspace.is_cuda or not workspace.is_contiguous() or workspace.device != q.device:
@@ -360,18 +364,20 @@ def fa2_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     lib = load_library()
+    ptrs = [_ptr(t) for t in (q, k, v, o, do, lse, dq, dk, dv)]
+    tail = (1 if causal else 0, float(scale), _DTYPES[q.dtype], _ptr(workspace),
+            workspace.numel() * workspace.element_size(), ctypes.c_void_p(stream.cuda_stream))
     with torch.cuda.device(q.device):
-        st = lib.fa2_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
-                         lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d,
-                         1 if causal else 0, float(scale), _DTYPES[q.dtype], workspace.data_ptr(),
-                         workspace.numel() * workspace.element_size(),
-                         ctypes.c_void_p(stream.cuda_stream))
+        if Nk == N:
+            st = lib.fa2_bwd(*ptrs, B, H, N, d, *tail)
+        else:
+            st = lib.fa2_bwd_cross(*ptrs, B, H, N, Nk, d, *tail)
     _check(st)
 
 
 def attention_backward(q, k, v, o, lse, do, causal: bool = False, scale: float | None = None):
     """Allocate dQ, dK, dV and a workspace, run fa2_bwd, return (dq, dk, dv)."""
-    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     B, H, N, d = q.shape
     ws = torch.empty(fa2_bwd_workspace_size(B, H, N, d), dtype=torch.uint8, device=q.device)
     fa2_bwd(q, k, v, o, do.contiguous(), lse, dq, dk, dv, ws, causal=causal, scale=scale)
@@ -379,7 +385,8 @@ def attention_backward(q, k, v, o, lse, do, causal: bool = False, scale: float |
 
 
 class FlashAttention(torch.autograd.Function):
-    """Autograd wrapper: forward through fa2_fwd, backward through fa2_bwd (bfloat16)."""
+    """Autograd wrapper: forward through fa2_fwd / fa2_fwd_cross, backward through fa2_bwd /
+    fa2_bwd_cross (bfloat16 or float16; d = 64 or 128 for the backward)."""
 
     @staticmethod
     def forward(ctx, q, k, v, causal=False, scale=None):

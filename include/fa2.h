@@ -248,14 +248,15 @@ const char* fa2_strerror(fa2_status_t status);
  * diagonal).  dQ is computed by a second, query-outer pass rather than with
  * atomics, so results are deterministic.
  *
- *   Q, K, V, O, dO   [B][H][N][d] bf16 inputs, device memory, 16-byte aligned; O
- *                    is fa2_fwd's output for Q, K, V (only rowsum(dO * O) is used).
+ *   Q, K, V, O, dO   [B][H][N][d] inputs of type dtype, device memory, 16-byte
+ *                    aligned; O is fa2_fwd's output for Q, K, V (only
+ *                    rowsum(dO * O) is used).
  *   L                [B][H][N] float32, fa2_fwd's L, device memory, 4-byte aligned.
- *   dQ, dK, dV       [B][H][N][d] bf16 outputs, device memory, 16-byte aligned.
+ *   dQ, dK, dV       [B][H][N][d] outputs of type dtype, device memory, 16-byte aligned.
  *   B, H, N, causal, scale, stream: as for fa2_fwd (the same values as the
  *                    forward call).  B*H*N == 0 does nothing and returns FA2_OK.
- *   d                64 or 128 (256 and others: FA2_ENOTSUP).
- *   dtype            FA2_BF16 only (others: FA2_ENOTSUP).
+ *   d                64 or 128 (others: FA2_ENOTSUP).
+ *   dtype            FA2_BF16 or FA2_FP16 (FA2_FP32: FA2_ENOTSUP).
  *   workspace        device memory owned by the caller, 4-byte aligned, at least
  *                    fa2_bwd_workspace_size() bytes (it receives D); contents on
  *                    entry do not matter.  workspace_bytes is its size.
@@ -268,9 +269,24 @@ fa2_status_t fa2_bwd(const void* Q, const void* K, const void* V, const void* O,
                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * fa2_bwd_cross - the backward pass of fa2_fwd_cross: Q, O, dO, L and dQ have
+ * Nq rows ([B][H][Nq][d], L [B][H][Nq]), K, V, dK and dV Nk rows; the causal
+ * mask is aligned bottom-right as in the forward (key j visible to query i iff
+ * j <= i + Nk - Nq).  A query that sees no key adds nothing (its dQ row is 0),
+ * and a key no query sees gets dK = dV = 0.  Arrays of zero size may be NULL.
+ * Everything else as for fa2_bwd; the workspace holds one float32 per query
+ * row (fa2_bwd_workspace_size with N = Nq).
+ */
+fa2_status_t fa2_bwd_cross(const void* Q, const void* K, const void* V, const void* O,
+                           const void* dO, const float* L, void* dQ, void* dK, void* dV,
+                           int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int causal,
+                           float scale, fa2_dtype_t dtype, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/*
  * fa2_bwd_workspace_size - bytes of workspace fa2_bwd needs: B*H*N * 4 (one
- * float32 per row).  Host-only: makes no HIP call.  Returns the size and head
- * dimension errors fa2_bwd would.
+ * float32 per query row; N = Nq for fa2_bwd_cross).  Host-only: makes no HIP
+ * call.  Returns the size and head dimension errors fa2_bwd would.
  */
 fa2_status_t fa2_bwd_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d, size_t* bytes);
 

@@ -32,7 +32,7 @@ def _declared_functions():
 
 
 def test_header_declares_the_boundary():
-    assert _declared_functions() == ["fa2_bwd", "fa2_bwd_workspace_size", "fa2_fwd",
+    assert _declared_functions() == ["fa2_bwd", "fa2_bwd_cross", "fa2_bwd_workspace_size", "fa2_fwd",
                                      "fa2_fwd_cross", "fa2_fwd_partial", "fa2_fwd_splitkv",
                                      "fa2_last_error", "fa2_launch_shape", "fa2_merge",
                                      "fa2_num_splits", "fa2_splitkv_workspace_size",
@@ -266,7 +266,7 @@ def test_bwd_workspace_size_formula():
 
 
 @pytest.mark.parametrize("kw,status,needle", [
-    (dict(dtype=F.FA2_FP32), F.FA2_ENOTSUP, "FA2_BF16 only"),
+    (dict(dtype=F.FA2_FP32), F.FA2_ENOTSUP, "FA2_BF16 and FA2_FP16 only"),
     (dict(d=256), F.FA2_ENOTSUP, "d=256"),
     (dict(d=96), F.FA2_ENOTSUP, "d=96"),
     (dict(do=None), F.FA2_EINVAL, "dO is NULL"),
@@ -347,3 +347,40 @@ def test_merge_of_no_rows_is_a_no_op():
 def test_partial_and_merge_without_a_device_report_the_hip_error():
     assert _partial() == F.FA2_EHIP
     assert _merge() == F.FA2_EHIP
+
+
+def _bwd_cross(dtype=F.FA2_BF16, ws_bytes=1 << 16, **kw):
+    base = FAKE
+    a = dict(q=base, k=base + 0x100000, v=base + 0x200000, o=base + 0x300000, do=base + 0x400000,
+             L=base + 0x500000, dq=base + 0x600000, dk=base + 0x700000, dv=base + 0x800000,
+             ws=base + 0x900000, B=1, H=1, Nq=16, Nk=48, d=64, causal=1, scale=0.125)
+    a.update(kw)
+    return F.load_library().fa2_bwd_cross(
+        a["q"], a["k"], a["v"], a["o"], a["do"], a["L"], a["dq"], a["dk"], a["dv"], a["B"], a["H"],
+        a["Nq"], a["Nk"], a["d"], a["causal"], a["scale"], dtype, a["ws"], ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(Nk=-1), F.FA2_EINVAL, "sizes must be >= 0"),
+    (dict(dk=None), F.FA2_EINVAL, "dK is NULL"),
+    # dK holds 48 rows of 128 bytes: dV placed 4 KB after its start overlaps it
+    (dict(dv=FAKE + 0x700000 + 4096), F.FA2_EINVAL, "overlaps"),
+    (dict(d=96), F.FA2_ENOTSUP, "d=96"),
+])
+def test_bwd_cross_invalid_arguments_before_any_hip_call(kw, status, needle):
+    assert _bwd_cross(**kw) == status
+    assert needle in F.fa2_last_error()
+
+
+def test_bwd_cross_empty_problem_is_a_no_op():
+    nulls = dict(q=None, k=None, v=None, o=None, do=None, L=None, dq=None, dk=None, dv=None,
+                 ws=None)
+    assert _bwd_cross(Nq=0, Nk=0, **nulls) == F.FA2_OK
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="needs a host without a visible GPU")
+def test_bwd_cross_zero_size_sides_need_no_pointers():
+    # No queries: Q, O, dO, L, dQ and the workspace are empty and may be NULL (dK = dV = 0 is
+    # still written, so the call then needs the device); likewise K, V, dK, dV without keys.
+    assert _bwd_cross(q=None, o=None, do=None, L=None, dq=None, ws=None, ws_bytes=0, Nq=0) == F.FA2_EHIP
+    assert _bwd_cross(k=None, v=None, dk=None, dv=None, Nk=0) == F.FA2_EHIP

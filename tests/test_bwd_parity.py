@@ -110,3 +110,74 @@ def test_autograd_wrapper():
     o = FlashAttention.apply(qd, kd, vd, True, None)
     o.backward(do.cuda())
     _check((qd.grad, kd.grad, vd.grad), ref, "autograd wrapper")
+
+
+# ---- fp16 and query/key lengths that differ --------------------------------------------------
+def _run_bwd(q, k, v, do, causal, scale=None):
+    qd, kd, vd, dod = (t.cuda() for t in (q, k, v, do))
+    o, lse = attention(qd, kd, vd, causal=causal, scale=scale)
+    got = attention_backward(qd, kd, vd, o, lse, dod, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return got
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", [(1, 2, 64, 64), (2, 1, 127, 128), (1, 2, 300, 64),
+                                   (1, 1, 513, 128)], ids=lambda s: "x".join(map(str, s)))
+def test_bwd_fp16(shape, causal):
+    B, H, N, d = shape
+    _say(f"fp16 B={B} H={H} N={N} d={d} causal={causal}")
+    q, k, v = make_random(B, H, N, d, seed=N + d + causal + 5, dtype="fp16")
+    do = make_upstream(B, H, N, d, seed=N + d, dtype="fp16")
+    ref = attention_bwd_fp64(q, k, v, do, causal=causal)
+    _check(_run_bwd(q, k, v, do, causal), ref, f"fp16 {shape} causal={causal}")
+
+
+CROSS = [
+    # (B, H, Nq, Nk, d): short query blocks over long keys, one query, more queries than keys
+    # (the first Nq - Nk rows see no key under the causal mask), ragged both ways, one key
+    (1, 2, 5, 300, 64), (2, 1, 64, 200, 128), (1, 2, 1, 513, 128), (1, 2, 200, 64, 64),
+    (1, 1, 300, 129, 128), (1, 2, 129, 1, 64), (2, 2, 100, 1000, 64),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("case", CROSS, ids=lambda c: "x".join(map(str, c)))
+def test_bwd_cross_lengths(case, causal, dtype):
+    B, H, Nq, Nk, d = case
+    _say(f"cross {dtype} B={B} H={H} Nq={Nq} Nk={Nk} d={d} causal={causal}")
+    q, k, v = make_random(B, H, Nq, d, seed=Nq + 3 * Nk + causal, dtype=dtype, Nk=Nk)
+    do = make_upstream(B, H, Nq, d, seed=Nq + Nk, dtype=dtype)
+    ref = attention_bwd_fp64(q, k, v, do, causal=causal)
+    got = _run_bwd(q, k, v, do, causal)
+    assert got[0].shape == q.shape and got[1].shape == k.shape and got[2].shape == v.shape
+    _check(got, ref, f"cross {dtype} {case} causal={causal}")
+
+
+def test_bwd_cross_no_queries_and_no_keys():
+    from exact_attention_62_amd import fa2_bwd, fa2_bwd_workspace_size
+    # No queries: dK = dV = 0 must still be written; no keys: dQ = 0.
+    for Nq, Nk in ((0, 70), (70, 0)):
+        q, k, v = (t.cuda() for t in make_random(1, 2, Nq, 64, seed=9, Nk=Nk))
+        do = make_upstream(1, 2, Nq, 64, seed=9).cuda()
+        o = torch.zeros_like(q)
+        lse = torch.full((1, 2, Nq), float("-inf"), device="cuda")
+        dq, dk, dv = (torch.full_like(t, float("nan")) for t in (q, k, v))
+        ws = torch.empty(max(4, fa2_bwd_workspace_size(1, 2, Nq, 64)), dtype=torch.uint8,
+                         device="cuda")
+        fa2_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, causal=True)
+        torch.cuda.synchronize()
+        for t in (dq, dk, dv):
+            assert bool(torch.all(t == 0)), f"Nq={Nq} Nk={Nk}: not all zero"
+
+
+def test_autograd_wrapper_cross_fp16():
+    q, k, v = make_random(1, 2, 96, 64, seed=12, dtype="fp16", Nk=333)
+    do = make_upstream(1, 2, 96, 64, seed=12, dtype="fp16")
+    ref = attention_bwd_fp64(q, k, v, do, causal=True)
+    qd, kd, vd = (t.cuda().requires_grad_() for t in (q, k, v))
+    out = FlashAttention.apply(qd, kd, vd, True, None)
+    out.backward(do.cuda())
+    torch.cuda.synchronize()
+    _check((qd.grad, kd.grad, vd.grad), ref, "autograd cross fp16")
