@@ -143,6 +143,21 @@ def test_full_size_workload_sampled(name, causal, seed):
     _say(f"{name}: max |dO| = {worst_o:.3e}, max |dL| = {worst_l:.3e}")
 
 
+def test_very_long_sequence_sampled():
+    # A 2^21-key causal sequence (512 MB per tensor at d = 128): row and element offsets far
+    # past the benchmark shapes.  Rows sampled at the start, around block edges, at random and
+    # at the end.
+    N, d = 1 << 21, 128
+    _say(f"one head, N={N} d={d} causal")
+    q, k, v = make_random(1, 1, N, d, seed=21)
+    o, lse = _run(q, k, v, True)
+    rng = np.random.default_rng(21)
+    rows = sorted(set([0, 1, 127, 128, N // 2, N // 2 + 1, N - 129, N - 128, N - 1]) |
+                  set(rng.integers(0, N, 12).tolist()))
+    O, L = attention_rows_fp64(q, k, v, 0, 0, rows, causal=True)
+    _cmp(o[0, 0, rows].cpu(), lse[0, 0, rows].cpu(), O, L, "bf16", f"N={N}")
+
+
 def test_ragged_sigma2_reading():
     # "N(0,4)" read as variance 4 (sigma 2): logits reach ~25 instead of ~100.
     w = WORKLOADS["ragged"]

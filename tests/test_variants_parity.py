@@ -226,3 +226,16 @@ def test_decode_shape_full(dtype):
     _cmp(o, lse, O, L, dtype, f"decode split {dtype}")
     o2, lse2 = _cross(q, k, v, True)
     _cmp(o2, lse2, O, L, dtype, f"decode plain {dtype}")
+
+
+def test_decode_over_two_million_keys():
+    # One query per head over 2^21 cached keys (512 MB of K at d = 128), through split-KV with
+    # the pages' rule and through the plain path.
+    B, H, Nq, Nk, d = 1, 2, 1, 1 << 21, 128
+    q, k, v = make_random(B, H, Nq, d, seed=77, Nk=Nk)
+    _say(f"decode over {Nk} keys")
+    O, L = attention_fp64(q, k, v, causal=True)
+    o, lse = _split(q, k, v, True, 0)
+    _cmp(o, lse, O, L, "bf16", "decode 2M split")
+    o2, lse2 = _cross(q, k, v, True)
+    _cmp(o2, lse2, O, L, "bf16", "decode 2M plain")
