@@ -172,6 +172,16 @@ __device__ __forceinline__ void store_rows(const f32x16_t (&acc)[D / 32], float 
     }
 }
 
+// Workgroup ids are dealt to the 8 XCDs round-robin (id % 8), and each XCD has
+// its own L2.  The logical block index gives XCD x a contiguous range of
+// blocks, so the blocks of one head (which read the same Q/dO or K/V tiles)
+// run on one XCD and share its L2.  A bijection on [0, G) for any G; only
+// speed depends on the dispatcher actually dealing ids this way.
+__device__ __forceinline__ int xcd_block(int id, int G) {
+  const int x = id & 7, i = id >> 3, q = G >> 3, r = G & 7;
+  return x < r ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
+}
+
 // ---------------------------------------------------------------- D = rowsum(dO * O)
 template <typename T, int D>
 __global__ void __launch_bounds__(kThreads)
@@ -215,9 +225,11 @@ fa2_bwd_dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict_
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int half = lane >> 5, col = lane & 31;
-  // With the causal mask the first key blocks are the heaviest; they go out first.
-  const int kb = (int)blockIdx.x % num_k_block;
-  const int bh = blockIdx.x / num_k_block;
+  // The key blocks of a head are consecutive logical blocks, so they run side by
+  // side on one XCD; with the causal mask the first (heaviest) goes out first.
+  const int blk = xcd_block(blockIdx.x, gridDim.x);
+  const int kb = blk % num_k_block;
+  const int bh = blk / num_k_block;
   const size_t qslice = (size_t)bh * Nq * D, kslice = (size_t)bh * Nk * D;
   const uint16_t *Qh = Qg + qslice, *dOh = dOg + qslice;
   const float *Lh = Lg + (size_t)bh * Nq, *Dh = Dg + (size_t)bh * Nq;
@@ -232,7 +244,10 @@ fa2_bwd_dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict_
 #pragma unroll
   for (int t = 0; t < DT; ++t) dk[t] = dv[t] = f32x16_t{};
 
-  // Query steps: from the first that can see the block's keys to the end.
+  // Query steps: those from the first that can see the block's keys to the end,
+  // walked from the last down.  Every key block of a head then starts at the
+  // same query step, and the blocks running side by side read each staged Q/dO
+  // tile at about the same time (from L2), whatever their first step.
   const int first_q = kb * kRows - off;  // the first query that sees the block's first key
   const int i_beg = CAUSAL ? (first_q > 0 ? first_q / kQStep : 0) : 0;
   const int i_end = (Nq + kQStep - 1) / kQStep;
@@ -244,11 +259,11 @@ fa2_bwd_dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict_
     if (wave == 0) stage_vec(Lh, i * kQStep, Nq, b + 2 * TILE, lane);
     if (wave == 1) stage_vec(Dh, i * kQStep, Nq, b + 2 * TILE + 256, lane);
   };
-  if (i_beg < i_end) stage(i_beg);
-  for (int i = i_beg; i < i_end; ++i) {
+  if (i_beg < i_end) stage(i_end - 1);
+  for (int i = i_end - 1; i >= i_beg; --i) {
     wait_vmcnt<0>();
     lds_barrier();
-    if (i + 1 < i_end) stage(i + 1);
+    if (i > i_beg) stage(i - 1);
     const char* b = buf(i);
     const char* qtile = b;
     const char* dtile = b + TILE;
@@ -313,9 +328,12 @@ fa2_bwd_dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int half = lane >> 5, col = lane & 31;
-  const int mi = (int)blockIdx.x % num_m_block;
-  const int m = CAUSAL ? num_m_block - 1 - mi : mi;  // heaviest query blocks first
-  const int bh = blockIdx.x / num_m_block;
+  // The query blocks of a head are consecutive logical blocks (one XCD, one
+  // L2 for the K/V tiles they all walk from key 0); heaviest causal block first.
+  const int blk = xcd_block(blockIdx.x, gridDim.x);
+  const int mi = blk % num_m_block;
+  const int m = CAUSAL ? num_m_block - 1 - mi : mi;
+  const int bh = blk / num_m_block;
   const size_t qslice = (size_t)bh * Nq * D, kslice = (size_t)bh * Nk * D;
   const uint16_t *Kh = Kg + kslice, *Vh = Vg + kslice;
   const int off = Nk - Nq;  // key j visible to query i when j <= i + off
