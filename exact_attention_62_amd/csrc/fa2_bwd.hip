@@ -55,16 +55,25 @@ constexpr int kRows = 32 * kWaves;  // keys (dK/dV) or queries (dQ) per workgrou
 constexpr int kStep = 64;           // queries (dK/dV) or keys (dQ) per inner step
 
 // Byte offset of element (row r, dim c) of a staged [rows][D] 16-bit tile.
+// Rows go in groups of 4 (g = r/4, 8D bytes each) and dims in 16-dim segments of
+// 128 bytes; a segment holds two 64-byte halves (its dims 0-7 and 8-15), each
+// 4 rows x 16 bytes.  Odd row groups swap adjacent segments and row groups
+// with bit 1 set swap the halves.  The 16 lanes of one pass of a 16-byte row
+// read (4 row groups x 4 rows, one 16-dim segment) then reach all 64 banks
+// once, and each 16-lane group of a transposing read still reads one whole
+// 128-byte segment.
 template <int D>
 __device__ __forceinline__ constexpr int toff(int r, int c) {
-  return (r >> 2) * (8 * D) + (c >> 4) * 128 + 32 * (r & 3) + 2 * (c & 15);
+  return (r >> 2) * (8 * D) + ((c >> 4) ^ ((r >> 2) & 1)) * 128 +
+         64 * (((c >> 3) & 1) ^ ((r >> 3) & 1)) + 16 * (r & 3) + 2 * (c & 7);
 }
 
 // Stage rows [r0, r0 + ROWS) of a [N][D] 16-bit slice into LDS in the tile layout
 // (rows past N are clamped to row N - 1; callers mask them).  Load i of this
-// thread fills 1 KB chunk n = wave*LOADS + i: its lane L writes 16 bytes, row
-// 4*(bk / NSEG) + (L%8)/2 and dims 16*(bk % NSEG) + 8*(L%2) of 128-byte block
-// bk = 8n + L/8.
+// thread fills 1 KB chunk n = wave*LOADS + i: its lane L writes the 16 bytes at
+// slot L%8 of 128-byte block bk = 8n + L/8, which is segment position bk % NSEG
+// of row group g = bk / NSEG: row 4g + L%4, dims 16*((bk % NSEG) ^ (g%2)) +
+// 8*((L%8)/4 ^ (g/2)%2).
 template <int D, int ROWS = kStep>
 __device__ __forceinline__ void stage_tile(const uint16_t* head, int r0, int N, char* buf,
                                            int wave, int lane) {
@@ -76,8 +85,9 @@ __device__ __forceinline__ void stage_tile(const uint16_t* head, int r0, int N, 
   for (int i = 0; i < LOADS; ++i) {
     const int n = wave * LOADS + i;
     const int bk = 8 * n + lane / 8;
-    const int r = min(r0 + 4 * (bk / NSEG) + (lane % 8) / 2, N - 1);
-    const int c = 16 * (bk % NSEG) + 8 * (lane % 2);
+    const int g = bk / NSEG;
+    const int r = min(r0 + 4 * g + lane % 4, N - 1);
+    const int c = 16 * ((bk % NSEG) ^ (g & 1)) + 8 * (((lane % 8) / 4) ^ ((g >> 1) & 1));
     lds_dma(head + (size_t)r * D + c, lds_addr(buf + n * 1024));
   }
 }
@@ -90,46 +100,117 @@ __device__ __forceinline__ void stage_vec(const float* v, int r0, int N, char* b
                : : "s"(lds_addr(buf)), "v"(src) : "memory", "m0");
 }
 
-// LDS addresses of fragments in a staged tile, as one per-lane base (computed
+// LDS addresses of fragments in a staged tile, as two per-lane bases (computed
 // once) plus compile-time offsets.
 //
-// Row fragment: the A operand of a 32x32x16 MFMA, rows m = row0 + lane%32 and
-// dims 16*ks + 8*(lane/32) .. +8, one 16-byte read at
-//   row_base(lane) + (row0/4)*8D + 128*ks,
-//   row_base(lane) = ((lane%32)/4)*8D + 32*(lane%4) + 16*(lane/32).
+// Row fragment: the A operand of a 32x32x16 MFMA, rows m = row0 + lane%32
+// (row0 a multiple of 32) and dims 16*ks + 8*(lane/32) .. +8, one 16-byte read
+// at base[ks % 2] + (row0/4)*8D + 256*(ks/2), with g = (lane%32)/4 and
+//   base[p](lane) = g*8D + 128*(p ^ g%2) + 64*(lane/32 ^ (g/2)%2) + 16*(lane%4).
 template <int D>
-__device__ __forceinline__ uint32_t row_base(int lane) {
-  return (uint32_t)(((lane & 31) >> 2) * (8 * D) + 32 * (lane & 3) + 16 * (lane >> 5));
+__device__ __forceinline__ constexpr int row_base(int lane, int p) {
+  const int g = (lane & 31) >> 2;
+  return g * (8 * D) + 128 * (p ^ (g & 1)) + 64 * ((lane >> 5) ^ ((g >> 1) & 1)) + 16 * (lane & 3);
 }
+template <int D>
+struct Bases {
+  uint32_t row[2], tr[2];
+};
 template <typename T, int D>
-__device__ __forceinline__ typename Vec16<T>::x8 row_frag(const char* tile, uint32_t rbase, int row0,
-                                                          int ks) {
-  return *(const typename Vec16<T>::x8*)(tile + rbase + (row0 / 4) * (8 * D) + 128 * ks);
+__device__ __forceinline__ typename Vec16<T>::x8 row_frag(const char* tile, const Bases<D>& b,
+                                                          int row0, int ks) {
+  return *(const typename Vec16<T>::x8*)(tile + b.row[ks & 1] + (row0 / 4) * (8 * D) +
+                                         256 * (ks >> 1));
 }
 // Transposed fragment: the A operand (dims x rows) for rows 16u .. 16u+15 of
 // the tile and dims 32t .. 32t+31, in the permuted row order that matches a B
 // operand packed from accumulator registers 8*(u%2) .. 8*(u%2)+7 of the
-// 32-row tile u/2.  Within each 16-lane group (g = lane/16, i = lane%16),
-// lane 4*r + c points at 4 consecutive dims of row kbase + r;
+// 32-row tile u/2.  Within each 16-lane group (sb = (lane/16)%2, i = lane%16),
+// lane 4*r + c points at dims 32t + 16sb + 4c .. +3 of row kbase + r;
 // ds_read_b64_tr_b16 hands lane t of the group the 4 rows kbase .. kbase+3 of
-// dim t.  kbase = 16u + 4*half (first 4 slots) and 16u + 8 + 4*half (last 4),
-// so the group reads one whole 128-byte block of the layout:
-//   tr_base(lane) = half*8D + 128*(g%2) + 8*i,
-//   + 32D*u + 256*t, and + 16D for the last 4.
+// dim t.  kbase = 16u + 4*half (first 4 slots, e = 0) and 16u + 8 + 4*half
+// (last 4, e = 1): row group g = 4u + half + 2e, so the group reads one whole
+// 128-byte segment, at
+//   base.tr[e](lane) = half*8D + 16D*e + 128*(sb ^ half) + 64*(c/2 ^ e) + 16*r + 8*(c%2),
+//   + 32D*u + 256*t.
 template <int D>
-__device__ __forceinline__ uint32_t tr_base(int lane) {
-  return (uint32_t)((lane >> 5) * (8 * D) + 128 * ((lane >> 4) & 1) + 8 * (lane & 15));
+__device__ __forceinline__ constexpr int tr_base(int lane, int e) {
+  const int half = lane >> 5, sb = (lane >> 4) & 1, i = lane & 15, c = i & 3;
+  return half * (8 * D) + 16 * D * e + 128 * (sb ^ half) + 64 * ((c >> 1) ^ e) + 16 * (i >> 2) +
+         8 * (c & 1);
+}
+template <int D>
+__device__ __forceinline__ Bases<D> bases(int lane) {
+  Bases<D> b;
+#pragma unroll
+  for (int p = 0; p < 2; ++p) b.row[p] = (uint32_t)row_base<D>(lane, p);
+#pragma unroll
+  for (int e = 0; e < 2; ++e) b.tr[e] = (uint32_t)tr_base<D>(lane, e);
+  return b;
 }
 template <typename T, int D>
-__device__ __forceinline__ typename Vec16<T>::x8 tr_frag(const char* tile, uint32_t tbase, int u,
+__device__ __forceinline__ typename Vec16<T>::x8 tr_frag(const char* tile, const Bases<D>& b, int u,
                                                          int t) {
-  const char* p = tile + tbase + 32 * D * u + 256 * t;
-  const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr_t)p);
-  const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr_t)(p + 16 * D));
+  const int o = 32 * D * u + 256 * t;
+  const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr_t)(tile + b.tr[0] + o));
+  const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr_t)(tile + b.tr[1] + o));
   return __builtin_bit_cast(typename Vec16<T>::x8,
                             __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
-static_assert(toff<128>(5, 40) == 1 * 1024 + 2 * 128 + 32 * 1 + 2 * 8, "tile layout");
+
+// Compile-time proof of the layout for a [ROWS][D] tile: the direct loads of
+// stage_tile fill every element where toff puts it; row and transposing
+// fragment addresses equal toff of the (row, dims) the MFMA operand needs;
+// each 16-lane pass of a row read reaches 16 distinct 16-byte bank groups
+// (64 banks of 4 bytes) and each 16-lane group of a transposing read 16
+// distinct 8-byte slots of one 128-byte span.
+template <int D, int ROWS>
+__device__ __forceinline__ constexpr bool tile_layout_ok() {
+  constexpr int NSEG = D / 16;
+  for (int n = 0; n < ROWS * D * 2 / 1024; ++n)
+    for (int L = 0; L < 64; ++L) {
+      const int bk = 8 * n + L / 8, g = bk / NSEG;
+      const int r = 4 * g + L % 4;
+      const int c = 16 * ((bk % NSEG) ^ (g & 1)) + 8 * (((L % 8) / 4) ^ ((g >> 1) & 1));
+      for (int k = 0; k < 8; ++k)
+        if (toff<D>(r, c + k) != n * 1024 + 16 * L + 2 * k) return false;
+    }
+  for (int row0 = 0; row0 < ROWS; row0 += 32)
+    for (int ks = 0; ks < D / 16; ++ks)
+      for (int pass = 0; pass < 4; ++pass) {
+        bool used[16] = {};
+        for (int l = 16 * pass; l < 16 * pass + 16; ++l) {
+          const int a = row_base<D>(l, ks & 1) + (row0 / 4) * (8 * D) + 256 * (ks >> 1);
+          for (int k = 0; k < 8; ++k)
+            if (toff<D>(row0 + (l & 31), 16 * ks + 8 * (l >> 5) + k) != a + 2 * k) return false;
+          if (used[(a / 16) % 16]) return false;
+          used[(a / 16) % 16] = true;
+        }
+      }
+  for (int u = 0; u < ROWS / 16; ++u)
+    for (int t = 0; t < D / 32; ++t)
+      for (int e = 0; e < 2; ++e)
+        for (int grp = 0; grp < 4; ++grp) {
+          bool used[16] = {};
+          int lo = 1 << 30;
+          for (int l = 16 * grp; l < 16 * grp + 16; ++l) {
+            const int a = tr_base<D>(l, e) + 32 * D * u + 256 * t;
+            lo = a < lo ? a : lo;
+          }
+          for (int l = 16 * grp; l < 16 * grp + 16; ++l) {
+            const int a = tr_base<D>(l, e) + 32 * D * u + 256 * t, i = l & 15;
+            const int row = 16 * u + 4 * (l >> 5) + 8 * e + (i >> 2);
+            const int dim = 32 * t + 16 * ((l >> 4) & 1) + 4 * (i & 3);
+            for (int k = 0; k < 4; ++k)
+              if (toff<D>(row, dim + k) != a + 2 * k) return false;
+            if (a - lo >= 128 || used[(a - lo) / 8]) return false;
+            used[(a - lo) / 8] = true;
+          }
+        }
+  return true;
+}
+static_assert(tile_layout_ok<64, 32>() && tile_layout_ok<64, 64>(), "tile layout, d = 64");
+static_assert(tile_layout_ok<128, 32>() && tile_layout_ok<128, 64>(), "tile layout, d = 128");
 
 // B operand fragments of a [N][D] 16-bit slice held in registers: for k-step ks,
 // lane l holds row r0 + l%32, dims 16*ks + 8*(l/32) .. +8 (zero past N).
@@ -142,6 +223,18 @@ __device__ __forceinline__ void load_frags(typename Vec16<T>::x8 (&f)[D / 16], c
     if (row < N) t = *(const u32x4_t*)(head + (size_t)row * D + 16 * ks + 8 * half);
     f[ks] = __builtin_bit_cast(typename Vec16<T>::x8, t);
   }
+}
+
+// Wait for the fragment loads issued before a kernel's main loop and pass the
+// registers through an empty asm statement.  The compiler then sees them
+// defined by that statement rather than by pending loads, and puts no
+// vmcnt wait inside the loop, where it would also wait for the direct loads
+// that stage the next step (they are invisible to it).
+template <typename V, int KS>
+__device__ __forceinline__ void hold_loaded(V (&a)[KS], V (&b)[KS]) {
+  wait_vmcnt<0>();
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(a[ks]), "+v"(b[ks]));
 }
 
 // Store a transposed accumulator (DT tiles of 32 dims x 32 rows; lane = row)
@@ -235,11 +328,12 @@ fa2_bwd_dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict_
   const float *Lh = Lg + (size_t)bh * Nq, *Dh = Dg + (size_t)bh * Nq;
   const int off = Nk - Nq;                // key j visible to query i when j <= i + off
   const int k0 = kb * kRows + 32 * wave;  // this wavefront's first key
-  const uint32_t rbase = row_base<D>(lane), tbase = tr_base<D>(lane);
+  const Bases<D> lb = bases<D>(lane);
 
   t8_t kf[KS], vf[KS];
   load_frags<T, D>(kf, Kg + kslice, k0 + col, Nk, half);
   load_frags<T, D>(vf, Vg + kslice, k0 + col, Nk, half);
+  hold_loaded(kf, vf);
   f32x16_t dk[DT], dv[DT];
 #pragma unroll
   for (int t = 0; t < DT; ++t) dk[t] = dv[t] = f32x16_t{};
@@ -273,8 +367,8 @@ fa2_bwd_dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict_
     f32x16_t S = f32x16_t{}, dP = f32x16_t{};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      S = mfma32x32x16(row_frag<T, D>(qtile, rbase, 0, ks), kf[ks], S);
-      dP = mfma32x32x16(row_frag<T, D>(dtile, rbase, 0, ks), vf[ks], dP);
+      S = mfma32x32x16(row_frag<T, D>(qtile, lb, 0, ks), kf[ks], S);
+      dP = mfma32x32x16(row_frag<T, D>(dtile, lb, 0, ks), vf[ks], dP);
     }
     // This lane's key is k0 + col; accumulator r holds query
     // q_base + cr + 4*half with cr = 8*(r/4) + r%4 (a constant).  The query is
@@ -304,8 +398,8 @@ fa2_bwd_dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict_
     for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int t = 0; t < DT; ++t) {
-        dv[t] = mfma32x32x16(tr_frag<T, D>(dtile, tbase, u, t), pb[u], dv[t]);
-        dk[t] = mfma32x32x16(tr_frag<T, D>(qtile, tbase, u, t), sb[u], dk[t]);
+        dv[t] = mfma32x32x16(tr_frag<T, D>(dtile, lb, u, t), pb[u], dv[t]);
+        dk[t] = mfma32x32x16(tr_frag<T, D>(qtile, lb, u, t), sb[u], dk[t]);
       }
   }
   store_rows<T, D>(dv, 1.f, dVg + kslice, k0, Nk, lane);
@@ -339,13 +433,15 @@ fa2_bwd_dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ 
   const int off = Nk - Nq;  // key j visible to query i when j <= i + off
   const int q0 = m * kRows + 32 * wave;
   const int qrow = q0 + col;
-  const uint32_t rbase = row_base<D>(lane), tbase = tr_base<D>(lane);
+  const Bases<D> lb = bases<D>(lane);
 
   t8_t qf[KS], df[KS];
   load_frags<T, D>(qf, Qg + qslice, qrow, Nq, half);
   load_frags<T, D>(df, dOg + qslice, qrow, Nq, half);
-  const float l2 = qrow < Nq ? Lg[(size_t)bh * Nq + qrow] * kLog2e : 0.f;
-  const float dd = qrow < Nq ? Dg[(size_t)bh * Nq + qrow] : 0.f;
+  float l2 = qrow < Nq ? Lg[(size_t)bh * Nq + qrow] * kLog2e : 0.f;
+  float dd = qrow < Nq ? Dg[(size_t)bh * Nq + qrow] : 0.f;
+  hold_loaded(qf, df);
+  asm volatile("" : "+v"(l2), "+v"(dd));
   f32x16_t dq[DT];
 #pragma unroll
   for (int t = 0; t < DT; ++t) dq[t] = f32x16_t{};
@@ -374,8 +470,8 @@ fa2_bwd_dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ 
       f32x16_t S = f32x16_t{}, dP = f32x16_t{};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        S = mfma32x32x16(row_frag<T, D>(kt_, rbase, 32 * kt, ks), qf[ks], S);
-        dP = mfma32x32x16(row_frag<T, D>(vt, rbase, 32 * kt, ks), df[ks], dP);
+        S = mfma32x32x16(row_frag<T, D>(kt_, lb, 32 * kt, ks), qf[ks], S);
+        dP = mfma32x32x16(row_frag<T, D>(vt, lb, 32 * kt, ks), df[ks], dP);
       }
       // This lane's query is qrow; accumulator r holds key
       // j*64 + 32*kt + cr + 4*half with cr = 8*(r/4) + r%4 (a constant),
@@ -397,7 +493,7 @@ fa2_bwd_dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ 
     for (int u = 0; u < 4; ++u)
 #pragma unroll
       for (int t = 0; t < DT; ++t)
-        dq[t] = mfma32x32x16(tr_frag<T, D>(kt_, tbase, u, t), sb[u], dq[t]);
+        dq[t] = mfma32x32x16(tr_frag<T, D>(kt_, lb, u, t), sb[u], dq[t]);
   }
   store_rows<T, D>(dq, scale, dQg + qslice, q0, Nq, lane);
 }
