@@ -458,7 +458,8 @@ fa2_status_t fa2_bwd_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d, 
   if (d != 64 && d != 128)
     return fail(FA2_ENOTSUP, "the backward pass supports d = 64 and 128 (d=%lld)", (long long)d);
   if (!bytes) return fail(FA2_EINVAL, "bytes is NULL");
-  *bytes = static_cast<size_t>(B * H * N * 4);  // D = rowsum(dO * O), float32 per row
+  // D = rowsum(dO * O) and L * log2(e), float32 per row, rows padded per head
+  *bytes = static_cast<size_t>(B * H * fa2::bwd_rows(N) * 8);
   return FA2_OK;
 }
 
@@ -487,9 +488,10 @@ fa2_status_t bwd_common(const void* Q, const void* K, const void* V, const void*
   if (B * H * (Nq + Nk) == 0) return FA2_OK;  // no element of dQ, dK or dV
 
   const int64_t qb = B * H * Nq * d * 2, kb = B * H * Nk * d * 2, lb = B * H * Nq * 4;
+  const int64_t wb = B * H * fa2::bwd_rows(Nq) * 8;
   constexpr int n = 10;
   const void* ptrs[n] = {Q, K, V, O, dO, L, dQ, dK, dV, workspace};
-  const int64_t sizes[n] = {qb, kb, kb, qb, qb, lb, qb, kb, kb, lb};
+  const int64_t sizes[n] = {qb, kb, kb, qb, qb, lb, qb, kb, kb, wb};
   const char* names[n] = {"Q", "K", "V", "O", "dO", "L", "dQ", "dK", "dV", "workspace"};
   for (int i = 0; i < n; ++i) {
     if (sizes[i] == 0) continue;
@@ -498,9 +500,9 @@ fa2_status_t bwd_common(const void* Q, const void* K, const void* V, const void*
     if (reinterpret_cast<uintptr_t>(ptrs[i]) % align != 0)
       return fail(FA2_EINVAL, "%s=%p is not %d-byte aligned", names[i], ptrs[i], (int)align);
   }
-  if (static_cast<int64_t>(workspace_bytes) < lb)
+  if (static_cast<int64_t>(workspace_bytes) < wb)
     return fail(FA2_EINVAL, "workspace of %llu bytes is smaller than the %lld bytes needed",
-                (unsigned long long)workspace_bytes, (long long)lb);
+                (unsigned long long)workspace_bytes, (long long)wb);
   for (int o = 6; o < n; ++o)  // outputs and workspace: disjoint from everything else
     for (int i = 0; i < n; ++i)
       if (i != o && sizes[o] > 0 && sizes[i] > 0 &&

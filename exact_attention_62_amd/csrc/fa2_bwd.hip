@@ -41,6 +41,8 @@
 
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "fa2_device.h"
 #include "fa2_internal.h"
 
@@ -68,36 +70,61 @@ __device__ __forceinline__ constexpr int toff(int r, int c) {
          64 * (((c >> 3) & 1) ^ ((r >> 3) & 1)) + 16 * (r & 3) + 2 * (c & 7);
 }
 
-// Stage rows [r0, r0 + ROWS) of a [N][D] 16-bit slice into LDS in the tile layout
-// (rows past N are clamped to row N - 1; callers mask them).  Load i of this
-// thread fills 1 KB chunk n = wave*LOADS + i: its lane L writes the 16 bytes at
-// slot L%8 of 128-byte block bk = 8n + L/8, which is segment position bk % NSEG
-// of row group g = bk / NSEG: row 4g + L%4, dims 16*((bk % NSEG) ^ (g%2)) +
-// 8*((L%8)/4 ^ (g/2)%2).
-template <int D, int ROWS = kStep>
-__device__ __forceinline__ void stage_tile(const uint16_t* head, int r0, int N, char* buf,
-                                           int wave, int lane) {
+// What the direct loads that stage a tile read.  Direct load n fills 1 KB
+// chunk n of the tile: its lane L writes the 16 bytes at slot L%8 of 128-byte
+// block bk = 8n + L/8, which is segment position bk % NSEG of row group
+// g = bk / NSEG: row 4g + L%4, dims 16*((bk % NSEG) ^ (g%2)) + 8*((L%8)/4 ^ (g/2)%2).
+// As 8n is a multiple of NSEG, the row is stage_row(n, 0) (uniform) plus a
+// part that depends on L only.
+template <int D>
+__device__ __forceinline__ constexpr int stage_row(int n, int L) {
+  return 4 * ((8 * n + L / 8) / (D / 16)) + L % 4;
+}
+template <int D>
+__device__ __forceinline__ constexpr int stage_col(int n, int L) {
   constexpr int NSEG = D / 16;
+  const int bk = 8 * n + L / 8, g = bk / NSEG;
+  return 16 * ((bk % NSEG) ^ (g & 1)) + 8 * (((L % 8) / 4) ^ ((g >> 1) & 1));
+}
+
+// Stage rows [r0, r0 + ROWS) of a [N][D] 16-bit slice into LDS in the tile
+// layout; load i of this thread is direct load n = wave*LOADS + i.  With CLAMP,
+// rows past N are clamped to row N - 1 (callers mask them); without, every row
+// must exist, and each load is a scalar base (the row stage_row(n, 0)) plus a
+// per-lane byte offset.
+template <int D, int ROWS, bool CLAMP>
+__device__ __forceinline__ void stage_tile(const uint16_t* head, int r0, int N, char* buf,
+                                           int wave) {
   constexpr int LOADS = ROWS * D * 2 / 1024 / kWaves;
   static_assert(LOADS >= 1 && ROWS * D * 2 % (1024 * kWaves) == 0, "tile splits over the waves");
-  lane = fresh_lane();  // recomputed here: not kept in registers across the loop
+  const int lane = fresh_lane();  // recomputed here: not kept in registers across the loop
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
     const int n = wave * LOADS + i;
-    const int bk = 8 * n + lane / 8;
-    const int g = bk / NSEG;
-    const int r = min(r0 + 4 * g + lane % 4, N - 1);
-    const int c = 16 * ((bk % NSEG) ^ (g & 1)) + 8 * (((lane % 8) / 4) ^ ((g >> 1) & 1));
-    lds_dma(head + (size_t)r * D + c, lds_addr(buf + n * 1024));
+    if constexpr (CLAMP) {
+      const int r = min(r0 + stage_row<D>(n, lane), N - 1);
+      lds_dma(head + (size_t)r * D + stage_col<D>(n, lane), lds_addr(buf + n * 1024));
+    } else {
+      const uint32_t voff =
+          (uint32_t)(((stage_row<D>(n, lane) - stage_row<D>(n, 0)) * D + stage_col<D>(n, lane)) * 2);
+      lds_dma(head + (size_t)(r0 + stage_row<D>(n, 0)) * D, voff, lds_addr(buf + n * 1024));
+    }
   }
 }
 
-// Stage 64 floats v[r0 .. r0+64) (clamped to index N - 1) into LDS: one
-// 4-byte direct load per lane.
-__device__ __forceinline__ void stage_vec(const float* v, int r0, int N, char* buf, int lane) {
-  const float* src = v + min(r0 + lane, N - 1);
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
-               : : "s"(lds_addr(buf)), "v"(src) : "memory", "m0");
+// Stage 64 floats v[r0 .. r0+64) into LDS: one 4-byte direct load per lane.
+// With CLAMP the index is clamped to N - 1; without, all 64 must exist.
+template <bool CLAMP>
+__device__ __forceinline__ void stage_vec(const float* v, int r0, int N, char* buf) {
+  const int lane = fresh_lane();
+  if constexpr (CLAMP) {
+    const float* src = v + min(r0 + lane, N - 1);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
+                 : : "s"(lds_addr(buf)), "v"(src) : "memory", "m0");
+  } else {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
+                 : : "s"(lds_addr(buf)), "v"((uint32_t)(4 * lane)), "s"(v + r0) : "memory", "m0");
+  }
 }
 
 // LDS addresses of fragments in a staged tile, as two per-lane bases (computed
@@ -166,12 +193,10 @@ __device__ __forceinline__ typename Vec16<T>::x8 tr_frag(const char* tile, const
 // distinct 8-byte slots of one 128-byte span.
 template <int D, int ROWS>
 __device__ __forceinline__ constexpr bool tile_layout_ok() {
-  constexpr int NSEG = D / 16;
   for (int n = 0; n < ROWS * D * 2 / 1024; ++n)
     for (int L = 0; L < 64; ++L) {
-      const int bk = 8 * n + L / 8, g = bk / NSEG;
-      const int r = 4 * g + L % 4;
-      const int c = 16 * ((bk % NSEG) ^ (g & 1)) + 8 * (((L % 8) / 4) ^ ((g >> 1) & 1));
+      const int r = stage_row<D>(n, L), c = stage_col<D>(n, L);
+      if (r - stage_row<D>(n, 0) != r % 4 + 4 * ((L / 8) / (D / 16))) return false;
       for (int k = 0; k < 8; ++k)
         if (toff<D>(r, c + k) != n * 1024 + 16 * L + 2 * k) return false;
     }
@@ -211,6 +236,7 @@ __device__ __forceinline__ constexpr bool tile_layout_ok() {
 }
 static_assert(tile_layout_ok<64, 32>() && tile_layout_ok<64, 64>(), "tile layout, d = 64");
 static_assert(tile_layout_ok<128, 32>() && tile_layout_ok<128, 64>(), "tile layout, d = 128");
+static_assert(tile_layout_ok<64, 128>() && tile_layout_ok<128, 128>(), "tile layout, 128 rows");
 
 // B operand fragments of a [N][D] 16-bit slice held in registers: for k-step ks,
 // lane l holds row r0 + l%32, dims 16*ks + 8*(l/32) .. +8 (zero past N).
@@ -276,24 +302,34 @@ __device__ __forceinline__ int xcd_block(int id, int G) {
 }
 
 // ---------------------------------------------------------------- D = rowsum(dO * O)
+// Rows are padded per head to Npad (a multiple of the dK/dV kernel's query
+// step): padded rows get D = 0 and L*log2(e) = +inf, so exp2(c*S - L*log2(e))
+// is 0 there and the dK/dV kernel needs no test for queries past Nq.
 template <typename T, int D>
 __global__ void __launch_bounds__(kThreads)
 fa2_bwd_prep_kernel(const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO,
-                    float* __restrict__ Dv, int rows) {
+                    const float* __restrict__ L, float* __restrict__ Dv, float* __restrict__ L2v,
+                    int Nq, int Npad, int rows) {
   typedef typename Vec16<T>::x8 t8_t;
   constexpr int TPR = D / 8;  // threads per row, 8 dims each
   const int row = blockIdx.x * (kThreads / TPR) + threadIdx.x / TPR;
   const int t = threadIdx.x % TPR;
+  const int bh = row / Npad, q = row - bh * Npad;
+  const bool valid = row < rows && q < Nq;
+  const size_t src = (size_t)bh * Nq + q;
   float acc = 0.f;
-  if (row < rows) {
-    const t8_t o = *(const t8_t*)(O + (size_t)row * D + 8 * t);
-    const t8_t g = *(const t8_t*)(dO + (size_t)row * D + 8 * t);
+  if (valid) {
+    const t8_t o = *(const t8_t*)(O + src * D + 8 * t);
+    const t8_t g = *(const t8_t*)(dO + src * D + 8 * t);
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc += (float)o[i] * (float)g[i];
   }
 #pragma unroll
   for (int m = TPR / 2; m >= 1; m /= 2) acc += __shfl_xor(acc, m, 64);
-  if (row < rows && t == 0) Dv[row] = acc;
+  if (row < rows && t == 0) {
+    Dv[row] = acc;
+    L2v[row] = valid ? L[src] * kLog2e : __builtin_inff();
+  }
 }
 
 // ---------------------------------------------------------------- dK, dV
@@ -306,9 +342,9 @@ template <typename T, int D, bool CAUSAL>
 __global__ void __launch_bounds__(kThreads, 2)
 fa2_bwd_dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
                     const uint16_t* __restrict__ Vg, const uint16_t* __restrict__ dOg,
-                    const float* __restrict__ Lg, const float* __restrict__ Dg,
+                    const float* __restrict__ L2g, const float* __restrict__ Dg,
                     uint16_t* __restrict__ dKg, uint16_t* __restrict__ dVg, int Nq, int Nk,
-                    int num_k_block, float c, float scale) {
+                    int Npad, int num_k_block, float c, float scale) {
   typedef typename Vec16<T>::x8 t8_t;
   constexpr int KS = D / 16, DT = D / 32;
   constexpr int TILE = kQStep * D * 2;  // bytes of one staged [32][D] tile
@@ -325,7 +361,8 @@ fa2_bwd_dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict_
   const int bh = blk / num_k_block;
   const size_t qslice = (size_t)bh * Nq * D, kslice = (size_t)bh * Nk * D;
   const uint16_t *Qh = Qg + qslice, *dOh = dOg + qslice;
-  const float *Lh = Lg + (size_t)bh * Nq, *Dh = Dg + (size_t)bh * Nq;
+  // L*log2(e) and D, Npad rows per head (padded rows: +inf and 0).
+  const float *Lh = L2g + (size_t)bh * Npad, *Dh = Dg + (size_t)bh * Npad;
   const int off = Nk - Nq;                // key j visible to query i when j <= i + off
   const int k0 = kb * kRows + 32 * wave;  // this wavefront's first key
   const Bases<D> lb = bases<D>(lane);
@@ -346,18 +383,21 @@ fa2_bwd_dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict_
   const int i_beg = CAUSAL ? (first_q > 0 ? first_q / kQStep : 0) : 0;
   const int i_end = (Nq + kQStep - 1) / kQStep;
   auto buf = [&](int i) { return smem + (i & 1) * (2 * TILE + 512); };
-  auto stage = [&](int i) {
+  // Only the first step walked (the last one) can reach past Nq; the others are
+  // staged with scalar bases and no clamping.
+  auto stage = [&](int i, auto clamp) {
+    constexpr bool C = decltype(clamp)::value;
     char* b = buf(i);
-    stage_tile<D, kQStep>(Qh, i * kQStep, Nq, b, wave, lane);
-    stage_tile<D, kQStep>(dOh, i * kQStep, Nq, b + TILE, wave, lane);
-    if (wave == 0) stage_vec(Lh, i * kQStep, Nq, b + 2 * TILE, lane);
-    if (wave == 1) stage_vec(Dh, i * kQStep, Nq, b + 2 * TILE + 256, lane);
+    stage_tile<D, kQStep, C>(Qh, i * kQStep, Nq, b, wave);
+    stage_tile<D, kQStep, C>(dOh, i * kQStep, Nq, b + TILE, wave);
+    if (wave == 0) stage_vec<C>(Lh, i * kQStep, Npad, b + 2 * TILE);
+    if (wave == 1) stage_vec<C>(Dh, i * kQStep, Npad, b + 2 * TILE + 256);
   };
-  if (i_beg < i_end) stage(i_end - 1);
+  if (i_beg < i_end) stage(i_end - 1, std::true_type{});
   for (int i = i_end - 1; i >= i_beg; --i) {
     wait_vmcnt<0>();
     lds_barrier();
-    if (i > i_beg) stage(i - 1);
+    if (i > i_beg) stage(i - 1, std::false_type{});
     const char* b = buf(i);
     const char* qtile = b;
     const char* dtile = b + TILE;
@@ -371,14 +411,14 @@ fa2_bwd_dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict_
       dP = mfma32x32x16(row_frag<T, D>(dtile, lb, 0, ks), vf[ks], dP);
     }
     // This lane's key is k0 + col; accumulator r holds query
-    // q_base + cr + 4*half with cr = 8*(r/4) + r%4 (a constant).  The query is
-    // visible to the key when lo <= cr < hi (key <= query + off, query < Nq);
-    // steps whose queries all see every key of the wavefront and lie before
-    // Nq need no test (uniform for the wavefront).  A query that sees no key
-    // at all has L = -inf; every one of its entries is masked.
-    const bool clean = q_base + kQStep <= Nq && (!CAUSAL || q_base + off >= k0 + 31);
-    const int lo = CAUSAL ? k0 + col - off - q_base - 4 * half : -1;
-    const int hi = Nq - q_base - 4 * half;
+    // q_base + cr + 4*half with cr = 8*(r/4) + r%4 (a constant).  With the
+    // causal mask the query is visible to the key when cr >= lo
+    // (key <= query + off); steps whose queries all see every key of the
+    // wavefront need no test (uniform for the wavefront).  A query that sees
+    // no key at all has L = -inf; every one of its entries is masked.  Queries
+    // past Nq have L*log2(e) = +inf and so P = 0.
+    const bool clean = !CAUSAL || q_base + off >= k0 + 31;
+    const int lo = k0 + col - off - q_base - 4 * half;
     t8_t pb[2], sb[2];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
@@ -388,8 +428,8 @@ fa2_bwd_dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict_
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int cr = 8 * g + r;
-        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(S[g * 4 + r], c, -L4[r] * kLog2e));
-        if (!clean) p = (cr < lo || cr >= hi) ? 0.f : p;
+        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(S[g * 4 + r], c, -L4[r]));
+        if (!clean) p = cr < lo ? 0.f : p;
         pb[g / 2][(g % 2) * 4 + r] = (T)p;
         sb[g / 2][(g % 2) * 4 + r] = (T)(p * (dP[g * 4 + r] - D4[r]));
       }
@@ -411,8 +451,8 @@ template <typename T, int D, bool CAUSAL>
 __global__ void __launch_bounds__(kThreads, 2)
 fa2_bwd_dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
                   const uint16_t* __restrict__ Vg, const uint16_t* __restrict__ dOg,
-                  const float* __restrict__ Lg, const float* __restrict__ Dg,
-                  uint16_t* __restrict__ dQg, int Nq, int Nk, int num_m_block, float c,
+                  const float* __restrict__ L2g, const float* __restrict__ Dg,
+                  uint16_t* __restrict__ dQg, int Nq, int Nk, int Npad, int num_m_block, float c,
                   float scale) {
   typedef typename Vec16<T>::x8 t8_t;
   constexpr int KS = D / 16, DT = D / 32;
@@ -438,8 +478,9 @@ fa2_bwd_dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ 
   t8_t qf[KS], df[KS];
   load_frags<T, D>(qf, Qg + qslice, qrow, Nq, half);
   load_frags<T, D>(df, dOg + qslice, qrow, Nq, half);
-  float l2 = qrow < Nq ? Lg[(size_t)bh * Nq + qrow] * kLog2e : 0.f;
-  float dd = qrow < Nq ? Dg[(size_t)bh * Nq + qrow] : 0.f;
+  // L*log2(e) and D of this lane's query (Npad rows per head).
+  float l2 = qrow < Nq ? L2g[(size_t)bh * Npad + qrow] : 0.f;
+  float dd = qrow < Nq ? Dg[(size_t)bh * Npad + qrow] : 0.f;
   hold_loaded(qf, df);
   asm volatile("" : "+v"(l2), "+v"(dd));
   f32x16_t dq[DT];
@@ -453,8 +494,8 @@ fa2_bwd_dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ 
   const int j_end = CAUSAL ? (last_key < 0 ? 0 : min(last_key / kStep + 1, nkb)) : nkb;
   auto buf = [&](int j) { return smem + (j & 1) * (2 * TILE); };
   auto stage = [&](int j) {
-    stage_tile<D>(Kh, j * kStep, Nk, buf(j), wave, lane);
-    stage_tile<D>(Vh, j * kStep, Nk, buf(j) + TILE, wave, lane);
+    stage_tile<D, kStep, true>(Kh, j * kStep, Nk, buf(j), wave);
+    stage_tile<D, kStep, true>(Vh, j * kStep, Nk, buf(j) + TILE, wave);
   };
   if (j_end > 0) stage(0);
   for (int j = 0; j < j_end; ++j) {
@@ -501,26 +542,29 @@ fa2_bwd_dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ 
 template <typename T, int D, bool CAUSAL>
 hipError_t launch(const BwdArgs& a) {
   const float c = a.scale * kLog2e;
-  const int qrows = a.BH * a.Nq;
+  const int Npad = (int)bwd_rows(a.Nq);
+  const int qrows = a.BH * Npad;
+  float* L2v = a.Dvec + (size_t)qrows;
   constexpr int RPB = kThreads / (D / 8);
   // Kernels with nothing to do are not launched: no queries leaves dK = dV = 0
   // (written by the dK/dV kernel, which then walks no query step); no keys
   // leaves dQ = 0 (written by the dQ kernel, which then walks no key block).
   if (qrows > 0)
     hipLaunchKernelGGL((fa2_bwd_prep_kernel<T, D>), dim3((qrows + RPB - 1) / RPB), dim3(kThreads),
-                       0, a.stream, (const uint16_t*)a.O, (const uint16_t*)a.dO, a.Dvec, qrows);
+                       0, a.stream, (const uint16_t*)a.O, (const uint16_t*)a.dO, a.L, a.Dvec, L2v,
+                       a.Nq, Npad, qrows);
   const int nkb = (a.Nk + kRows - 1) / kRows;
   if (nkb * a.BH > 0)
     hipLaunchKernelGGL((fa2_bwd_dkdv_kernel<T, D, CAUSAL>), dim3(nkb * a.BH), dim3(kThreads), 0,
                        a.stream, (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V,
-                       (const uint16_t*)a.dO, a.L, a.Dvec, (uint16_t*)a.dK, (uint16_t*)a.dV, a.Nq,
-                       a.Nk, nkb, c, a.scale);
+                       (const uint16_t*)a.dO, L2v, a.Dvec, (uint16_t*)a.dK, (uint16_t*)a.dV, a.Nq,
+                       a.Nk, Npad, nkb, c, a.scale);
   const int nmb = (a.Nq + kRows - 1) / kRows;
   if (nmb * a.BH > 0)
     hipLaunchKernelGGL((fa2_bwd_dq_kernel<T, D, CAUSAL>), dim3(nmb * a.BH), dim3(kThreads), 0,
                        a.stream, (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V,
-                       (const uint16_t*)a.dO, a.L, a.Dvec, (uint16_t*)a.dQ, a.Nq, a.Nk, nmb, c,
-                       a.scale);
+                       (const uint16_t*)a.dO, L2v, a.Dvec, (uint16_t*)a.dQ, a.Nq, a.Nk, Npad, nmb,
+                       c, a.scale);
   return hipGetLastError();
 }
 

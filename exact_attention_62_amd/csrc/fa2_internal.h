@@ -52,7 +52,7 @@ struct BwdArgs {
   void* dQ;
   void* dK;
   void* dV;
-  float* Dvec;  // workspace: rowsum(dO * O), [BH][Nq]
+  float* Dvec;  // workspace: rowsum(dO * O), [BH][bwd_rows(Nq)], then L * log2(e), same shape
   int BH, Nq, Nk, d, causal;  // causal aligned bottom-right when Nq != Nk
   float scale;
   int elem;  // Elem of Q, K, V, O, dO and the gradients (bf16 or fp16)
@@ -73,5 +73,8 @@ hipError_t launch_combine(const FwdArgs& a);
 hipError_t launch_fill_no_keys(const FwdArgs& a);
 // Enqueue the backward pass (three kernels) on a.stream.
 hipError_t launch_bwd(const BwdArgs& a);
+// Rows per head of the backward workspace's two arrays: Nq rounded up to the
+// dK/dV kernel's 32-query step (padded rows hold D = 0 and L * log2(e) = +inf).
+constexpr int64_t bwd_rows(int64_t Nq) { return (Nq + 31) / 32 * 32; }
 
 }  // namespace fa2

@@ -258,8 +258,8 @@ const char* fa2_strerror(fa2_status_t status);
  *   d                64 or 128 (others: FA2_ENOTSUP).
  *   dtype            FA2_BF16 or FA2_FP16 (FA2_FP32: FA2_ENOTSUP).
  *   workspace        device memory owned by the caller, 4-byte aligned, at least
- *                    fa2_bwd_workspace_size() bytes (it receives D); contents on
- *                    entry do not matter.  workspace_bytes is its size.
+ *                    fa2_bwd_workspace_size() bytes (it receives D and L*log2(e));
+ *                    contents on entry do not matter.  workspace_bytes is its size.
  * The outputs and the workspace must not overlap each other or any input.
  * Every element of dQ, dK and dV is written; results are deterministic.
  */
@@ -275,7 +275,7 @@ fa2_status_t fa2_bwd(const void* Q, const void* K, const void* V, const void* O,
  * j <= i + Nk - Nq).  A query that sees no key adds nothing (its dQ row is 0),
  * and a key no query sees gets dK = dV = 0.  Arrays of zero size may be NULL.
  * Everything else as for fa2_bwd; the workspace holds one float32 per query
- * row (fa2_bwd_workspace_size with N = Nq).
+ * row, padded (fa2_bwd_workspace_size with N = Nq).
  */
 fa2_status_t fa2_bwd_cross(const void* Q, const void* K, const void* V, const void* O,
                            const void* dO, const float* L, void* dQ, void* dK, void* dV,
@@ -284,8 +284,10 @@ fa2_status_t fa2_bwd_cross(const void* Q, const void* K, const void* V, const vo
                            size_t workspace_bytes, void* stream);
 
 /*
- * fa2_bwd_workspace_size - bytes of workspace fa2_bwd needs: B*H*N * 4 (one
- * float32 per query row; N = Nq for fa2_bwd_cross).  Host-only: makes no HIP
+ * fa2_bwd_workspace_size - bytes of workspace fa2_bwd needs: B*H*N32 * 8 with
+ * N32 = N rounded up to a multiple of 32 (two float32 arrays, D = rowsum(dO*O)
+ * and L*log2(e), with each head's rows padded to N32; N = Nq for
+ * fa2_bwd_cross).  Host-only: makes no HIP
  * call.  Returns the size and head dimension errors fa2_bwd would.
  */
 fa2_status_t fa2_bwd_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d, size_t* bytes);

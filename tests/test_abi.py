@@ -259,7 +259,11 @@ def _bwd(dtype=F.FA2_BF16, ws_bytes=1 << 16, **kw):
 
 
 def test_bwd_workspace_size_formula():
-    assert F.fa2_bwd_workspace_size(2, 4, 1024, 64) == 2 * 4 * 1024 * 4
+    # two float32 arrays (D and L*log2 e), each head's rows padded to a multiple of 32
+    assert F.fa2_bwd_workspace_size(2, 4, 1024, 64) == 2 * 4 * 1024 * 8
+    assert F.fa2_bwd_workspace_size(2, 4, 1000, 64) == 2 * 4 * 1024 * 8
+    assert F.fa2_bwd_workspace_size(1, 3, 33, 128) == 3 * 64 * 8
+    assert F.fa2_bwd_workspace_size(1, 1, 0, 128) == 0
     with pytest.raises(F.FA2Error) as e:
         F.fa2_bwd_workspace_size(1, 1, 16, 256)
     assert e.value.status == F.FA2_ENOTSUP
