@@ -458,7 +458,7 @@ fa2_status_t fa2_bwd_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d, 
   if (d != 64 && d != 128)
     return fail(FA2_ENOTSUP, "the backward pass supports d = 64 and 128 (d=%lld)", (long long)d);
   if (!bytes) return fail(FA2_EINVAL, "bytes is NULL");
-  // D = rowsum(dO * O) and L * log2(e), float32 per row, rows padded per head
+  // -D = -rowsum(dO * O) and L * log2(e), float32 per row, rows padded per head
   *bytes = static_cast<size_t>(B * H * fa2::bwd_rows(N) * 8);
   return FA2_OK;
 }

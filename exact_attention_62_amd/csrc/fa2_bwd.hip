@@ -262,6 +262,12 @@ __device__ __forceinline__ void hold_loaded(V (&a)[KS], V (&b)[KS]) {
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(a[ks]), "+v"(b[ks]));
 }
+template <typename V, int KS>
+__device__ __forceinline__ void hold_loaded(V (&a)[KS]) {
+  wait_vmcnt<0>();
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(a[ks]));
+}
 
 // Store a transposed accumulator (DT tiles of 32 dims x 32 rows; lane = row)
 // times `mul` as rows [row0, row0+32) of a [N][D] slice of type T, through a
@@ -302,9 +308,11 @@ __device__ __forceinline__ int xcd_block(int id, int G) {
 }
 
 // ---------------------------------------------------------------- D = rowsum(dO * O)
-// Rows are padded per head to Npad (a multiple of the dK/dV kernel's query
-// step): padded rows get D = 0 and L*log2(e) = +inf, so exp2(c*S - L*log2(e))
-// is 0 there and the dK/dV kernel needs no test for queries past Nq.
+// Writes -D (the dK/dV kernel starts its dP accumulators from it) and
+// L*log2(e).  Rows are padded per head to Npad (a multiple of the dK/dV
+// kernel's query step): padded rows get D = 0 and L*log2(e) = +inf, so
+// exp2(c*S - L*log2(e)) is 0 there and the dK/dV kernel needs no test for
+// queries past Nq.
 template <typename T, int D>
 __global__ void __launch_bounds__(kThreads)
 fa2_bwd_prep_kernel(const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO,
@@ -327,7 +335,7 @@ fa2_bwd_prep_kernel(const uint16_t* __restrict__ O, const uint16_t* __restrict__
 #pragma unroll
   for (int m = TPR / 2; m >= 1; m /= 2) acc += __shfl_xor(acc, m, 64);
   if (row < rows && t == 0) {
-    Dv[row] = acc;
+    Dv[row] = -acc;
     L2v[row] = valid ? L[src] * kLog2e : __builtin_inff();
   }
 }
@@ -348,8 +356,10 @@ fa2_bwd_dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict_
   typedef typename Vec16<T>::x8 t8_t;
   constexpr int KS = D / 16, DT = D / 32;
   constexpr int TILE = kQStep * D * 2;  // bytes of one staged [32][D] tile
-  // Q, dO tiles, then 64 L and 64 D values (32 used), for two steps.
+  // Q, dO tiles, then 64 L and 64 D values (32 used), for two steps; and the
+  // block's V rows (the B operand of dP), staged once.
   __shared__ __attribute__((aligned(1024))) char smem[2 * (2 * TILE + 512)];
+  __shared__ __attribute__((aligned(1024))) char vtile[kRows * D * 2];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -367,10 +377,11 @@ fa2_bwd_dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict_
   const int k0 = kb * kRows + 32 * wave;  // this wavefront's first key
   const Bases<D> lb = bases<D>(lane);
 
-  t8_t kf[KS], vf[KS];
+  // K fragments stay in registers (the B operand of S); V is read from LDS,
+  // which leaves registers for the dP accumulators to start from -D.
+  t8_t kf[KS];
   load_frags<T, D>(kf, Kg + kslice, k0 + col, Nk, half);
-  load_frags<T, D>(vf, Vg + kslice, k0 + col, Nk, half);
-  hold_loaded(kf, vf);
+  hold_loaded(kf);
   f32x16_t dk[DT], dv[DT];
 #pragma unroll
   for (int t = 0; t < DT; ++t) dk[t] = dv[t] = f32x16_t{};
@@ -393,7 +404,11 @@ fa2_bwd_dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict_
     if (wave == 0) stage_vec<C>(Lh, i * kQStep, Npad, b + 2 * TILE);
     if (wave == 1) stage_vec<C>(Dh, i * kQStep, Npad, b + 2 * TILE + 256);
   };
-  if (i_beg < i_end) stage(i_end - 1, std::true_type{});
+  if (i_beg < i_end) {
+    // Rows past Nk are clamped copies: their dK and dV rows are never stored.
+    stage_tile<D, kRows, true>(Vg + kslice, kb * kRows, Nk, vtile, wave);
+    stage(i_end - 1, std::true_type{});
+  }
   for (int i = i_end - 1; i >= i_beg; --i) {
     wait_vmcnt<0>();
     lds_barrier();
@@ -404,11 +419,20 @@ fa2_bwd_dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict_
     const float* lv = (const float*)(b + 2 * TILE);
     const float* dvec = (const float*)(b + 2 * TILE + 256);
     const int q_base = i * kQStep;
-    f32x16_t S = f32x16_t{}, dP = f32x16_t{};
+    // dP starts from -D of each accumulator's query (the workspace holds -D),
+    // so the products leave dP - D in it.
+    f32x16_t S = f32x16_t{}, dP;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4_t D4 = *(const f32x4_t*)(dvec + 8 * g + 4 * half);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dP[g * 4 + r] = D4[r];
+    }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       S = mfma32x32x16(row_frag<T, D>(qtile, lb, 0, ks), kf[ks], S);
-      dP = mfma32x32x16(row_frag<T, D>(dtile, lb, 0, ks), vf[ks], dP);
+      dP = mfma32x32x16(row_frag<T, D>(dtile, lb, 0, ks), row_frag<T, D>(vtile, lb, 32 * wave, ks),
+                        dP);
     }
     // This lane's key is k0 + col; accumulator r holds query
     // q_base + cr + 4*half with cr = 8*(r/4) + r%4 (a constant).  With the
@@ -424,14 +448,13 @@ fa2_bwd_dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict_
     for (int g = 0; g < 4; ++g) {
       const int qr = 8 * g + 4 * half;  // first of 4 consecutive queries
       const f32x4_t L4 = *(const f32x4_t*)(lv + qr);
-      const f32x4_t D4 = *(const f32x4_t*)(dvec + qr);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int cr = 8 * g + r;
         float p = __builtin_amdgcn_exp2f(__builtin_fmaf(S[g * 4 + r], c, -L4[r]));
         if (!clean) p = cr < lo ? 0.f : p;
         pb[g / 2][(g % 2) * 4 + r] = (T)p;
-        sb[g / 2][(g % 2) * 4 + r] = (T)(p * (dP[g * 4 + r] - D4[r]));
+        sb[g / 2][(g % 2) * 4 + r] = (T)(p * dP[g * 4 + r]);
       }
     }
 #pragma unroll
@@ -480,7 +503,7 @@ fa2_bwd_dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ 
   load_frags<T, D>(df, dOg + qslice, qrow, Nq, half);
   // L*log2(e) and D of this lane's query (Npad rows per head).
   float l2 = qrow < Nq ? L2g[(size_t)bh * Npad + qrow] : 0.f;
-  float dd = qrow < Nq ? Dg[(size_t)bh * Npad + qrow] : 0.f;
+  float dd = qrow < Nq ? -Dg[(size_t)bh * Npad + qrow] : 0.f;
   hold_loaded(qf, df);
   asm volatile("" : "+v"(l2), "+v"(dd));
   f32x16_t dq[DT];

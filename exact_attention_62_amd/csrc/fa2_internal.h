@@ -52,7 +52,7 @@ struct BwdArgs {
   void* dQ;
   void* dK;
   void* dV;
-  float* Dvec;  // workspace: rowsum(dO * O), [BH][bwd_rows(Nq)], then L * log2(e), same shape
+  float* Dvec;  // workspace: -rowsum(dO * O), [BH][bwd_rows(Nq)], then L * log2(e), same shape
   int BH, Nq, Nk, d, causal;  // causal aligned bottom-right when Nq != Nk
   float scale;
   int elem;  // Elem of Q, K, V, O, dO and the gradients (bf16 or fp16)

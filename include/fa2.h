@@ -258,7 +258,7 @@ const char* fa2_strerror(fa2_status_t status);
  *   d                64 or 128 (others: FA2_ENOTSUP).
  *   dtype            FA2_BF16 or FA2_FP16 (FA2_FP32: FA2_ENOTSUP).
  *   workspace        device memory owned by the caller, 4-byte aligned, at least
- *                    fa2_bwd_workspace_size() bytes (it receives D and L*log2(e));
+ *                    fa2_bwd_workspace_size() bytes (it receives -D and L*log2(e));
  *                    contents on entry do not matter.  workspace_bytes is its size.
  * The outputs and the workspace must not overlap each other or any input.
  * Every element of dQ, dK and dV is written; results are deterministic.
@@ -285,7 +285,7 @@ fa2_status_t fa2_bwd_cross(const void* Q, const void* K, const void* V, const vo
 
 /*
  * fa2_bwd_workspace_size - bytes of workspace fa2_bwd needs: B*H*N32 * 8 with
- * N32 = N rounded up to a multiple of 32 (two float32 arrays, D = rowsum(dO*O)
+ * N32 = N rounded up to a multiple of 32 (two float32 arrays, -D = -rowsum(dO*O)
  * and L*log2(e), with each head's rows padded to N32; N = Nq for
  * fa2_bwd_cross).  Host-only: makes no HIP
  * call.  Returns the size and head dimension errors fa2_bwd would.
