@@ -501,11 +501,16 @@ fa2_bwd_dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ 
   t8_t qf[KS], df[KS];
   load_frags<T, D>(qf, Qg + qslice, qrow, Nq, half);
   load_frags<T, D>(df, dOg + qslice, qrow, Nq, half);
-  // L*log2(e) and D of this lane's query (Npad rows per head).
+  // L*log2(e) and -D of this lane's query (Npad rows per head).
   float l2 = qrow < Nq ? L2g[(size_t)bh * Npad + qrow] : 0.f;
-  float dd = qrow < Nq ? -Dg[(size_t)bh * Npad + qrow] : 0.f;
+  float dd = qrow < Nq ? Dg[(size_t)bh * Npad + qrow] : 0.f;  // -D
   hold_loaded(qf, df);
   asm volatile("" : "+v"(l2), "+v"(dd));
+  // Every dP accumulator starts from -D of the lane's query, so the products
+  // leave dP - D in it (one register tile, held across the loop).
+  f32x16_t neg_d;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) neg_d[r] = dd;
   f32x16_t dq[DT];
 #pragma unroll
   for (int t = 0; t < DT; ++t) dq[t] = f32x16_t{};
@@ -516,9 +521,16 @@ fa2_bwd_dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ 
   const int last_key = min(Nq, (m + 1) * kRows) - 1 + off;
   const int j_end = CAUSAL ? (last_key < 0 ? 0 : min(last_key / kStep + 1, nkb)) : nkb;
   auto buf = [&](int j) { return smem + (j & 1) * (2 * TILE); };
+  // Blocks wholly before Nk are staged with scalar bases; only a ragged last
+  // block needs clamped per-lane addresses.
   auto stage = [&](int j) {
-    stage_tile<D, kStep, true>(Kh, j * kStep, Nk, buf(j), wave);
-    stage_tile<D, kStep, true>(Vh, j * kStep, Nk, buf(j) + TILE, wave);
+    if ((j + 1) * kStep <= Nk) {
+      stage_tile<D, kStep, false>(Kh, j * kStep, Nk, buf(j), wave);
+      stage_tile<D, kStep, false>(Vh, j * kStep, Nk, buf(j) + TILE, wave);
+    } else {
+      stage_tile<D, kStep, true>(Kh, j * kStep, Nk, buf(j), wave);
+      stage_tile<D, kStep, true>(Vh, j * kStep, Nk, buf(j) + TILE, wave);
+    }
   };
   if (j_end > 0) stage(0);
   for (int j = 0; j < j_end; ++j) {
@@ -531,7 +543,7 @@ fa2_bwd_dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ 
     t8_t sb[4];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      f32x16_t S = f32x16_t{}, dP = f32x16_t{};
+      f32x16_t S = f32x16_t{}, dP = neg_d;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         S = mfma32x32x16(row_frag<T, D>(kt_, lb, 32 * kt, ks), qf[ks], S);
@@ -550,7 +562,7 @@ fa2_bwd_dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ 
         const int cr = 8 * (r / 4) + (r % 4);
         float p = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], c, -l2));
         if (!clean) p = cr > th ? 0.f : p;
-        sb[kt * 2 + r / 8][r % 8] = (T)(p * (dP[r] - dd));
+        sb[kt * 2 + r / 8][r % 8] = (T)(p * dP[r]);
       }
     }
 #pragma unroll
