@@ -552,18 +552,20 @@ fa2_bwd_dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ 
       // This lane's query is qrow; accumulator r holds key
       // j*64 + 32*kt + cr + 4*half with cr = 8*(r/4) + r%4 (a constant),
       // visible when cr <= th (key <= query + off, key < Nk).  Blocks whose keys
-      // every query of the wavefront sees, before Nk, need no test; a query
-      // that sees no key (L = -inf) has every entry masked.
+      // every query of the wavefront sees, before Nk, skip the test (a branch
+      // that is uniform for the wavefront); a query that sees no key
+      // (L = -inf) has every entry masked.
       const int kb0 = j * kStep + 32 * kt + 4 * half;
       int th = Nk - 1 - kb0;
       if (CAUSAL) th = min(th, qrow + off - kb0);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int cr = 8 * (r / 4) + (r % 4);
-        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], c, -l2));
-        if (!clean) p = cr > th ? 0.f : p;
-        sb[kt * 2 + r / 8][r % 8] = (T)(p * dP[r]);
+      for (int r = 0; r < 16; ++r) S[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], c, -l2));
+      if (!clean) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) S[r] = 8 * (r / 4) + (r % 4) > th ? 0.f : S[r];
       }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sb[kt * 2 + r / 8][r % 8] = (T)(S[r] * dP[r]);
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u)
