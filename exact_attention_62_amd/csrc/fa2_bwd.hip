@@ -409,7 +409,8 @@ fa2_bwd_dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict_
     stage_tile<D, kRows, true>(Vg + kslice, kb * kRows, Nk, vtile, wave);
     stage(i_end - 1, std::true_type{});
   }
-  for (int i = i_end - 1; i >= i_beg; --i) {
+  auto step = [&](int i, auto mask_tag) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     wait_vmcnt<0>();
     lds_barrier();
     if (i > i_beg) stage(i - 1, std::false_type{});
@@ -438,10 +439,9 @@ fa2_bwd_dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict_
     // q_base + cr + 4*half with cr = 8*(r/4) + r%4 (a constant).  With the
     // causal mask the query is visible to the key when cr >= lo
     // (key <= query + off); steps whose queries all see every key of the
-    // wavefront need no test (uniform for the wavefront).  A query that sees
-    // no key at all has L = -inf; every one of its entries is masked.  Queries
-    // past Nq have L*log2(e) = +inf and so P = 0.
-    const bool clean = !CAUSAL || q_base + off >= k0 + 31;
+    // wavefront run without the test (MASK false).  A query that sees no key
+    // at all has L = -inf; every one of its entries is masked.  Queries past
+    // Nq have L*log2(e) = +inf and so P = 0.
     const int lo = k0 + col - off - q_base - 4 * half;
     t8_t pb[2], sb[2];
 #pragma unroll
@@ -452,7 +452,7 @@ fa2_bwd_dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict_
       for (int r = 0; r < 4; ++r) {
         const int cr = 8 * g + r;
         float p = __builtin_amdgcn_exp2f(__builtin_fmaf(S[g * 4 + r], c, -L4[r]));
-        if (!clean) p = cr < lo ? 0.f : p;
+        if constexpr (MASK) p = cr < lo ? 0.f : p;
         pb[g / 2][(g % 2) * 4 + r] = (T)p;
         sb[g / 2][(g % 2) * 4 + r] = (T)(p * dP[g * 4 + r]);
       }
@@ -464,7 +464,13 @@ fa2_bwd_dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict_
         dv[t] = mfma32x32x16(tr_frag<T, D>(dtile, lb, u, t), pb[u], dv[t]);
         dk[t] = mfma32x32x16(tr_frag<T, D>(qtile, lb, u, t), sb[u], dk[t]);
       }
-  }
+  };
+  // Steps from i_clean up see every key of this wavefront (q_base + off >= k0 + 31):
+  // they run without the mask; the rest (walked last) with it.
+  const int need = k0 + 31 - off;
+  const int i_clean = !CAUSAL ? i_beg : min(i_end, max(i_beg, need <= 0 ? 0 : (need + 31) / 32));
+  for (int i = i_end - 1; i >= i_clean; --i) step(i, std::false_type{});
+  for (int i = i_clean - 1; i >= i_beg; --i) step(i, std::true_type{});
   store_rows<T, D>(dv, 1.f, dVg + kslice, k0, Nk, lane);
   store_rows<T, D>(dk, scale, dKg + kslice, k0, Nk, lane);
 }
