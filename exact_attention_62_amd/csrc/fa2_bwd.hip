@@ -112,19 +112,47 @@ __device__ __forceinline__ void stage_tile(const uint16_t* head, int r0, int N, 
   }
 }
 
+// The per-lane byte offsets of stage_tile without CLAMP, computed once by a
+// kernel that keeps them in registers across its loop.
+template <int D, int ROWS>
+struct StageOffsets {
+  static constexpr int LOADS = ROWS * D * 2 / 1024 / kWaves;
+  uint32_t tile[LOADS];
+  uint32_t vec;  // 4 * lane, for stage_vec
+};
+template <int D, int ROWS>
+__device__ __forceinline__ StageOffsets<D, ROWS> stage_offsets(int wave) {
+  StageOffsets<D, ROWS> o;
+  const int lane = fresh_lane();
+#pragma unroll
+  for (int i = 0; i < o.LOADS; ++i) {
+    const int n = wave * o.LOADS + i;
+    o.tile[i] = (uint32_t)(((stage_row<D>(n, lane) - stage_row<D>(n, 0)) * D + stage_col<D>(n, lane)) * 2);
+  }
+  o.vec = (uint32_t)(4 * lane);
+  return o;
+}
+template <int D, int ROWS>
+__device__ __forceinline__ void stage_tile_at(const uint16_t* head, int r0, char* buf, int wave,
+                                              const StageOffsets<D, ROWS>& o) {
+#pragma unroll
+  for (int i = 0; i < o.LOADS; ++i) {
+    const int n = wave * o.LOADS + i;
+    lds_dma(head + (size_t)(r0 + stage_row<D>(n, 0)) * D, o.tile[i], lds_addr(buf + n * 1024));
+  }
+}
+
 // Stage 64 floats v[r0 .. r0+64) into LDS: one 4-byte direct load per lane.
 // With CLAMP the index is clamped to N - 1; without, all 64 must exist.
-template <bool CLAMP>
 __device__ __forceinline__ void stage_vec(const float* v, int r0, int N, char* buf) {
-  const int lane = fresh_lane();
-  if constexpr (CLAMP) {
-    const float* src = v + min(r0 + lane, N - 1);
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
-                 : : "s"(lds_addr(buf)), "v"(src) : "memory", "m0");
-  } else {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
-                 : : "s"(lds_addr(buf)), "v"((uint32_t)(4 * lane)), "s"(v + r0) : "memory", "m0");
-  }
+  const float* src = v + min(r0 + fresh_lane(), N - 1);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
+               : : "s"(lds_addr(buf)), "v"(src) : "memory", "m0");
+}
+// The same without clamping (all 64 must exist); voff = 4 * lane.
+__device__ __forceinline__ void stage_vec_at(const float* v, int r0, uint32_t voff, char* buf) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
+               : : "s"(lds_addr(buf)), "v"(voff), "s"(v + r0) : "memory", "m0");
 }
 
 // LDS addresses of fragments in a staged tile, as two per-lane bases (computed
@@ -395,14 +423,21 @@ fa2_bwd_dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict_
   const int i_end = (Nq + kQStep - 1) / kQStep;
   auto buf = [&](int i) { return smem + (i & 1) * (2 * TILE + 512); };
   // Only the first step walked (the last one) can reach past Nq; the others are
-  // staged with scalar bases and no clamping.
+  // staged with scalar bases, no clamping and per-lane offsets held in registers.
+  const StageOffsets<D, kQStep> so = stage_offsets<D, kQStep>(wave);
   auto stage = [&](int i, auto clamp) {
-    constexpr bool C = decltype(clamp)::value;
     char* b = buf(i);
-    stage_tile<D, kQStep, C>(Qh, i * kQStep, Nq, b, wave);
-    stage_tile<D, kQStep, C>(dOh, i * kQStep, Nq, b + TILE, wave);
-    if (wave == 0) stage_vec<C>(Lh, i * kQStep, Npad, b + 2 * TILE);
-    if (wave == 1) stage_vec<C>(Dh, i * kQStep, Npad, b + 2 * TILE + 256);
+    if constexpr (decltype(clamp)::value) {
+      stage_tile<D, kQStep, true>(Qh, i * kQStep, Nq, b, wave);
+      stage_tile<D, kQStep, true>(dOh, i * kQStep, Nq, b + TILE, wave);
+      if (wave == 0) stage_vec(Lh, i * kQStep, Npad, b + 2 * TILE);
+      if (wave == 1) stage_vec(Dh, i * kQStep, Npad, b + 2 * TILE + 256);
+    } else {
+      stage_tile_at<D, kQStep>(Qh, i * kQStep, b, wave, so);
+      stage_tile_at<D, kQStep>(dOh, i * kQStep, b + TILE, wave, so);
+      if (wave == 0) stage_vec_at(Lh, i * kQStep, so.vec, b + 2 * TILE);
+      if (wave == 1) stage_vec_at(Dh, i * kQStep, so.vec, b + 2 * TILE + 256);
+    }
   };
   if (i_beg < i_end) {
     // Rows past Nk are clamped copies: their dK and dV rows are never stored.
