@@ -312,6 +312,8 @@ def main(argv=None) -> int:
     c = "true" if causal else "false"
     if dtype == "fp32":
         kname = f"fa2_fwd_f32_kernel<{d}, {c}>"
+    elif Nq == 1 and d in (64, 128, 256):  # one query row per head: the decoding kernel
+        kname = f"fa2_decode_kernel<{KERNEL_TYPE[dtype]}, {d}>"
     else:
         kname = f"fa2_fwd_kernel<{KERNEL_TYPE[dtype]}, {d}, {c}, {'true' if splits else 'false'}>"
     if splits is not None:

@@ -206,6 +206,9 @@ fa2_status_t prepare(const void* Q, const void* K, const void* V, void* O, float
 
 hipError_t launch_fwd(const fa2::FwdArgs& a) {
   if (a.Nk == 0) return fa2::launch_fill_no_keys(a);  // every row's sum is empty
+  // One query row per head (decoding): the row sees every key, and the pass is
+  // bound by HBM; it has a kernel of its own.
+  if (a.Nq == 1 && fa2::decode_supported(a.d, a.elem)) return fa2::launch_decode(a);
   switch (a.elem) {
     case fa2::kBF16: return fa2::launch_fwd_bf16(a);
     case fa2::kFP16: return fa2::launch_fwd_fp16(a);

@@ -73,6 +73,11 @@ hipError_t launch_combine(const FwdArgs& a);
 hipError_t launch_fill_no_keys(const FwdArgs& a);
 // Enqueue the backward pass (three kernels) on a.stream.
 hipError_t launch_bwd(const BwdArgs& a);
+// One query per (batch, head): the decoding kernel (d = 64, 128, 256; bf16 or
+// fp16).  Plain (num_splits == 0: O and L) or partial (num_splits splits:
+// ws_O, ws_L in the split-KV layout).
+bool decode_supported(int d, int elem);
+hipError_t launch_decode(const FwdArgs& a);
 // Rows per head of the backward workspace's two arrays: Nq rounded up to the
 // dK/dV kernel's 32-query step (padded rows hold D = 0 and L * log2(e) = +inf).
 constexpr int64_t bwd_rows(int64_t Nq) { return (Nq + 31) / 32 * 32; }
