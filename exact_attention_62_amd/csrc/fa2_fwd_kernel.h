@@ -27,6 +27,13 @@
 // and light causal blocks balance.  While the last K/V block of an item is
 // processed, the next item's Q rows and first K/V blocks are already loading.
 //
+// Issue priority.  Two workgroups share each CU, and the SIMDs' arbitration
+// favours the older one: with the same number of blocks each, the younger
+// finished up to 15% later and then ran alone on its CU.  Each wavefront
+// therefore lowers its priority (s_setprio 3, 2, 1, 0) as its workgroup
+// passes each quarter of its blocks, so that the partner that is behind wins
+// the arbitration until it reaches the same quarter.
+//
 // Wavefront layout (the pages' split-Q warp scheme, re-derived for 64-wide
 // wavefronts and 32x32 MFMA tiles): each wavefront owns 32 query rows against
 // the shared K/V block and never exchanges partial results with another.
@@ -442,6 +449,10 @@ fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
   const uint32_t vaddr =
       (uint32_t)(((lane >> 4) >> 1) * 4 * ROWB + ((lane >> 4) & 1) * 128 + 8 * (lane & 15));
 
+  // Issue priority: lowered by one each time another prio_step blocks of this
+  // workgroup's sequence have started (set before the first item).
+  int prio_step = 1, prio_next = 1, prio_level = 3;
+
   f32x16_t o[DT];
   float m_ref = kNegInf;  // reference max of the (sign-adjusted) raw logits
   float l_part = 0.f;     // running sum over this lane's half of the keys
@@ -537,6 +548,13 @@ fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
     if (j == j_beg && k_item > 0) wait_vmcnt<NSTORE>();
     else wait_vmcnt<0>();
     lds_barrier();
+    if (g0 + (j - j_beg) >= prio_next) {  // a quarter of the blocks passed
+      prio_next += prio_step;
+      --prio_level;
+      if (prio_level == 2) __builtin_amdgcn_s_setprio(2);
+      else if (prio_level == 1) __builtin_amdgcn_s_setprio(1);
+      else __builtin_amdgcn_s_setprio(0);
+    }
     if (j + 2 < j_end) issue_k(Kh, (j + 2) * BN, Kb0 + ((gb + j) & 1) * TB);
     if (j + 1 < j_end) issue_v(Vh, (j + 1) * BN, Vb0 + ((gb + j + 1) & 1) * TBV);
   };
@@ -640,6 +658,18 @@ fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
 
   int logical = logical_of(0);
   if (logical < 0) return;  // uniform for the workgroup
+  {
+    int blocks = 0;  // this workgroup's K/V blocks over all its items
+    for (int k = 0, lg = logical; lg >= 0; lg = logical_of(++k)) {
+      int b_, m_, s_, beg_, end_;
+      decode(lg, b_, m_, s_);
+      range_of(m_, s_, beg_, end_);
+      blocks += end_ - beg_;
+    }
+    prio_step = max(1, (blocks + 3) / 4);
+    prio_next = prio_step;
+    __builtin_amdgcn_s_setprio(3);
+  }
   set_item(logical);
   if (!finish_empty_items()) return;
   if (k_item == 0) {
