@@ -187,7 +187,8 @@ def main(argv=None) -> int:
     import torch
 
     from exact_attention_62_amd import (fa2_bwd, fa2_bwd_workspace_size, fa2_fwd, fa2_fwd_cross,
-                                        fa2_fwd_partial, fa2_fwd_splitkv, fa2_merge,
+                                        fa2_fwd_partial, fa2_fwd_splitkv, fa2_launch_shape,
+                                        fa2_merge,
                                         fa2_num_splits, fa2_splitkv_workspace_size, load_library)
     from exact_attention_62_amd.inputs import WORKLOADS, make, make_upstream
 
@@ -307,6 +308,8 @@ def main(argv=None) -> int:
     # Below the ridge point (peak flops per HBM byte) the roofline is bandwidth.
     hbm_bound = not args.backward and flops / alg_bytes < peak * 1e12 / (PEAK_HBM_GBS * 1e9)
 
+    block_m = fa2_launch_shape(B, H, Nq, d, {"bf16": torch.bfloat16, "fp16": torch.float16,
+                                              "fp32": torch.float32}[dtype])[0]
     traffic = (measured_traffic(w.name, causal, dtype)
                if splits is None and not args.backward and not overridden else None)
     c = "true" if causal else "false"
@@ -315,12 +318,15 @@ def main(argv=None) -> int:
     elif Nq == 1 and d in (64, 128, 256):  # one query row per head: the decoding kernel
         kname = f"fa2_decode_kernel<{KERNEL_TYPE[dtype]}, {d}>"
     else:
-        kname = f"fa2_fwd_kernel<{KERNEL_TYPE[dtype]}, {d}, {c}, {'true' if splits else 'false'}>"
+        # Wavefronts per workgroup: kBlockM / 32 (the split kernel always has four).
+        waves = 4 if splits is not None else block_m // 32
+        kname = (f"fa2_fwd_kernel<{KERNEL_TYPE[dtype]}, {d}, {c}, "
+                 f"{'true' if splits is not None else 'false'}, {waves}>")
     if splits is not None:
         kname += (f" + fa2_combine_kernel<{KERNEL_TYPE[dtype]}, {d}> (both per step; kernel_ms "
                   f"covers the two)")
     if args.ring is not None:
-        kname = (f"{G} x fa2_fwd_kernel<{KERNEL_TYPE[dtype]}, {d}, *, true> + "
+        kname = (f"{G} x fa2_fwd_kernel<{KERNEL_TYPE[dtype]}, {d}, *, true, 4> + "
                  f"fa2_combine_kernel<{KERNEL_TYPE[dtype]}, {d}> (all per step; kernel_ms covers them)")
     if args.backward:
         T = KERNEL_TYPE[dtype]
@@ -352,7 +358,7 @@ def main(argv=None) -> int:
         "data": "synthetic (seeded normal Q, K, V; see exact_attention_62_amd/inputs.py)",
         "config": {"workload": name, "B": B, "H": H, "N": Nq, "d": d,
                    **({"Nk": Nk} if Nk != Nq else {}),
-                   "causal": causal, "scale": scale, "kBlockM": 128,
+                   "causal": causal, "scale": scale, "kBlockM": block_m,
                    "flops_per_step": flops,
                    **({"path": "split-KV", "num_splits": splits} if splits is not None else {}),
                    **({"path": f"one GPU's share of {args.ring} key/value shards (the last query "

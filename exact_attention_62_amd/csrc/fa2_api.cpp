@@ -53,7 +53,7 @@ fa2_status_t check_shape(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d
                 (long long)(Nq > Nk ? Nq : Nk), (long long)kMaxLen);
   if (B > 0 && H > (int64_t(1) << 31) / B)
     return fail(FA2_EINVAL, "B*H=%lld*%lld exceeds 2^31", (long long)B, (long long)H);
-  const int64_t bm = dtype == FA2_FP32 ? fa2::kBlockM_f32 : fa2::kBlockM_mfma;
+  const int64_t bm = dtype == FA2_FP32 ? fa2::kBlockM_f32 : fa2::fwd_block_m(d, B * H, Nq);
   const int64_t nmb = (Nq + bm - 1) / bm;
   if (B * H > 0 && nmb > ((int64_t(1) << 31) - 1) / (B * H))
     return fail(FA2_EINVAL, "grid of %lld x %lld workgroups exceeds 2^31 - 1", (long long)nmb,
@@ -198,6 +198,7 @@ fa2_status_t prepare(const void* Q, const void* K, const void* V, void* O, float
   a->d = static_cast<int>(d);
   a->causal = causal;
   a->scale = scale;
+  a->block_m = static_cast<int>(bm);
   a->num_m_block = static_cast<int>((Nq + bm - 1) / bm);
   a->elem = static_cast<int>(dtype);
   a->stream = static_cast<hipStream_t>(stream);
@@ -240,7 +241,7 @@ int64_t splitkv_bytes(int64_t B, int64_t H, int64_t Nq, int64_t d, int64_t split
   return splits * B * H * Nq * (d + 1) * 4;  // O_s [splits][B*H][Nq][d], L_s [splits][B*H][Nq]
 }
 
-fa2_status_t check_splits(int64_t B, int64_t H, int64_t Nq, int num_splits) {
+fa2_status_t check_splits(int64_t B, int64_t H, int64_t Nq, int64_t d, int num_splits) {
   if (num_splits < 1 || num_splits > FA2_MAX_SPLITS)
     return fail(FA2_EINVAL, "num_splits=%d is not in 1..%d", num_splits, FA2_MAX_SPLITS);
   const int64_t nmb = (Nq + fa2::kBlockM_mfma - 1) / fa2::kBlockM_mfma;
@@ -267,6 +268,13 @@ fa2_status_t heuristic_splits(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int6
   const int64_t max_splits = kv_blocks < FA2_MAX_SPLITS ? kv_blocks : FA2_MAX_SPLITS;
   *num_splits = choose_num_splits(nmb * B * H, slots, max_splits);
   return FA2_OK;
+}
+
+// The split kernel always runs four wavefronts (kBlockM_mfma query rows) per
+// workgroup: it exists for grids too small to fill the chip.
+void use_split_blocks(fa2::FwdArgs* a) {
+  a->block_m = fa2::kBlockM_mfma;
+  a->num_m_block = (a->Nq + fa2::kBlockM_mfma - 1) / fa2::kBlockM_mfma;
 }
 
 fa2_status_t fwd_common(const void* Q, const void* K, const void* V, void* O, float* L,
@@ -307,7 +315,7 @@ fa2_status_t fa2_splitkv_workspace_size(int64_t B, int64_t H, int64_t Nq, int64_
   int64_t bm = 0;
   fa2_status_t s = check_shape(B, H, Nq, Nk, d, FA2_BF16, &bm);
   if (s != FA2_OK) return s;
-  s = check_splits(B, H, Nq, num_splits);
+  s = check_splits(B, H, Nq, d, num_splits);
   if (s != FA2_OK) return s;
   if (!bytes) return fail(FA2_EINVAL, "bytes is NULL");
   *bytes = static_cast<size_t>(splitkv_bytes(B, H, Nq, d, num_splits));
@@ -340,7 +348,7 @@ fa2_status_t fa2_fwd_splitkv(const void* Q, const void* K, const void* V, void* 
     s = heuristic_splits(B, H, Nq, Nk, d, &num_splits);
     if (s != FA2_OK) return s;
   }
-  s = check_splits(B, H, Nq, num_splits);
+  s = check_splits(B, H, Nq, d, num_splits);
   if (s != FA2_OK) return s;
   const int64_t need = splitkv_bytes(B, H, Nq, d, num_splits);
   if (workspace == nullptr) return fail(FA2_EINVAL, "workspace is NULL");
@@ -351,6 +359,7 @@ fa2_status_t fa2_fwd_splitkv(const void* Q, const void* K, const void* V, void* 
   s = prepare(Q, K, V, O, L, B, H, Nq, Nk, d, causal, scale, dtype, stream, workspace, need, &a);
   if (s != FA2_OK) return s;
   a.num_splits = num_splits;
+  use_split_blocks(&a);
   a.ws_O = static_cast<float*>(workspace);
   a.ws_L = a.ws_O + static_cast<size_t>(num_splits) * B * H * Nq * d;
   (void)hipGetLastError();
@@ -379,6 +388,7 @@ fa2_status_t fa2_fwd_partial(const void* Q, const void* K, const void* V, float*
   } else {
     // The split kernel with one split writes exactly the float32 partial result.
     a.num_splits = 1;
+    use_split_blocks(&a);
     a.ws_O = O_part;
     a.ws_L = L_part;
     e = launch_fwd(a);

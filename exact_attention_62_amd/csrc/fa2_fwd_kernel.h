@@ -98,10 +98,6 @@ namespace {
 
 using namespace dev;
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kBM = 32 * kWaves;  // query rows per workgroup
-static_assert(kBM == kBlockM_mfma, "kBlockM mismatch");
 
 constexpr float kTau = 8.0f;  // lazy-rescale threshold, log2 units
 
@@ -109,6 +105,10 @@ constexpr float kTau = 8.0f;  // lazy-rescale threshold, log2 units
 template <int D> struct Cfg {
   static constexpr int BN = mfma_block_n(D), kWavesPerSimd = mfma_waves_per_simd(D);
 };
+// Workgroups resident per CU with WAVES wavefronts each.
+template <int D, int WAVES> constexpr int groups_per_cu() {
+  return Cfg<D>::kWavesPerSimd * 4 / WAVES;
+}
 
 // LDS layout of a K block: key row r lives in 1 KB piece blk(r) at row slot
 // slot(r); pieces are kPiece bytes apart, so piece b starts 16*b bytes further
@@ -173,8 +173,8 @@ template <int D> __host__ __device__ constexpr int v_dim(int n, int l) {
   return 16 * ((8 * n + l / 8) % (D / 16)) + 8 * (l % 2);
 }
 
-template <typename T, int D, bool CAUSAL, bool SPLIT>
-__global__ void __launch_bounds__(kThreads, Cfg<D>::kWavesPerSimd)
+template <typename T, int D, bool CAUSAL, bool SPLIT, int WAVES>
+__global__ void __launch_bounds__(64 * WAVES, (groups_per_cu<D, WAVES>()))
 fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
                const uint16_t* __restrict__ Vg, uint16_t* __restrict__ Og,
                float* __restrict__ Lg, float* __restrict__ Ow, float* __restrict__ Lw,
@@ -183,6 +183,9 @@ fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
   typedef typename Vec16<T>::x8 t8_t;
   typedef typename Vec16<T>::x4 t4_t;
   constexpr int BN = Cfg<D>::BN;
+  constexpr int kWaves = WAVES;              // wavefronts per workgroup
+  constexpr int kBM = 32 * WAVES;            // query rows per work item
+  static_assert((WAVES == 4 || WAVES == 8) && groups_per_cu<D, WAVES>() >= 1, "wavefronts");
   constexpr int CH = D / 8;                  // 16-byte chunks per key row
   constexpr int KT = BN / 32;                // 32-key sub-blocks per block
   constexpr int KS = D / 16;                 // MFMA k-steps over the head dimension
@@ -218,6 +221,12 @@ fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps LDS bases scalar
   const int col = lane & 31;  // this lane's query row within the wavefront's 32
+  // The wavefront's group of 32 query rows in a work item.  With eight
+  // wavefronts, w and w + 4 share a SIMD; they take groups w and 7 - w, so
+  // that each SIMD holds one early and one late group of the item and the
+  // causal diagonal's work (and the blocks it hides) splits evenly over the
+  // SIMDs.
+  const int rgrp = kWaves == 8 && wave >= 4 ? 11 - wave : wave;
   const int half = lane >> 5;
 
   // Causal offset: key j is visible to query i when j <= i + off.
@@ -246,7 +255,7 @@ fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
   };
 
   // ---- per-item state
-  int bh = 0, m = 0, q0 = 0, qrow = 0, j_beg = 0, j_end = 0, j_mask = 0;
+  int bh = 0, m = 0, q0 = 0, qrow = 0, j_beg = 0, j_end = 0, j_mask = 0, j_cend = 0;
   int g0 = 0;      // running block count of this workgroup at the current item's first block
   int k_item = 0;  // index of the current item in this workgroup's sequence
   const uint16_t *Qh = Qg, *Kh = Kg, *Vh = Vg;
@@ -316,13 +325,19 @@ fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
       l_rsrc = __builtin_amdgcn_make_buffer_rsrc(Lg + (size_t)bh * Nq + (size_t)m * kBM, (short)0,
                                                  rows * 4, kBufferFlags);
     }
-    q0 = m * kBM + wave * 32;  // first query row of this wavefront
+    q0 = m * kBM + rgrp * 32;  // first query row of this wavefront
     qrow = q0 + col;
     gb = g0 - j_beg;
     // Blocks before j_mask need no mask for this wavefront (every key visible
     // to every one of its rows: below the first row's diagonal, and whole).
     const int seen = q0 + off + 1;  // keys visible to the wavefront's first row
     j_mask = CAUSAL ? (seen <= 0 ? 0 : min(seen / BN, Nk / BN)) : Nk / BN;
+    // Blocks from j_cend on are hidden from every row of this wavefront (past
+    // its last row's diagonal; the item's later rows need them): it takes part
+    // in their loads and barriers only.  At least one block is computed (a
+    // wavefront whose rows see no key computes one block fully masked).
+    const int last_seen = q0 + 31 + off;  // last key visible to the wavefront's last row
+    j_cend = CAUSAL ? max(j_beg + 1, min(j_end, last_seen < 0 ? 0 : last_seen / BN + 1)) : j_end;
   };
 
   // Q fragments (the B operand of S^T = K Q^T), kept in registers for an item.
@@ -599,7 +614,7 @@ fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
   auto prefetch_next = [&]() __attribute__((always_inline)) {
     if (next >= 0 && nend > nbeg) {
       const size_t nqs = (size_t)nbh * (size_t)Nq * D, nks = (size_t)nbh * (size_t)Nk * D;
-      issue_item_start(Qg + nqs, Kg + nks, Vg + nks, nm * kBM + wave * 32 + col, nbeg,
+      issue_item_start(Qg + nqs, Kg + nks, Vg + nks, nm * kBM + rgrp * 32 + col, nbeg,
                        nend - nbeg, g0 + (j_end - j_beg));
     }
   };
@@ -608,7 +623,7 @@ fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
   auto store_result = [&]() __attribute__((always_inline)) {
     const float l_tot = halves_sum(l_part);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    const int lrow = wave * 32 + col;  // this lane's row in the query block
+    const int lrow = rgrp * 32 + col;  // this lane's row in the query block
 #pragma unroll
     for (int t = 0; t < DT; ++t)
 #pragma unroll
@@ -681,7 +696,7 @@ fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
 
   for (;;) {
     look_ahead();
-    const int j_unmasked = min(j_mask, j_end - 1);  // unmasked blocks that have a successor
+    const int j_unmasked = min(j_mask, j_cend - 1);  // unmasked blocks that have a successor
     f32x16_t SB[KT];
     int j = j_beg;
     // Unrolled by two so that the S registers alternate between S_cur and SB
@@ -702,7 +717,7 @@ fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
       for (int kt = 0; kt < KT; ++kt) S_cur[kt] = SB[kt];
       ++j;
     }
-    for (; j + 2 < j_end; j += 2) {
+    for (; j + 2 < j_cend; j += 2) {
       advance(j);
       consume(std::true_type{}, j, S_cur,
               [&]() { compute_S(Kb0 + ((gb + j + 1) & 1) * TB, SB); });
@@ -710,7 +725,7 @@ fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
       consume(std::true_type{}, j + 1, SB,
               [&]() { compute_S(Kb0 + ((gb + j) & 1) * TB, S_cur); });
     }
-    if (j + 1 < j_end) {
+    if (j + 1 < j_cend) {
       advance(j);
       consume(std::true_type{}, j, S_cur,
               [&]() { compute_S(Kb0 + ((gb + j + 1) & 1) * TB, SB); });
@@ -718,15 +733,20 @@ fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
       for (int kt = 0; kt < KT; ++kt) S_cur[kt] = SB[kt];
       ++j;
     }
-    // Last block of the item.  Both K buffers and the other V buffer are free
-    // now, and so are the Q registers: the next item's Q, K_beg, V_beg,
-    // K_beg+1 go out here and overlap this block's softmax, its PV product and
-    // the O stores.
+    // Last block that this wavefront computes.  At the item's last block both
+    // K buffers and the other V buffer are free, and so are the Q registers:
+    // the next item's Q, K_beg, V_beg, K_beg+1 go out there and overlap that
+    // block's softmax, its PV product and the O stores.
     advance(j);
-    prefetch_next();
+    if (j + 1 == j_end) prefetch_next();
     // Always the masked form: one copy of the code, and for an unmasked block
     // the threshold test hides nothing.
     consume(std::true_type{}, j, S_cur, [] {});
+    // Blocks hidden from all of this wavefront's rows: loads and barriers.
+    for (++j; j < j_end; ++j) {
+      advance(j);
+      if (j + 1 == j_end) prefetch_next();
+    }
     store_result();
     if (next < 0) break;
     g0 += j_end - j_beg;
@@ -737,17 +757,19 @@ fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
   }
 }
 
-template <typename T, int D, bool CAUSAL, bool SPLIT>
+template <typename T, int D, bool CAUSAL, bool SPLIT, int WAVES>
 hipError_t launch(const FwdArgs& a) {
+  if (a.block_m != 32 * WAVES) return hipErrorInvalidValue;  // num_m_block counts other blocks
   const int splits = SPLIT ? a.num_splits : 1;
   const int total = a.num_m_block * a.BH * splits;
   // Persistent grid: as many workgroups as fit on the chip at once (a 4-wave
   // workgroup puts one wave on each SIMD of a CU, so kWavesPerSimd workgroups
-  // per CU), each walking its share of the work items.
+  // per CU; an 8-wave one two, so one workgroup per CU), each walking its
+  // share of the work items.
   int cus = 0;
   const hipError_t e = cu_count(&cus);
   if (e != hipSuccess) return e;
-  const int resident = Cfg<D>::kWavesPerSimd * cus;
+  const int resident = groups_per_cu<D, WAVES>() * cus;
   const int grid = total < resident ? total : resident;
   // The kernel works with c = |scale| * log2(e) > 0: a negative scale flips the
   // sign of Q and a zero scale zeroes Q (both exact), with |scale| = 1 then.
@@ -755,7 +777,7 @@ hipError_t launch(const FwdArgs& a) {
   const float sa = zero ? 1.f : (a.scale < 0.f ? -a.scale : a.scale);
   const uint32_t qsign = a.scale < 0.f ? 0x80008000u : 0u;
   const uint32_t qkeep = zero ? 0u : 0xFFFFFFFFu;
-  hipLaunchKernelGGL((fa2_fwd_kernel<T, D, CAUSAL, SPLIT>), dim3(grid), dim3(kThreads), 0,
+  hipLaunchKernelGGL((fa2_fwd_kernel<T, D, CAUSAL, SPLIT, WAVES>), dim3(grid), dim3(64 * WAVES), 0,
                      a.stream, (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V,
                      (uint16_t*)a.O, a.L, a.ws_O, a.ws_L, a.Nq, a.Nk, a.BH, a.num_m_block,
                      splits, total, sa * kLog2e, sa, qsign, qkeep);
@@ -769,19 +791,26 @@ hipError_t dispatch_fwd_mfma(const FwdArgs& a) {
   const bool split = a.num_splits > 0;
   switch ((a.d * 2 + a.causal) * 2 + split) {
 #define FA2_CASE(D, C)                                                  \
-  case (D * 2 + C) * 2 + 0: return launch<T, D, (bool)C, false>(a);    \
-  case (D * 2 + C) * 2 + 1: return launch<T, D, (bool)C, true>(a);
+  case (D * 2 + C) * 2 + 0: return launch<T, D, (bool)C, false, 4>(a); \
+  case (D * 2 + C) * 2 + 1: return launch<T, D, (bool)C, true, 4>(a);
     FA2_CASE(32, 0)
     FA2_CASE(32, 1)
     FA2_CASE(64, 0)
     FA2_CASE(64, 1)
     FA2_CASE(96, 0)
     FA2_CASE(96, 1)
-    FA2_CASE(128, 0)
-    FA2_CASE(128, 1)
     FA2_CASE(256, 0)
     FA2_CASE(256, 1)
 #undef FA2_CASE
+    // d = 128 without splits: eight wavefronts per workgroup on large grids.
+    case (128 * 2 + 0) * 2 + 0:
+      return a.block_m == kBlockM_wide ? launch<T, 128, false, false, 8>(a)
+                                       : launch<T, 128, false, false, 4>(a);
+    case (128 * 2 + 1) * 2 + 0:
+      return a.block_m == kBlockM_wide ? launch<T, 128, true, false, 8>(a)
+                                       : launch<T, 128, true, false, 4>(a);
+    case (128 * 2 + 0) * 2 + 1: return launch<T, 128, false, true, 4>(a);
+    case (128 * 2 + 1) * 2 + 1: return launch<T, 128, true, true, 4>(a);
   }
   return hipErrorInvalidValue;
 }

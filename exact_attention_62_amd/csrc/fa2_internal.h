@@ -7,9 +7,18 @@
 namespace fa2 {
 
 // Query rows per workgroup (the pages' kBlockM).  16-bit types (bf16, fp16):
-// four wavefronts of 32 rows each.  fp32 exact mode: four wavefronts of one
-// row each.
+// four wavefronts of 32 rows each, two workgroups per CU; for d = 128 without
+// splits, on a grid of at least kWideMinItems items of 256 rows, eight
+// wavefronts (one workgroup per CU, both wavefronts of a SIMD in the same
+// workgroup).  fp32 exact mode: four wavefronts of one row each.
 constexpr int kBlockM_mfma = 128;
+constexpr int kBlockM_wide = 256;
+constexpr int64_t kWideMinItems = 256;
+constexpr int64_t fwd_block_m(int64_t d, int64_t BH, int64_t Nq) {
+  return d == 128 && BH * ((Nq + kBlockM_wide - 1) / kBlockM_wide) >= kWideMinItems
+             ? kBlockM_wide
+             : kBlockM_mfma;
+}
 constexpr int kBlockM_f32 = 4;
 // Keys per K/V block of the 16-bit kernel, and its wavefronts per SIMD (the
 // workgroups that stay resident on one CU).
@@ -31,6 +40,7 @@ struct FwdArgs {
   int d;            // head dimension
   int causal;       // 0 or 1; aligned bottom-right when Nq != Nk
   float scale;      // softmax scale
+  int block_m = kBlockM_mfma;  // query rows per work item (kBlockM)
   int num_m_block;  // ceil(Nq / kBlockM)
   int elem;         // Elem of Q, K, V and O
   hipStream_t stream;

@@ -146,11 +146,17 @@ def test_grid_matches_the_pages_worked_example():
 
 
 def test_grid_of_the_named_workloads():
-    # (query blocks, batch, head) for the five workloads at kBlockM = 128 (bf16).
+    # (kBlockM, query blocks, items) for the five workloads (bf16): 128 query
+    # rows per workgroup (four wavefronts of 32), 256 for d = 128 (eight).
     assert F.fa2_launch_shape(2, 4, 1024, 64) == (128, 8, 64)
-    assert F.fa2_launch_shape(16, 16, 2048, 128) == (128, 16, 4096)
-    assert F.fa2_launch_shape(1, 16, 16384, 128) == (128, 128, 2048)
+    assert F.fa2_launch_shape(16, 16, 2048, 128) == (256, 8, 2048)
+    assert F.fa2_launch_shape(1, 16, 16384, 128) == (256, 64, 1024)
     assert F.fa2_launch_shape(2, 16, 8191, 256) == (128, 64, 2048)
+    # d = 128 takes 256-row blocks only on grids of at least 256 such items.
+    assert F.fa2_launch_shape(1, 16, 4096, 128) == (256, 16, 256)
+    assert F.fa2_launch_shape(1, 16, 3840, 128) == (128, 30, 480)
+    assert F.fa2_launch_shape(1, 64, 1000, 128) == (256, 4, 256)
+    assert F.fa2_launch_shape(64, 1, 1000, 64) == (128, 8, 512)
     assert F.fa2_launch_shape(1, 1, 128, 64, torch.float32) == (4, 32, 32)
 
 

@@ -16,7 +16,7 @@ import numpy as np
 import pytest
 import torch
 
-from exact_attention_62_amd import attention, fa2_fwd
+from exact_attention_62_amd import attention, fa2_fwd, fa2_fwd_cross, fa2_launch_shape
 from exact_attention_62_amd.inputs import WORKLOADS, make, make_random
 from oracle import attention_fp64, attention_rows_fp64
 
@@ -169,6 +169,36 @@ def test_ragged_sigma2_reading():
         rows = _sample_rows(w.N, rng, 32)
         O, L = attention_rows_fp64(q, k, v, 0, h, rows, causal=True, scale=w.scale)
         _cmp(o[0, h, rows].cpu(), lse[0, h, rows].cpu(), O, L, "bf16", f"sigma2 head {h}")
+
+
+# ----------------------------------------- d = 128 with eight wavefronts per workgroup
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_wide_workgroups_ragged(causal):
+    # 64 heads x ceil(1000 / 256) = 256 items: the 256-row, eight-wavefront
+    # kernel, with a ragged last block and (causal) blocks hidden from the
+    # first wavefronts' rows.
+    assert fa2_launch_shape(1, 64, 1000, 128)[0] == 256
+    _say(f"wide bf16 B=1 H=64 N=1000 d=128 causal={causal}")
+    q, k, v = make_random(1, 64, 1000, 128, seed=91 + causal)
+    O, L = attention_fp64(q, k, v, causal=causal)
+    o, lse = _run(q, k, v, causal)
+    _cmp(o, lse, O, L, "bf16", f"wide causal={causal}")
+
+
+def test_wide_workgroups_cross_lengths():
+    # 96 heads x ceil(700 / 256) = 288 items; Nk > Nq with the causal mask
+    # aligned bottom-right.
+    B, H, Nq, Nk, d = 1, 96, 700, 1300, 128
+    _say(f"wide bf16 cross Nq={Nq} Nk={Nk}")
+    q, k, v = make_random(B, H, Nq, d, seed=17, Nk=Nk)
+    O, L = attention_fp64(q, k, v, causal=True)
+    qd, kd, vd = (t.cuda() for t in (q, k, v))
+    o = torch.empty_like(qd)
+    lse = torch.empty(B, H, Nq, device="cuda")
+    fa2_fwd_cross(qd, kd, vd, o, lse, causal=True)
+    torch.cuda.synchronize()
+    _cmp(o, lse, O, L, "bf16", "wide cross")
 
 
 # ------------------------------------------------------------ closed forms on the GPU
