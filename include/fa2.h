@@ -159,7 +159,8 @@ fa2_status_t fa2_splitkv_workspace_size(int64_t B, int64_t H, int64_t Nq, int64_
  * problem on the current device (page "Flash Attention V2原理解读", the
  * thread-block grid section): for every candidate s in 1..min(K/V blocks of
  * the Nk keys, FA2_MAX_SPLITS), the utilisation of the GPU by items * s work
- * items, items = B*H*ceil(Nq / kBlockM), over the device's concurrently
+ * items, items = B*H*ceil(Nq / 128) (the split kernel's 128-row query
+ * blocks), over the device's concurrently
  * resident workgroups (the busy fraction of the last round:
  * (n / slots) / ceil(n / slots)); then the smallest s whose utilisation is at
  * least 0.95 of the best.  Queries the current device's compute-unit count (a
@@ -222,7 +223,10 @@ fa2_status_t fa2_merge(const float* O_parts, const float* L_parts, int num_parts
  * blocks (page "FlashAttention学习笔记(2)", section "V2中的thread blocks排布";
  * "Flash Attention V2原理解读", the thread-block grid section).  Writes
  * kBlockM, num_m_block and the item count B*H*num_m_block through the
- * non-NULL out pointers (N is the query length).  The 16-bit kernel runs the
+ * non-NULL out pointers (N is the query length).  kBlockM is 128 for the
+ * 16-bit kernel (four wavefronts of 32 rows), except for d = 128 when
+ * B*H*ceil(N / 256) >= 256: 256 (eight wavefronts, one workgroup per compute
+ * unit); 4 for fp32.  The 16-bit kernel runs the
  * items on a persistent grid of min(items, resident workgroups) workgroups;
  * the fp32 kernel launches one workgroup per item.  Makes no HIP call.  Returns FA2_EINVAL / FA2_ENOTSUP
  * for arguments fa2_fwd would reject on those grounds.
