@@ -318,15 +318,21 @@ def main(argv=None) -> int:
     elif Nq == 1 and d in (64, 128, 256):  # one query row per head: the decoding kernel
         kname = f"fa2_decode_kernel<{KERNEL_TYPE[dtype]}, {d}>"
     else:
-        # Wavefronts per workgroup: kBlockM / 32 (the split kernel always has four).
+        # Wavefronts per workgroup: kBlockM / 32 (the split kernel always has
+        # four); wavefronts per SIMD: 2, or 1 for d = 256 with splits or on a
+        # grid of fewer than two items per CU.
         waves = 4 if splits is not None else block_m // 32
+        cus = torch.cuda.get_device_properties(0).multi_processor_count
+        items = B * H * ((Nq + block_m - 1) // block_m)
+        occ = 1 if d == 256 and (splits is not None or items < 2 * cus) else 2
         kname = (f"fa2_fwd_kernel<{KERNEL_TYPE[dtype]}, {d}, {c}, "
-                 f"{'true' if splits is not None else 'false'}, {waves}>")
+                 f"{'true' if splits is not None else 'false'}, {waves}, {occ}>")
     if splits is not None:
         kname += (f" + fa2_combine_kernel<{KERNEL_TYPE[dtype]}, {d}> (both per step; kernel_ms "
                   f"covers the two)")
     if args.ring is not None:
-        kname = (f"{G} x fa2_fwd_kernel<{KERNEL_TYPE[dtype]}, {d}, *, true, 4> + "
+        kname = (f"{G} x fa2_fwd_kernel<{KERNEL_TYPE[dtype]}, {d}, *, true, 4, "
+                 f"{1 if d == 256 else 2}> + "
                  f"fa2_combine_kernel<{KERNEL_TYPE[dtype]}, {d}> (all per step; kernel_ms covers them)")
     if args.backward:
         T = KERNEL_TYPE[dtype]

@@ -103,12 +103,10 @@ constexpr float kTau = 8.0f;  // lazy-rescale threshold, log2 units
 
 // Keys per K/V block and wavefronts per SIMD for each head dimension.
 template <int D> struct Cfg {
-  static constexpr int BN = mfma_block_n(D), kWavesPerSimd = mfma_waves_per_simd(D);
+  static constexpr int BN = mfma_block_n(D);
 };
 // Workgroups resident per CU with WAVES wavefronts each.
-template <int D, int WAVES> constexpr int groups_per_cu() {
-  return Cfg<D>::kWavesPerSimd * 4 / WAVES;
-}
+template <int WAVES, int OCC> constexpr int groups_per_cu() { return OCC * 4 / WAVES; }
 
 // LDS layout of a K block: key row r lives in 1 KB piece blk(r) at row slot
 // slot(r); pieces are kPiece bytes apart, so piece b starts 16*b bytes further
@@ -173,8 +171,8 @@ template <int D> __host__ __device__ constexpr int v_dim(int n, int l) {
   return 16 * ((8 * n + l / 8) % (D / 16)) + 8 * (l % 2);
 }
 
-template <typename T, int D, bool CAUSAL, bool SPLIT, int WAVES>
-__global__ void __launch_bounds__(64 * WAVES, (groups_per_cu<D, WAVES>()))
+template <typename T, int D, bool CAUSAL, bool SPLIT, int WAVES, int OCC>
+__global__ void __launch_bounds__(64 * WAVES, (groups_per_cu<WAVES, OCC>()))
 fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
                const uint16_t* __restrict__ Vg, uint16_t* __restrict__ Og,
                float* __restrict__ Lg, float* __restrict__ Ow, float* __restrict__ Lw,
@@ -185,7 +183,7 @@ fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
   constexpr int BN = Cfg<D>::BN;
   constexpr int kWaves = WAVES;              // wavefronts per workgroup
   constexpr int kBM = 32 * WAVES;            // query rows per work item
-  static_assert((WAVES == 4 || WAVES == 8) && groups_per_cu<D, WAVES>() >= 1, "wavefronts");
+  static_assert((WAVES == 4 || WAVES == 8) && groups_per_cu<WAVES, OCC>() >= 1, "wavefronts");
   constexpr int CH = D / 8;                  // 16-byte chunks per key row
   constexpr int KT = BN / 32;                // 32-key sub-blocks per block
   constexpr int KS = D / 16;                 // MFMA k-steps over the head dimension
@@ -757,19 +755,21 @@ fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
   }
 }
 
-template <typename T, int D, bool CAUSAL, bool SPLIT, int WAVES>
+// OCC: wavefronts per SIMD that the kernel's registers allow (1: up to 512
+// VGPRs, 2: up to 256).
+template <typename T, int D, bool CAUSAL, bool SPLIT, int WAVES, int OCC>
 hipError_t launch(const FwdArgs& a) {
   if (a.block_m != 32 * WAVES) return hipErrorInvalidValue;  // num_m_block counts other blocks
   const int splits = SPLIT ? a.num_splits : 1;
   const int total = a.num_m_block * a.BH * splits;
   // Persistent grid: as many workgroups as fit on the chip at once (a 4-wave
-  // workgroup puts one wave on each SIMD of a CU, so kWavesPerSimd workgroups
-  // per CU; an 8-wave one two, so one workgroup per CU), each walking its
-  // share of the work items.
+  // workgroup puts one wave on each SIMD of a CU, so mfma_waves_per_simd
+  // workgroups per CU; an 8-wave one two, so one workgroup per CU), each
+  // walking its share of the work items.
   int cus = 0;
   const hipError_t e = cu_count(&cus);
   if (e != hipSuccess) return e;
-  const int resident = groups_per_cu<D, WAVES>() * cus;
+  const int resident = groups_per_cu<WAVES, OCC>() * cus;
   const int grid = total < resident ? total : resident;
   // The kernel works with c = |scale| * log2(e) > 0: a negative scale flips the
   // sign of Q and a zero scale zeroes Q (both exact), with |scale| = 1 then.
@@ -777,7 +777,7 @@ hipError_t launch(const FwdArgs& a) {
   const float sa = zero ? 1.f : (a.scale < 0.f ? -a.scale : a.scale);
   const uint32_t qsign = a.scale < 0.f ? 0x80008000u : 0u;
   const uint32_t qkeep = zero ? 0u : 0xFFFFFFFFu;
-  hipLaunchKernelGGL((fa2_fwd_kernel<T, D, CAUSAL, SPLIT, WAVES>), dim3(grid), dim3(64 * WAVES), 0,
+  hipLaunchKernelGGL((fa2_fwd_kernel<T, D, CAUSAL, SPLIT, WAVES, OCC>), dim3(grid), dim3(64 * WAVES), 0,
                      a.stream, (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V,
                      (uint16_t*)a.O, a.L, a.ws_O, a.ws_L, a.Nq, a.Nk, a.BH, a.num_m_block,
                      splits, total, sa * kLog2e, sa, qsign, qkeep);
@@ -790,27 +790,41 @@ template <typename T>
 hipError_t dispatch_fwd_mfma(const FwdArgs& a) {
   const bool split = a.num_splits > 0;
   switch ((a.d * 2 + a.causal) * 2 + split) {
-#define FA2_CASE(D, C)                                                  \
-  case (D * 2 + C) * 2 + 0: return launch<T, D, (bool)C, false, 4>(a); \
-  case (D * 2 + C) * 2 + 1: return launch<T, D, (bool)C, true, 4>(a);
+#define FA2_CASE(D, C)                                                     \
+  case (D * 2 + C) * 2 + 0: return launch<T, D, (bool)C, false, 4, 2>(a); \
+  case (D * 2 + C) * 2 + 1: return launch<T, D, (bool)C, true, 4, 2>(a);
     FA2_CASE(32, 0)
     FA2_CASE(32, 1)
     FA2_CASE(64, 0)
     FA2_CASE(64, 1)
     FA2_CASE(96, 0)
     FA2_CASE(96, 1)
-    FA2_CASE(256, 0)
-    FA2_CASE(256, 1)
 #undef FA2_CASE
     // d = 128 without splits: eight wavefronts per workgroup on large grids.
-    case (128 * 2 + 0) * 2 + 0:
-      return a.block_m == kBlockM_wide ? launch<T, 128, false, false, 8>(a)
-                                       : launch<T, 128, false, false, 4>(a);
-    case (128 * 2 + 1) * 2 + 0:
-      return a.block_m == kBlockM_wide ? launch<T, 128, true, false, 8>(a)
-                                       : launch<T, 128, true, false, 4>(a);
-    case (128 * 2 + 0) * 2 + 1: return launch<T, 128, false, true, 4>(a);
-    case (128 * 2 + 1) * 2 + 1: return launch<T, 128, true, true, 4>(a);
+#define FA2_CASE_128(C)                                                         \
+  case (128 * 2 + C) * 2 + 0:                                                   \
+    return a.block_m == kBlockM_wide ? launch<T, 128, (bool)C, false, 8, 2>(a)  \
+                                     : launch<T, 128, (bool)C, false, 4, 2>(a); \
+  case (128 * 2 + C) * 2 + 1: return launch<T, 128, (bool)C, true, 4, 2>(a);
+    FA2_CASE_128(0)
+    FA2_CASE_128(1)
+#undef FA2_CASE_128
+    // d = 256: two wavefronts per SIMD (256 VGPRs, a few spilled) when the
+    // items fill two workgroups on every CU; otherwise, and with splits, one
+    // (512 VGPRs, no spill), which is faster for a workgroup alone on its CU.
+#define FA2_CASE_256(C)                                                            \
+  case (256 * 2 + C) * 2 + 0: {                                                    \
+    int cus = 0;                                                                   \
+    const hipError_t e = cu_count(&cus);                                           \
+    if (e != hipSuccess) return e;                                                 \
+    return (int64_t)a.num_m_block * a.BH >= 2 * (int64_t)cus                       \
+               ? launch<T, 256, (bool)C, false, 4, 2>(a)                           \
+               : launch<T, 256, (bool)C, false, 4, 1>(a);                          \
+  }                                                                                \
+  case (256 * 2 + C) * 2 + 1: return launch<T, 256, (bool)C, true, 4, 1>(a);
+    FA2_CASE_256(0)
+    FA2_CASE_256(1)
+#undef FA2_CASE_256
   }
   return hipErrorInvalidValue;
 }

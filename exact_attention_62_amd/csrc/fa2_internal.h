@@ -20,8 +20,10 @@ constexpr int64_t fwd_block_m(int64_t d, int64_t BH, int64_t Nq) {
              : kBlockM_mfma;
 }
 constexpr int kBlockM_f32 = 4;
-// Keys per K/V block of the 16-bit kernel, and its wavefronts per SIMD (the
-// workgroups that stay resident on one CU).
+// Keys per K/V block of the 16-bit kernel, and the wavefronts per SIMD of its
+// split form (with four-wavefront workgroups, the workgroups that stay
+// resident on one CU).  Without splits, d = 256 runs two wavefronts per SIMD
+// on grids of at least two items per CU (see dispatch_fwd_mfma).
 constexpr int mfma_block_n(int d) { return d == 256 ? 32 : 64; }
 constexpr int mfma_waves_per_simd(int d) { return d == 256 ? 1 : 2; }
 
