@@ -756,7 +756,7 @@ fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
 }
 
 // OCC: wavefronts per SIMD that the kernel's registers allow (1: up to 512
-// VGPRs, 2: up to 256).
+// VGPRs, 2: up to 256, 3: up to 168).
 template <typename T, int D, bool CAUSAL, bool SPLIT, int WAVES, int OCC>
 hipError_t launch(const FwdArgs& a) {
   if (a.block_m != 32 * WAVES) return hipErrorInvalidValue;  // num_m_block counts other blocks
@@ -790,15 +790,16 @@ template <typename T>
 hipError_t dispatch_fwd_mfma(const FwdArgs& a) {
   const bool split = a.num_splits > 0;
   switch ((a.d * 2 + a.causal) * 2 + split) {
-#define FA2_CASE(D, C)                                                     \
-  case (D * 2 + C) * 2 + 0: return launch<T, D, (bool)C, false, 4, 2>(a); \
-  case (D * 2 + C) * 2 + 1: return launch<T, D, (bool)C, true, 4, 2>(a);
-    FA2_CASE(32, 0)
-    FA2_CASE(32, 1)
-    FA2_CASE(64, 0)
-    FA2_CASE(64, 1)
-    FA2_CASE(96, 0)
-    FA2_CASE(96, 1)
+#define FA2_CASE(D, C, OCC)                                                  \
+  case (D * 2 + C) * 2 + 0: return launch<T, D, (bool)C, false, 4, OCC>(a); \
+  case (D * 2 + C) * 2 + 1: return launch<T, D, (bool)C, true, 4, OCC>(a);
+    // d = 32 fits 168 VGPRs: three wavefronts per SIMD.
+    FA2_CASE(32, 0, 3)
+    FA2_CASE(32, 1, 3)
+    FA2_CASE(64, 0, 2)
+    FA2_CASE(64, 1, 2)
+    FA2_CASE(96, 0, 2)
+    FA2_CASE(96, 1, 2)
 #undef FA2_CASE
     // d = 128 without splits: eight wavefronts per workgroup on large grids.
 #define FA2_CASE_128(C)                                                         \

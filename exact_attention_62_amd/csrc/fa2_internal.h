@@ -25,7 +25,7 @@ constexpr int kBlockM_f32 = 4;
 // resident on one CU).  Without splits, d = 256 runs two wavefronts per SIMD
 // on grids of at least two items per CU (see dispatch_fwd_mfma).
 constexpr int mfma_block_n(int d) { return d == 256 ? 32 : 64; }
-constexpr int mfma_waves_per_simd(int d) { return d == 256 ? 1 : 2; }
+constexpr int mfma_waves_per_simd(int d) { return d == 256 ? 1 : d == 32 ? 3 : 2; }
 
 // Element types, with the values of fa2_dtype_t.
 enum Elem { kBF16 = 0, kFP32 = 1, kFP16 = 2 };
