@@ -18,8 +18,8 @@ import numpy as np
 import pytest
 import torch
 
-from exact_attention_62_amd import (attention, fa2_fwd_cross, fa2_fwd_splitkv, fa2_num_splits,
-                                    fa2_splitkv_workspace_size)
+from exact_attention_62_amd import (attention, fa2_fwd_cross, fa2_fwd_splitkv, fa2_launch_shape,
+                                    fa2_num_splits, fa2_splitkv_workspace_size)
 from exact_attention_62_amd.inputs import make, make_random
 from oracle import attention_fp64, attention_rows_fp64
 
@@ -239,3 +239,37 @@ def test_decode_over_two_million_keys():
     _cmp(o, lse, O, L, "bf16", "decode 2M split")
     o2, lse2 = _cross(q, k, v, True)
     _cmp(o2, lse2, O, L, "bf16", "decode 2M plain")
+
+
+# ------------------------------------------ launch forms chosen by grid size
+
+def test_eight_wavefronts_more_queries_than_keys():
+    """d = 128 on a grid of >= 256 items of 256 rows (the eight-wavefront form)
+    with Nq > Nk and the causal mask: the first 600 query rows see no key, so
+    whole wavefronts compute one fully masked block and must still give
+    O = 0, L = -inf; the others stop at their own last visible block."""
+    B, H, Nq, Nk, d = 1, 48, 1300, 700, 128
+    assert fa2_launch_shape(B, H, Nq, d)[0] == 256  # 48 x 6 = 288 items
+    _say(f"eight wavefronts B={B} H={H} Nq={Nq} Nk={Nk} d={d} causal")
+    q, k, v = make_random(B, H, Nq, d, seed=29, Nk=Nk)
+    O, L = attention_fp64(q, k, v, causal=True)
+    o, lse = _cross(q, k, v, causal=True)
+    _cmp(o, lse, O, L, "bf16", "eight wavefronts, Nq > Nk")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_d256_two_wavefronts_per_simd_cross_lengths(causal):
+    """d = 256 on a grid of >= 2 items per CU (two wavefronts per SIMD, 256
+    VGPRs) with Nq != Nk and a ragged last block; sampled rows of four heads."""
+    B, H, Nq, Nk, d = 1, 32, 2100, 2500, 256
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert fa2_launch_shape(B, H, Nq, d)[2] >= 2 * cus  # 32 x 17 = 544 items
+    _say(f"d=256 two per SIMD B={B} H={H} Nq={Nq} Nk={Nk} causal={causal}")
+    q, k, v = make_random(B, H, Nq, d, seed=31 + causal, Nk=Nk)
+    o, lse = _cross(q, k, v, causal=causal)
+    rows = np.unique(np.concatenate([np.arange(0, 40), np.arange(1000, 1040),
+                                     np.arange(Nq - 60, Nq)]))
+    for h in (0, 7, 20, 31):
+        O, L = attention_rows_fp64(q, k, v, 0, h, rows, causal=causal)
+        idx = torch.as_tensor(rows)
+        _cmp(o[0, h][idx], lse[0, h][idx], O, L, "bf16", f"d=256 head {h}")
