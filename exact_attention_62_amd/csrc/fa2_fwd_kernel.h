@@ -4,10 +4,11 @@
 //
 // The algorithm (pages "FlashAttention学习笔记(2)" and "Flash Attention V2原理解读",
 // forward sections; "flash-attention123和ring-attention", 优化1-优化4):
-//   outer loop: one work item per block of kBlockM = 128 query rows of one
-//               (batch, head); items are independent;
+//   outer loop: one work item per block of kBlockM = 32 * WAVES query rows
+//               (128, or 256 with eight wavefronts) of one (batch, head);
+//               items are independent;
 //   inner loop: K_j, V_j blocks of BN keys, staged in LDS and shared by the
-//               workgroup's four wavefronts;
+//               workgroup's wavefronts;
 //   per block:  S = scale * Q_i K_j^T on MFMA, online row max / row sum, the
 //               running O rescaled by exp(m_old - m_new) and P~ V_j added on
 //               MFMA, no division by l inside the loop;
@@ -27,7 +28,7 @@
 // and light causal blocks balance.  While the last K/V block of an item is
 // processed, the next item's Q rows and first K/V blocks are already loading.
 //
-// Issue priority.  Two workgroups share each CU, and the SIMDs' arbitration
+// Issue priority.  Where two workgroups share a CU, the SIMDs' arbitration
 // favours the older one: with the same number of blocks each, the younger
 // finished up to 15% later and then ran alone on its CU.  Each wavefront
 // therefore lowers its priority (s_setprio 3, 2, 1, 0) as its workgroup
@@ -37,6 +38,10 @@
 // Wavefront layout (the pages' split-Q warp scheme, re-derived for 64-wide
 // wavefronts and 32x32 MFMA tiles): each wavefront owns 32 query rows against
 // the shared K/V block and never exchanges partial results with another.
+// WAVES = 4 (two or three workgroups per CU, as OCC, the wavefronts per SIMD
+// that the registers allow, permits) or 8 (d = 128 on large grids: one
+// workgroup per CU, both wavefronts of a SIMD in it, each K/V block staged
+// once per CU).
 //
 // MFMA orientation.  v_mfma_f32_32x32x16_{bf16,f16} produces a 32x32 fp32 tile
 // where lane l holds column (l % 32) and rows 8*(r/4) + 4*(l/32) + (r%4),
