@@ -241,7 +241,7 @@ int64_t splitkv_bytes(int64_t B, int64_t H, int64_t Nq, int64_t d, int64_t split
   return splits * B * H * Nq * (d + 1) * 4;  // O_s [splits][B*H][Nq][d], L_s [splits][B*H][Nq]
 }
 
-fa2_status_t check_splits(int64_t B, int64_t H, int64_t Nq, int64_t d, int num_splits) {
+fa2_status_t check_splits(int64_t B, int64_t H, int64_t Nq, int num_splits) {
   if (num_splits < 1 || num_splits > FA2_MAX_SPLITS)
     return fail(FA2_EINVAL, "num_splits=%d is not in 1..%d", num_splits, FA2_MAX_SPLITS);
   const int64_t nmb = (Nq + fa2::kBlockM_mfma - 1) / fa2::kBlockM_mfma;
@@ -315,7 +315,7 @@ fa2_status_t fa2_splitkv_workspace_size(int64_t B, int64_t H, int64_t Nq, int64_
   int64_t bm = 0;
   fa2_status_t s = check_shape(B, H, Nq, Nk, d, FA2_BF16, &bm);
   if (s != FA2_OK) return s;
-  s = check_splits(B, H, Nq, d, num_splits);
+  s = check_splits(B, H, Nq, num_splits);
   if (s != FA2_OK) return s;
   if (!bytes) return fail(FA2_EINVAL, "bytes is NULL");
   *bytes = static_cast<size_t>(splitkv_bytes(B, H, Nq, d, num_splits));
@@ -348,7 +348,7 @@ fa2_status_t fa2_fwd_splitkv(const void* Q, const void* K, const void* V, void* 
     s = heuristic_splits(B, H, Nq, Nk, d, &num_splits);
     if (s != FA2_OK) return s;
   }
-  s = check_splits(B, H, Nq, d, num_splits);
+  s = check_splits(B, H, Nq, num_splits);
   if (s != FA2_OK) return s;
   const int64_t need = splitkv_bytes(B, H, Nq, d, num_splits);
   if (workspace == nullptr) return fail(FA2_EINVAL, "workspace is NULL");
