@@ -6,16 +6,21 @@
 A step is one fa2_fwd call (the whole hot path: one kernel launch) over the
 workload's inputs (with --splits: one fa2_fwd_splitkv call, the split kernel and
 the merge kernel), which are generated with the seeded recipe and copied to
-HBM before timing starts.  W untimed steps, then exactly K timed steps
-bracketed by torch.cuda.synchronize(); the launches are also bracketed by HIP
-events recorded on the stream the kernel is enqueued on, which gives the
-average kernel duration used for the roofline figure.
+HBM before timing starts.  First a settle phase (--settle-seconds of untimed
+steps, reported in the line as "settle", so that a GPU that was idle reaches its
+sustained clocks), then W untimed warm-up steps, then exactly K timed steps
+bracketed by torch.cuda.synchronize().  An event recorded on the stream the
+kernels are enqueued on separates consecutive launches, so every launch is
+timed on its own: the roofline uses their mean, and the line gives their
+median, min and max.  The device's name, compute units and graphics clock
+(sampled through amdsmi during the timed steps) are reported beside it.
 
 Prints one JSON line.  ``value`` is TFLOP/s by the metric's count
 (4*B*H*N^2*d, halved with the causal mask); ``roofline`` compares the same
 algorithmic flops per launch against MI355X's dense bf16 MFMA peak;
 ``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of the same
-workload on this host's cores.
+workload on this host's cores, and ``parity`` compares the outputs of the last
+timed step with the oracle's on the slices of that sample.
 
 Variants: --dtype, --B, --H, --d, --q-len and --kv-len override the named
 workload's type and shape (same seeded recipe).  With query and key lengths
@@ -77,6 +82,9 @@ def parse_args(argv=None):
                    help="with --ring: spread the partial-result launches over K streams")
     p.add_argument("--splits", type=int, default=None, metavar="S",
                    help="time the split-KV path (fa2_fwd_splitkv) with S splits; 0 = the pages' rule")
+    p.add_argument("--settle-seconds", type=float, default=1.0,
+                   help="before the warm-up steps, run steps for this many seconds so the clocks "
+                        "reach their sustained level (reported as 'settle'; 0 disables it)")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target duration of the CPU-oracle baseline sample (0 disables it)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -136,11 +144,15 @@ def metric_flops(B: int, H: int, Nq: int, Nk: int, d: int, causal: bool) -> floa
     return 4.0 * B * H * pairs * d
 
 
-def cpu_baseline(w, q, k, v, causal: bool, scale: float, target_s: float):
+def cpu_baseline(w, q, k, v, o_gpu, l_gpu, causal: bool, scale: float, target_s: float):
     """Time the fp64 oracle on whole (batch, head) slices until ~target_s seconds pass.
 
-    q, k, v are the CPU copies of the very inputs the GPU run used.
+    q, k, v are the CPU copies of the very inputs the GPU run used; o_gpu and
+    l_gpu are the CPU copies of the outputs of the last timed step.  The oracle's
+    results for the slices it computed are compared with those outputs element
+    by element, which gives the parity of the timed run (returned separately).
     """
+    import numpy as np
     from threadpoolctl import threadpool_info
 
     from oracle import attention_fp64
@@ -149,17 +161,31 @@ def cpu_baseline(w, q, k, v, causal: bool, scale: float, target_s: float):
     Nk = k.shape[2]
     attention_fp64(q[:1, :1, :64], k[:1, :1, :64], v[:1, :1, :64], causal=causal)  # warm-up
     heads = 0
+    err_o = err_l = 0.0
+    finite = True
     t0 = time.perf_counter()
     elapsed = 0.0
-    while heads < B * H and (heads == 0 or elapsed < target_s):
+    spent = 0.0  # oracle time only (the comparison is not timed)
+    while heads < B * H and (heads == 0 or spent < target_s):
         b, h = divmod(heads, H)
-        attention_fp64(q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1],
-                       causal=causal, scale=scale)
+        t1 = time.perf_counter()
+        O, L = attention_fp64(q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1],
+                              causal=causal, scale=scale)
+        spent += time.perf_counter() - t1
+        og = o_gpu[b, h].double().numpy()
+        lg = l_gpu[b, h].double().numpy()
+        finite = finite and bool(np.isfinite(og).all())
+        err_o = max(err_o, float(np.abs(og - O[0, 0]).max(initial=0.0)))
+        seen = np.isfinite(L[0, 0])
+        if seen.any():
+            err_l = max(err_l, float(np.abs(lg[seen] - L[0, 0][seen]).max()))
+        if not np.array_equal(np.isfinite(lg), seen):
+            finite = False
         heads += 1
-        elapsed = time.perf_counter() - t0
+    elapsed = spent
     flops = metric_flops(1, heads, Nq, Nk, d, causal)
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    return {
+    base = {
         "value": flops / elapsed / 1e12,
         "unit": "TFLOP/s",
         "cores": int(threads),
@@ -171,6 +197,118 @@ def cpu_baseline(w, q, k, v, causal: bool, scale: float, target_s: float):
         "blas_threads": int(threads),
         "host_cpus": len(os.sched_getaffinity(0)),
     }
+    tol_o, tol_l = TOLERANCE[q_dtype_name(q)]
+    parity = {"slices": heads, "of": B * H, "rows": heads * Nq,
+              "max_abs_err_O": err_o, "max_abs_err_L": err_l, "tol_O": tol_o, "tol_L": tol_l,
+              "ok": bool(finite and err_o <= tol_o and err_l <= tol_l),
+              "compared": "the outputs of the last timed step, element by element, against "
+                          "the fp64 oracle on the slices of the CPU baseline"}
+    return base, parity
+
+
+def q_dtype_name(q) -> str:
+    import torch
+
+    return {torch.bfloat16: "bf16", torch.float16: "fp16", torch.float32: "fp32"}[q.dtype]
+
+
+# Parity tolerances (max-abs on O, max-abs on L): bf16 as the target states;
+# fp16 half of it (a finer output rounding); fp32 the exact mode's bound.
+TOLERANCE = {"bf16": (2e-2, 1e-3), "fp16": (1e-2, 1e-3), "fp32": (1e-5, 1e-5)}
+
+
+class ClockSampler:
+    """Samples the GPU's current graphics (shader) clock and socket power from a
+    host thread, through the amdsmi library, while the benchmark runs.
+
+    The device is matched to torch's device 0 by PCI bus address.  Any failure
+    (no amdsmi, no permission) leaves the samples empty and records why.
+    """
+
+    def __init__(self, dev_index: int = 0, period_s: float = 0.001):
+        import threading
+
+        self.samples = []  # (perf_counter seconds, MHz, watts or None)
+        self.error = None
+        self.period = period_s
+        self._stop = threading.Event()
+        self._thread = None
+        self._handle = None
+        try:
+            import amdsmi
+            import torch
+
+            self._amdsmi = amdsmi
+            amdsmi.amdsmi_init()
+            props = torch.cuda.get_device_properties(dev_index)
+            want = (props.pci_domain_id, props.pci_bus_id, props.pci_device_id)
+            for hnd in amdsmi.amdsmi_get_processor_handles():
+                bdf = amdsmi.amdsmi_get_gpu_device_bdf(hnd)  # "dddd:bb:dd.f"
+                dom, bus, rest = bdf.split(":")
+                if (int(dom, 16), int(bus, 16), int(rest.split(".")[0], 16)) == want:
+                    self._handle = hnd
+                    break
+            if self._handle is None:
+                self.error = f"no amdsmi device at PCI {want}"
+        except Exception as e:  # noqa: BLE001 - any failure only disables sampling
+            self.error = f"{type(e).__name__}: {e}"
+
+    def _read(self):
+        a = self._amdsmi
+        clk = a.amdsmi_get_clock_info(self._handle, a.AmdSmiClkType.SYS)
+        mhz = clk.get("clk") if isinstance(clk, dict) else None
+        watts = None
+        try:
+            pw = a.amdsmi_get_power_info(self._handle)
+            for key in ("current_socket_power", "average_socket_power"):
+                if isinstance(pw.get(key), (int, float)):
+                    watts = float(pw[key])
+                    break
+        except Exception:  # noqa: BLE001
+            pass
+        return mhz, watts
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                mhz, watts = self._read()
+                if isinstance(mhz, (int, float)):
+                    self.samples.append((time.perf_counter(), float(mhz), watts))
+            except Exception as e:  # noqa: BLE001
+                self.error = f"{type(e).__name__}: {e}"
+                return
+            self._stop.wait(self.period)
+
+    def start(self):
+        import threading
+
+        if self._handle is not None:
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+        return self
+
+    def stop(self):
+        self._stop.set()
+        if self._thread is not None:
+            self._thread.join()
+        try:
+            if self._handle is not None:
+                self._amdsmi.amdsmi_shut_down()
+        except Exception:  # noqa: BLE001
+            pass
+
+    def window(self, t0: float, t1: float):
+        """Clock statistics of the samples taken between perf_counter times t0 and t1."""
+        xs = [(mhz, w) for (t, mhz, w) in self.samples if t0 <= t <= t1]
+        if not xs:
+            return {"samples": 0, "error": self.error}
+        mhz = sorted(x[0] for x in xs)
+        watts = [x[1] for x in xs if x[1] is not None]
+        out = {"samples": len(mhz), "mean_mhz": round(sum(mhz) / len(mhz), 1),
+               "min_mhz": mhz[0], "max_mhz": mhz[-1]}
+        if watts:
+            out["mean_socket_w"] = round(sum(watts) / len(watts), 1)
+        return out
 
 
 def main(argv=None) -> int:
@@ -286,21 +424,44 @@ def main(argv=None) -> int:
         def step():
             fa2_fwd(q, k, v, o, lse, causal=causal, scale=scale)
 
+    props = torch.cuda.get_device_properties(dev)
+    clock = ClockSampler(0).start()
+    t_settle = time.perf_counter()
+    settled = 0
+    if args.settle_seconds > 0:
+        # Untimed, reported: enough launches for the clocks to reach their sustained
+        # level (a fresh GPU starts from idle clocks).  Synchronised every 16 launches
+        # so that the queue stays short.
+        while True:
+            for _ in range(16):
+                step()
+            settled += 16
+            torch.cuda.synchronize()
+            if time.perf_counter() - t_settle >= args.settle_seconds:
+                break
+    settle_s = time.perf_counter() - t_settle
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
+    # One event between consecutive launches, all on the stream the kernels are
+    # enqueued on: launch i runs between events i and i+1.
+    events = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
+    events[0].record(stream)
+    for i in range(args.steps):
         step()
-    ev1.record(stream)
+        events[i + 1].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kernel_ms = ev0.elapsed_time(ev1) / args.steps  # average launch duration on the stream
+    t1 = time.perf_counter()
+    wall = t1 - t0
+    clock.stop()
+    launch_ms = [events[i].elapsed_time(events[i + 1]) for i in range(args.steps)]
+    kernel_ms = sum(launch_ms) / len(launch_ms)  # average launch duration on the stream
+    srt = sorted(launch_ms)
+    median_ms = (srt[(len(srt) - 1) // 2] + srt[len(srt) // 2]) / 2
     ms_per_step = wall * 1e3 / args.steps
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (kernel_ms * 1e-3) / 1e12
@@ -324,7 +485,9 @@ def main(argv=None) -> int:
         waves = 4 if splits is not None else block_m // 32
         cus = torch.cuda.get_device_properties(0).multi_processor_count
         items = B * H * ((Nq + block_m - 1) // block_m)
-        occ = 1 if d == 256 and (splits is not None or items < 2 * cus) else 2
+        # The same rule as the library's dispatch: three per SIMD for d = 32 (168
+        # VGPRs), one for d = 256 with splits or on small grids, two otherwise.
+        occ = 3 if d == 32 else (1 if d == 256 and (splits is not None or items < 2 * cus) else 2)
         kname = (f"fa2_fwd_kernel<{KERNEL_TYPE[dtype]}, {d}, {c}, "
                  f"{'true' if splits is not None else 'false'}, {waves}, {occ}>")
     if splits is not None:
@@ -347,6 +510,10 @@ def main(argv=None) -> int:
         roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic}
     roofline.update({"kernel": kname, "kernel_ms": round(kernel_ms, 5),
+                     "launch_ms": {"mean": round(kernel_ms, 5), "median": round(median_ms, 5),
+                                   "min": round(srt[0], 5), "max": round(srt[-1], 5),
+                                   "n": len(srt)},
+                     "achieved_at_median": round(flops / (median_ms * 1e-3) / 1e12, 2),
                      "kernel_source_hash": kernel_source_hash(dtype)})
     name = w.name if not overridden else f"{w.name}-variant"
     out = {
@@ -373,9 +540,17 @@ def main(argv=None) -> int:
                    **({"path": "backward"} if args.backward else {})},
         "pct_of_peak": round(100.0 * tflops / peak, 2),
         "roofline": roofline,
+        "device": {"name": props.name, "arch": props.gcnArchName,
+                   "compute_units": props.multi_processor_count,
+                   "gfx_clock_timed": clock.window(t0, t1),
+                   "gfx_clock_settle": clock.window(t_settle, t_settle + settle_s)},
+        "settle": {"seconds": round(settle_s, 3), "launches": settled,
+                   "note": "untimed launches before the warm-up, so the clocks reach their "
+                           "sustained level"},
     }
     if args.cpu_seconds > 0 and not args.backward and not args.ring:
-        out["cpu_baseline"] = cpu_baseline(w, q_cpu, k_cpu, v_cpu, causal, scale, args.cpu_seconds)
+        out["cpu_baseline"], out["parity"] = cpu_baseline(
+            w, q_cpu, k_cpu, v_cpu, o.cpu(), lse.cpu(), causal, scale, args.cpu_seconds)
     print(json.dumps(out), flush=True)
     return 0
 
