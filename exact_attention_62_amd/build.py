@@ -22,7 +22,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfa2.so")
 
 SOURCES = ["fa2_api.cpp", "fa2_fwd_bf16.hip", "fa2_fwd_fp16.hip", "fa2_fwd_f32.hip",
-           "fa2_combine.hip", "fa2_bwd.hip", "fa2_decode.hip"]
+           "fa2_combine.hip", "fa2_bwd.hip", "fa2_decode.hip", "fa2_scratch.hip"]
 ARCH = "gfx950"
 
 

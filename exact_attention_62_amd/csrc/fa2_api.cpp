@@ -34,6 +34,7 @@ fa2_status_t fail_hip(hipError_t e, const char* what) {
 int64_t elem_size(fa2_dtype_t t) { return t == FA2_FP32 ? 4 : 2; }
 
 constexpr int64_t kMaxLen = (int64_t(1) << 31) / 256;  // per-slice offsets are 32-bit in the kernels
+static_assert(fa2::kScratchBytes == (int64_t)FA2_NOALLOC_SCRATCH_BYTES, "scratch size in fa2.h");
 
 // Checks that need no HIP call, for Nq queries over Nk keys.  On success
 // fills the query block size.
@@ -291,6 +292,63 @@ fa2_status_t fwd_common(const void* Q, const void* K, const void* V, void* O, fl
   return FA2_OK;
 }
 
+// fa2_fwd_splitkv with the partial results in the caller's workspace, or
+// (library_scratch) in the library's own device scratch, whose size bounds
+// the problem.  Neither path allocates device memory.
+fa2_status_t splitkv_common(const void* Q, const void* K, const void* V, void* O, float* L,
+                            int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int causal,
+                            float scale, fa2_dtype_t dtype, int num_splits, void* workspace,
+                            size_t workspace_bytes, void* stream, bool library_scratch) {
+  if (dtype == FA2_FP32)
+    return fail(FA2_ENOTSUP, "split-KV is implemented for FA2_BF16 and FA2_FP16 only");
+  int64_t bm = 0;
+  fa2_status_t s = check_shape(B, H, Nq, Nk, d, dtype, &bm);
+  if (s != FA2_OK) return s;
+  if (num_splits < 0) return fail(FA2_EINVAL, "num_splits=%d must be >= 0", num_splits);
+  if (B * H * Nq == 0) return FA2_OK;
+  if (num_splits == 0) {
+    s = heuristic_splits(B, H, Nq, Nk, d, &num_splits);
+    if (s != FA2_OK) return s;
+  }
+  s = check_splits(B, H, Nq, num_splits);
+  if (s != FA2_OK) return s;
+  const int64_t need = splitkv_bytes(B, H, Nq, d, num_splits);
+  if (library_scratch) {
+    if (need > fa2::kScratchBytes)
+      return fail(FA2_EINVAL,
+                  "the partial results need %lld bytes (num_splits * B*H*Nq * (d + 1) * 4), "
+                  "more than the library scratch of %lld bytes",
+                  (long long)need, (long long)fa2::kScratchBytes);
+  } else {
+    if (workspace == nullptr) return fail(FA2_EINVAL, "workspace is NULL");
+    if (static_cast<int64_t>(workspace_bytes) < need)
+      return fail(FA2_EINVAL, "workspace of %llu bytes is smaller than the %lld bytes needed",
+                  (unsigned long long)workspace_bytes, (long long)need);
+  }
+  fa2::FwdArgs a;
+  s = prepare(Q, K, V, O, L, B, H, Nq, Nk, d, causal, scale, dtype, stream,
+              library_scratch ? nullptr : workspace, library_scratch ? 0 : need, &a);
+  if (s != FA2_OK) return s;
+  if (library_scratch) {
+    // The library's array on this device (its address looked up once per device).
+    hipError_t e = fa2::scratch_address(&workspace);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      return fail_hip(e, "scratch address lookup");
+    }
+  }
+  a.num_splits = num_splits;
+  use_split_blocks(&a);
+  a.ws_O = static_cast<float*>(workspace);
+  a.ws_L = a.ws_O + static_cast<size_t>(num_splits) * B * H * Nq * d;
+  (void)hipGetLastError();
+  hipError_t e = launch_fwd(a);
+  if (e == hipSuccess && a.Nk > 0) e = fa2::launch_combine(a);
+  if (e == hipSuccess) e = hipGetLastError();
+  if (e != hipSuccess) return fail_hip(e, "kernel launch");
+  return FA2_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -337,37 +395,17 @@ fa2_status_t fa2_fwd_splitkv(const void* Q, const void* K, const void* V, void* 
                              float scale, fa2_dtype_t dtype, int num_splits, void* workspace,
                              size_t workspace_bytes, void* stream) {
   g_last_error[0] = '\0';
-  if (dtype == FA2_FP32)
-    return fail(FA2_ENOTSUP, "split-KV is implemented for FA2_BF16 and FA2_FP16 only");
-  int64_t bm = 0;
-  fa2_status_t s = check_shape(B, H, Nq, Nk, d, dtype, &bm);
-  if (s != FA2_OK) return s;
-  if (num_splits < 0) return fail(FA2_EINVAL, "num_splits=%d must be >= 0", num_splits);
-  if (B * H * Nq == 0) return FA2_OK;
-  if (num_splits == 0) {
-    s = heuristic_splits(B, H, Nq, Nk, d, &num_splits);
-    if (s != FA2_OK) return s;
-  }
-  s = check_splits(B, H, Nq, num_splits);
-  if (s != FA2_OK) return s;
-  const int64_t need = splitkv_bytes(B, H, Nq, d, num_splits);
-  if (workspace == nullptr) return fail(FA2_EINVAL, "workspace is NULL");
-  if (static_cast<int64_t>(workspace_bytes) < need)
-    return fail(FA2_EINVAL, "workspace of %llu bytes is smaller than the %lld bytes needed",
-                (unsigned long long)workspace_bytes, (long long)need);
-  fa2::FwdArgs a;
-  s = prepare(Q, K, V, O, L, B, H, Nq, Nk, d, causal, scale, dtype, stream, workspace, need, &a);
-  if (s != FA2_OK) return s;
-  a.num_splits = num_splits;
-  use_split_blocks(&a);
-  a.ws_O = static_cast<float*>(workspace);
-  a.ws_L = a.ws_O + static_cast<size_t>(num_splits) * B * H * Nq * d;
-  (void)hipGetLastError();
-  hipError_t e = launch_fwd(a);
-  if (e == hipSuccess && a.Nk > 0) e = fa2::launch_combine(a);
-  if (e == hipSuccess) e = hipGetLastError();
-  if (e != hipSuccess) return fail_hip(e, "kernel launch");
-  return FA2_OK;
+  return splitkv_common(Q, K, V, O, L, B, H, Nq, Nk, d, causal, scale, dtype, num_splits,
+                        workspace, workspace_bytes, stream, /*library_scratch=*/false);
+}
+
+fa2_status_t fa2_fwd_splitkv_noalloc(const void* Q, const void* K, const void* V, void* O,
+                                     float* L, int64_t B, int64_t H, int64_t Nq, int64_t Nk,
+                                     int64_t d, int causal, float scale, fa2_dtype_t dtype,
+                                     int num_splits, void* stream) {
+  g_last_error[0] = '\0';
+  return splitkv_common(Q, K, V, O, L, B, H, Nq, Nk, d, causal, scale, dtype, num_splits,
+                        nullptr, 0, stream, /*library_scratch=*/true);
 }
 
 fa2_status_t fa2_fwd_partial(const void* Q, const void* K, const void* V, float* O_part,

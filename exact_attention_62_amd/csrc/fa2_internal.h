@@ -74,6 +74,12 @@ struct BwdArgs {
 // Compute units of the current device (queried once per device).
 hipError_t cu_count(int* cus);
 
+// Size of the library-owned device scratch of fa2_fwd_splitkv_noalloc (one
+// copy per device), and its device address on the current device (looked up
+// once per device; fa2_scratch.hip).
+constexpr int64_t kScratchBytes = int64_t(32) << 20;
+hipError_t scratch_address(void** ptr);
+
 // Enqueue the kernel; returns the launch's hipError_t.
 hipError_t launch_fwd_bf16(const FwdArgs& a);
 hipError_t launch_fwd_fp16(const FwdArgs& a);

@@ -18,7 +18,7 @@ import torch
 
 __all__ = ["FA2Error", "FlashAttention", "attention", "attention_backward", "attention_partial",
            "fa2_bwd", "fa2_bwd_workspace_size", "fa2_fwd", "fa2_fwd_cross", "fa2_fwd_partial",
-           "fa2_fwd_splitkv", "fa2_launch_shape", "fa2_merge", "fa2_num_splits",
+           "fa2_fwd_splitkv", "fa2_fwd_splitkv_noalloc", "fa2_launch_shape", "fa2_merge", "fa2_num_splits",
            "fa2_splitkv_workspace_size", "fa2_strerror", "fa2_last_error", "library_path",
            "load_library", "merge_partials"]
 
@@ -71,6 +71,10 @@ def load_library() -> ctypes.CDLL:
                                         ctypes.c_int, ctypes.c_float, ctypes.c_int, ctypes.c_int,
                                         vp, ctypes.c_size_t, vp]
         lib.fa2_fwd_splitkv.restype = ctypes.c_int
+        lib.fa2_fwd_splitkv_noalloc.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                                                ctypes.c_int, ctypes.c_float, ctypes.c_int,
+                                                ctypes.c_int, vp]
+        lib.fa2_fwd_splitkv_noalloc.restype = ctypes.c_int
         lib.fa2_splitkv_workspace_size.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int,
                                                    ctypes.POINTER(ctypes.c_size_t)]
         lib.fa2_splitkv_workspace_size.restype = ctypes.c_int
@@ -239,6 +243,29 @@ def fa2_fwd_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.
                                  int(num_splits), _ptr(workspace),
                                  workspace.numel() * workspace.element_size(),
                                  ctypes.c_void_p(stream.cuda_stream))
+    _check(st)
+
+
+def fa2_fwd_splitkv_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+                            lse: torch.Tensor, num_splits: int = 0, causal: bool = False,
+                            scale: float | None = None,
+                            stream: torch.cuda.Stream | None = None) -> None:
+    """fa2_fwd_splitkv with the partial results in the library's own device scratch
+    (FA2_NOALLOC_SCRATCH_BYTES per GPU) instead of a workspace: the call allocates
+    nothing.  Calls that overlap on one GPU share that scratch and race.  Writes o
+    and lse in place."""
+    B, H, Nq, Nk, d = _check_tensors(q, k, v, o, lse)
+    dev = q.device
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    lib = load_library()
+    with torch.cuda.device(dev):
+        st = lib.fa2_fwd_splitkv_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H,
+                                         Nq, Nk, d, 1 if causal else 0, float(scale),
+                                         _DTYPES[q.dtype], int(num_splits),
+                                         ctypes.c_void_p(stream.cuda_stream))
     _check(st)
 
 

@@ -145,6 +145,35 @@ fa2_status_t fa2_fwd_splitkv(const void* Q, const void* K, const void* V, void* 
                              float scale, fa2_dtype_t dtype, int num_splits, void* workspace,
                              size_t workspace_bytes, void* stream);
 
+/* Size in bytes of the device scratch fa2_fwd_splitkv_noalloc uses (32 MiB). */
+#define FA2_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+/*
+ * fa2_fwd_splitkv_noalloc - fa2_fwd_splitkv for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc) and so cannot provide a workspace either.
+ *
+ * The partial results go to a scratch array that the library itself holds in
+ * device memory, FA2_NOALLOC_SCRATCH_BYTES per GPU, for the life of the
+ * process; the call allocates nothing (no hipMalloc, no allocating library
+ * routine).  The split kernel writes every partial entry the merge reads, so
+ * nothing needs clearing between calls.
+ *
+ *   Q, K, V, O, L, B, H, Nq, Nk, d, causal, scale, dtype, num_splits, stream:
+ *            as for fa2_fwd_splitkv, which computes the same result with the
+ *            same kernels.
+ * Limit: num_splits * B*H*Nq * (d + 1) * 4 (fa2_splitkv_workspace_size) must
+ * not exceed FA2_NOALLOC_SCRATCH_BYTES; larger problems return FA2_EINVAL
+ * before any HIP call (num_splits == 0 first takes fa2_num_splits's choice,
+ * a device query).
+ * Concurrency: every call on one GPU shares that GPU's scratch, so calls whose
+ * execution overlaps on one GPU (from several host threads, or on several
+ * streams without ordering) race and give wrong results; order them on one
+ * stream, or use fa2_fwd_splitkv with a workspace each.
+ */
+fa2_status_t fa2_fwd_splitkv_noalloc(const void* Q, const void* K, const void* V, void* O,
+                                     float* L, int64_t B, int64_t H, int64_t Nq, int64_t Nk,
+                                     int64_t d, int causal, float scale, fa2_dtype_t dtype,
+                                     int num_splits, void* stream);
 /*
  * fa2_splitkv_workspace_size - bytes of workspace fa2_fwd_splitkv needs with
  * num_splits splits: num_splits * B*H*Nq * (d + 1) * 4 (the float32 partial

@@ -34,7 +34,7 @@ def _declared_functions():
 def test_header_declares_the_boundary():
     assert _declared_functions() == ["fa2_bwd", "fa2_bwd_cross", "fa2_bwd_workspace_size", "fa2_fwd",
                                      "fa2_fwd_cross", "fa2_fwd_partial", "fa2_fwd_splitkv",
-                                     "fa2_last_error", "fa2_launch_shape", "fa2_merge",
+                                     "fa2_fwd_splitkv_noalloc", "fa2_last_error", "fa2_launch_shape", "fa2_merge",
                                      "fa2_num_splits", "fa2_splitkv_workspace_size",
                                      "fa2_strerror"]
 
@@ -238,6 +238,47 @@ def test_workspace_size_rejects_split_counts(s):
 def test_splitkv_invalid_arguments_before_any_hip_call(kw, status, needle):
     assert _split(**kw) == status
     assert needle in F.fa2_last_error()
+
+
+def _split_noalloc(num_splits=2, dtype=F.FA2_BF16, **kw):
+    args = dict(q=FAKE, k=FAKE + 0x100000, v=FAKE + 0x200000, o=FAKE + 0x300000,
+                L=FAKE + 0x400000, B=1, H=1, Nq=16, Nk=16, d=64, causal=0, scale=0.125)
+    args.update(kw)
+    return F.load_library().fa2_fwd_splitkv_noalloc(
+        args["q"], args["k"], args["v"], args["o"], args["L"], args["B"], args["H"], args["Nq"],
+        args["Nk"], args["d"], args["causal"], args["scale"], dtype, num_splits, None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(dtype=F.FA2_FP32), F.FA2_ENOTSUP, "FA2_BF16 and FA2_FP16 only"),
+    (dict(num_splits=-1), F.FA2_EINVAL, "num_splits=-1"),
+    (dict(num_splits=129), F.FA2_EINVAL, "num_splits=129"),
+    (dict(q=None), F.FA2_EINVAL, "Q is NULL"),
+    (dict(o=FAKE), F.FA2_EINVAL, "overlaps"),
+    # 8 * 64 * 1024 * 129 * 4 bytes of partial results: over the 32 MiB scratch
+    (dict(B=4, H=16, Nq=1024, Nk=1024, d=128, num_splits=8), F.FA2_EINVAL, "library scratch"),
+])
+def test_splitkv_noalloc_invalid_arguments_before_any_hip_call(kw, status, needle):
+    assert _split_noalloc(**kw) == status
+    assert needle in F.fa2_last_error()
+
+
+def test_splitkv_noalloc_limit_is_inclusive():
+    # 2 splits * 64527 rows * 65 * 4 bytes fit the 32 MiB scratch: the size check passes
+    # and the call fails later, on the fake pointers (or on the missing device).
+    nq = (32 << 20) // (4 * 65 * 2)
+    step = 0x1000000
+    st = _split_noalloc(q=FAKE, k=FAKE + step, v=FAKE + 2 * step, o=FAKE + 3 * step,
+                        L=FAKE + 4 * step, Nq=nq, Nk=64, num_splits=2)
+    assert st != F.FA2_OK and "library scratch" not in F.fa2_last_error()
+    st = _split_noalloc(q=FAKE, k=FAKE + step, v=FAKE + 2 * step, o=FAKE + 3 * step,
+                        L=FAKE + 4 * step, Nq=nq + 1, Nk=64, num_splits=2)
+    assert st == F.FA2_EINVAL and "library scratch" in F.fa2_last_error()
+
+
+def test_splitkv_noalloc_scratch_size_constant():
+    text = open(HEADER).read()
+    assert "#define FA2_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)" in text
 
 
 def test_splitkv_empty_problem_is_a_no_op():
