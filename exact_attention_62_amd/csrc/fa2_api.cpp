@@ -14,6 +14,7 @@
 
 #include "fa2.h"
 #include "fa2_internal.h"
+#include "fa2_schedule.h"
 
 namespace {
 
@@ -498,6 +499,82 @@ fa2_status_t fa2_merge(const float* O_parts, const float* L_parts, int num_parts
   e = fa2::launch_combine(a);
   if (e == hipSuccess) e = hipGetLastError();
   if (e != hipSuccess) return fail_hip(e, "kernel launch");
+  return FA2_OK;
+}
+
+fa2_status_t fa2_schedule_map(int64_t items, int64_t grid, int32_t* visits, int32_t* workgroup,
+                              int32_t* position) {
+  g_last_error[0] = '\0';
+  if (items < 1 || items > INT32_MAX || grid < 1 || grid > INT32_MAX)
+    return fail(FA2_EINVAL, "items=%lld and grid=%lld must be in 1..2^31-1", (long long)items,
+                (long long)grid);
+  if (!visits) return fail(FA2_EINVAL, "visits is NULL");
+  for (int64_t i = 0; i < items; ++i) visits[i] = 0;
+  for (int g = 0; g < static_cast<int>(grid); ++g) {
+    const fa2::sched::Walk w = fa2::sched::walk_of(static_cast<int>(items), static_cast<int>(grid), g);
+    for (int k = 0;; ++k) {
+      const int it = fa2::sched::item_of(w, k);
+      if (it < 0) break;
+      if (it >= items) return fail(FA2_EINVAL, "workgroup %d step %d maps outside the items", g, k);
+      ++visits[it];
+      if (workgroup) workgroup[it] = g;
+      if (position) position[it] = k;
+    }
+  }
+  return FA2_OK;
+}
+
+fa2_status_t fa2_schedule_blocks(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                                 fa2_dtype_t dtype, int causal, int num_splits, int64_t grid,
+                                 int64_t* blocks, int64_t* items) {
+  g_last_error[0] = '\0';
+  if (dtype == FA2_FP32)
+    return fail(FA2_ENOTSUP, "the float32 kernel launches one workgroup per item (no schedule)");
+  int64_t bm = 0;
+  fa2_status_t s = check_shape(B, H, Nq, Nk, d, dtype, &bm);
+  if (s != FA2_OK) return s;
+  if (causal != 0 && causal != 1) return fail(FA2_EINVAL, "causal=%d must be 0 or 1", causal);
+  const bool split = num_splits > 0;
+  if (split) {
+    s = check_splits(B, H, Nq, num_splits);
+    if (s != FA2_OK) return s;
+    bm = fa2::kBlockM_mfma;  // the split kernel's query blocks
+  } else if (num_splits < 0) {
+    return fail(FA2_EINVAL, "num_splits=%d must be >= 0", num_splits);
+  }
+  if (Nk < 1 || B * H * Nq < 1) return fail(FA2_EINVAL, "the schedule needs Nk >= 1 and B*H*Nq >= 1");
+  if (grid < 1 || grid > INT32_MAX) return fail(FA2_EINVAL, "grid=%lld must be >= 1", (long long)grid);
+  if (!blocks || !items) return fail(FA2_EINVAL, "blocks and items must not be NULL");
+  const int bn = fa2::mfma_block_n(static_cast<int>(d));
+  const int nmb = static_cast<int>((Nq + bm - 1) / bm);
+  const int nkb = static_cast<int>((Nk + bn - 1) / bn);
+  const int splits = split ? num_splits : 1;
+  const int64_t total = B * H * nmb * splits;
+  if (total > INT32_MAX) return fail(FA2_EINVAL, "%lld items exceed 2^31 - 1", (long long)total);
+  *items = total;
+  for (int g = 0; g < static_cast<int>(grid); ++g) {
+    const fa2::sched::Walk w = fa2::sched::walk_of(static_cast<int>(total), static_cast<int>(grid), g);
+    int64_t sum = 0;
+    for (int k = 0;; ++k) {
+      const int it = fa2::sched::item_of(w, k);
+      if (it < 0) break;
+      const fa2::sched::Item item = fa2::sched::decode(it, nmb, splits, causal != 0, split);
+      const int jt = fa2::sched::blocks_of(item.m, static_cast<int>(Nq), static_cast<int>(Nk - Nq),
+                                           nkb, static_cast<int>(bm), bn, causal != 0, split);
+      const fa2::sched::Range r = fa2::sched::range_of(jt, item.split, splits, split);
+      sum += r.end - r.beg;
+    }
+    blocks[g] = sum;
+  }
+  return FA2_OK;
+}
+
+fa2_status_t fa2_bwd_block_map(int64_t G, int32_t* logical) {
+  g_last_error[0] = '\0';
+  if (G < 1 || G > INT32_MAX) return fail(FA2_EINVAL, "G=%lld must be in 1..2^31-1", (long long)G);
+  if (!logical) return fail(FA2_EINVAL, "logical is NULL");
+  for (int64_t id = 0; id < G; ++id)
+    logical[id] = fa2::sched::xcd_block(static_cast<int>(id), static_cast<int>(G));
   return FA2_OK;
 }
 

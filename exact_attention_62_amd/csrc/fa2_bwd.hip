@@ -45,6 +45,7 @@
 
 #include "fa2_device.h"
 #include "fa2_internal.h"
+#include "fa2_schedule.h"
 
 namespace fa2 {
 namespace {
@@ -326,14 +327,12 @@ __device__ __forceinline__ void store_rows(const f32x16_t (&acc)[D / 32], float 
 }
 
 // Workgroup ids are dealt to the 8 XCDs round-robin (id % 8), and each XCD has
-// its own L2.  The logical block index gives XCD x a contiguous range of
-// blocks, so the blocks of one head (which read the same Q/dO or K/V tiles)
-// run on one XCD and share its L2.  A bijection on [0, G) for any G; only
-// speed depends on the dispatcher actually dealing ids this way.
-__device__ __forceinline__ int xcd_block(int id, int G) {
-  const int x = id & 7, i = id >> 3, q = G >> 3, r = G & 7;
-  return x < r ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
-}
+// its own L2.  The logical block index (sched::xcd_block, fa2_schedule.h) gives
+// XCD x a contiguous range of blocks, so the blocks of one head (which read the
+// same Q/dO or K/V tiles) run on one XCD and share its L2.  A bijection on
+// [0, G) for any G; only speed depends on the dispatcher actually dealing ids
+// this way.
+using sched::xcd_block;
 
 // ---------------------------------------------------------------- D = rowsum(dO * O)
 // Writes -D (the dK/dV kernel starts its dP accumulators from it) and

@@ -97,6 +97,7 @@
 
 #include "fa2_device.h"
 #include "fa2_internal.h"
+#include "fa2_schedule.h"
 
 namespace fa2 {
 namespace {
@@ -245,16 +246,11 @@ fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
   // snake order (group k: slot s takes position s, or P-1-s when k is odd), so
   // that heavy and light causal blocks alternate per workgroup.
   // (With fewer than 8 workgroups the ranges are split over that many.)
-  const int nx = gridDim.x < 8 ? (int)gridDim.x : 8;
-  const int xcd = blockIdx.x % nx;
-  const int lslot = blockIdx.x / nx;
-  const int P = ((int)gridDim.x - xcd + nx - 1) / nx;  // workgroups on this XCD
-  const int per = total_items / nx, rem = total_items % nx;
-  const int x_base = xcd * per + (xcd < rem ? xcd : rem);
-  const int x_items = per + (xcd < rem ? 1 : 0);
+  // (The walk and the item mapping are in fa2_schedule.h, shared with the
+  // library's host-side schedule queries.)
+  const sched::Walk walk = sched::walk_of(total_items, (int)gridDim.x, (int)blockIdx.x);
   auto logical_of = [&](int k) -> int {  // the k-th item of this workgroup, or -1
-    const int pos = k * P + ((k & 1) ? P - 1 - lslot : lslot);
-    return pos < x_items ? x_base + pos : -1;
+    return sched::item_of(walk, k);
   };
 
   // ---- per-item state
@@ -270,42 +266,24 @@ fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
   // logical item -> (batch*head, query block, split): splits fastest, then the
   // query blocks of a head (heaviest causal block first), then the heads.
   auto decode = [&](int logical, int& bh_, int& m_, int& s_) __attribute__((always_inline)) {
-    int mi = logical;
-    s_ = 0;
-    if constexpr (SPLIT) {
-      mi = logical / num_splits;
-      s_ = logical - mi * num_splits;
-    }
-    bh_ = mi / num_m_block;
-    mi -= bh_ * num_m_block;
-    m_ = CAUSAL ? num_m_block - 1 - mi : mi;
+    const sched::Item it = sched::decode(logical, num_m_block, num_splits, CAUSAL, SPLIT);
+    bh_ = it.bh;
+    m_ = it.m;
+    s_ = it.split;
   };
   // K/V blocks up to the last key that query block m sees.  A query block
-  // whose last row sees no key (causal, Nq > Nk) has none: with splits its
-  // items are empty; without, it runs block 0 fully masked, which leaves every
-  // row with l = 0 (O = 0, L = -inf) and keeps the empty-item path out of the
-  // plain kernel.  (Nk >= 1 here; the host handles Nk == 0.)
+  // whose last row sees no key has none: with splits its items are empty;
+  // without, it runs block 0 fully masked, which leaves every row with l = 0
+  // (O = 0, L = -inf) and keeps the empty-item path out of the plain kernel.
+  // (Nk >= 1 here; the host handles Nk == 0.)
   auto blocks_of = [&](int m_) __attribute__((always_inline)) -> int {
-    if (CAUSAL) {
-      const int last_key = min(Nq, (m_ + 1) * kBM) - 1 + off;
-      if (last_key < 0) return SPLIT ? 0 : 1;
-      return min(last_key / BN + 1, nkb);
-    }
-    return nkb;
+    return sched::blocks_of(m_, Nq, off, nkb, kBM, BN, CAUSAL, SPLIT);
   };
-  // KV blocks [beg, end) of split s of query block m: ceil(blocks / num_splits)
-  // blocks per split, so split 0 is empty only when the query block sees no
-  // key at all; later splits can be empty (SPLIT only).
+  // KV blocks [beg, end) of split s of query block m.
   auto range_of = [&](int m_, int s_, int& beg, int& end) __attribute__((always_inline)) {
-    const int jt = blocks_of(m_);
-    if constexpr (SPLIT) {
-      const int per = (jt + num_splits - 1) / num_splits;
-      beg = min(s_ * per, jt);
-      end = min(beg + per, jt);
-    } else {
-      beg = 0;
-      end = jt;
-    }
+    const sched::Range r = sched::range_of(blocks_of(m_), s_, num_splits, SPLIT);
+    beg = r.beg;
+    end = r.end;
   };
   auto set_item = [&](int logical) __attribute__((always_inline)) {
     int sp;

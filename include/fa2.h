@@ -263,6 +263,42 @@ fa2_status_t fa2_merge(const float* O_parts, const float* L_parts, int num_parts
 fa2_status_t fa2_launch_shape(int64_t B, int64_t H, int64_t N, int64_t d, fa2_dtype_t dtype,
                               int64_t* kBlockM, int64_t* num_m_block, int64_t* items);
 
+/*
+ * Host-only views of the work schedules (they make no HIP call and run on any
+ * host), computed by the same integer functions the kernels compile.
+ *
+ * fa2_schedule_map - the forward kernel's persistent grid: with `grid`
+ * workgroups over `items` work items (page "FlashAttention学习笔记(2)", section
+ * "V2中的thread blocks排布": one item per query block of one (batch, head), times
+ * the key/value splits of fa2_fwd_splitkv), workgroup g walks its XCD's
+ * contiguous range of items in snake-ordered rounds.  Writes, for each item i
+ * < items: visits[i], the number of workgroups that process it (1 in a correct
+ * schedule), and, where the pointers are not NULL, workgroup[i] and
+ * position[i], the workgroup that processes it and its place in that
+ * workgroup's sequence.  items and grid: 1..2^31-1 (FA2_EINVAL otherwise).
+ */
+fa2_status_t fa2_schedule_map(int64_t items, int64_t grid, int32_t* visits, int32_t* workgroup,
+                              int32_t* position);
+/*
+ * fa2_schedule_blocks - the key/value blocks each workgroup of the 16-bit
+ * forward kernel visits for a problem, summed over its items, when launched
+ * with `grid` workgroups: blocks[g] for g < grid, and *items, the number of
+ * work items.  B, H, Nq, Nk, d, dtype and causal are as for fa2_fwd_cross
+ * (Nk >= 1, B*H*Nq >= 1); num_splits 0 gives the plain kernel (kBlockM as
+ * fa2_launch_shape reports), 1..FA2_MAX_SPLITS the split-KV kernel.  The
+ * grid fa2_fwd uses is min(items, workgroups resident on the device).
+ * FA2_FP32 gives FA2_ENOTSUP (that kernel has one workgroup per item).
+ */
+fa2_status_t fa2_schedule_blocks(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                                 fa2_dtype_t dtype, int causal, int num_splits, int64_t grid,
+                                 int64_t* blocks, int64_t* items);
+/*
+ * fa2_bwd_block_map - the logical block (key block of the dK/dV kernel, query
+ * block of the dQ kernel) that workgroup id takes in a backward grid of G
+ * workgroups: logical[id] for id < G.  XCD x = id % 8 takes a contiguous range
+ * of logical blocks, so the blocks of one head share an L2.  G: 1..2^31-1.
+ */
+fa2_status_t fa2_bwd_block_map(int64_t G, int32_t* logical);
 /* fa2_strerror - static description of a status code (never NULL). */
 const char* fa2_strerror(fa2_status_t status);
 

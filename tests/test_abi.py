@@ -32,10 +32,12 @@ def _declared_functions():
 
 
 def test_header_declares_the_boundary():
-    assert _declared_functions() == ["fa2_bwd", "fa2_bwd_cross", "fa2_bwd_workspace_size", "fa2_fwd",
+    assert _declared_functions() == ["fa2_bwd", "fa2_bwd_block_map", "fa2_bwd_cross",
+                                     "fa2_bwd_workspace_size", "fa2_fwd",
                                      "fa2_fwd_cross", "fa2_fwd_partial", "fa2_fwd_splitkv",
                                      "fa2_fwd_splitkv_noalloc", "fa2_last_error", "fa2_launch_shape", "fa2_merge",
-                                     "fa2_num_splits", "fa2_splitkv_workspace_size",
+                                     "fa2_num_splits", "fa2_schedule_blocks",
+                                     "fa2_schedule_map", "fa2_splitkv_workspace_size",
                                      "fa2_strerror"]
 
 
