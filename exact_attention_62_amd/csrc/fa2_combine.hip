@@ -90,22 +90,30 @@ hipError_t dispatch(const FwdArgs& a) {
 }
 
 // Rows with no key at all (Nk == 0): O = 0, L = -inf.  One thread per 16
-// bytes of O (every row is a multiple of 64 bytes) and per row of L.
+// bytes of O (every row is a multiple of 64 bytes) and per row of L, in a
+// grid-stride loop over 64-bit indices (B*H*Nq may exceed 2^31).
 __global__ void __launch_bounds__(kThreads)
-fa2_fill_no_keys_kernel(u32x4_t* __restrict__ O, float* __restrict__ L, int64_t o_chunks, int rows) {
-  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (i < o_chunks) O[i] = u32x4_t{0u, 0u, 0u, 0u};
-  if (i < rows) L[i] = kNegInf;
+fa2_fill_no_keys_kernel(u32x4_t* __restrict__ O, float* __restrict__ L, int64_t o_chunks,
+                        int64_t rows) {
+  const int64_t n = o_chunks > rows ? o_chunks : rows;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += stride) {
+    if (i < o_chunks) O[i] = u32x4_t{0u, 0u, 0u, 0u};
+    if (i < rows) L[i] = kNegInf;
+  }
 }
 
 }  // namespace
 
 hipError_t launch_fill_no_keys(const FwdArgs& a) {
-  const int rows = a.BH * a.Nq;
-  const int64_t o_chunks = (int64_t)rows * a.d * (a.elem == kFP32 ? 4 : 2) / 16;
+  constexpr int64_t kMaxBlocks = 2048;  // the loop strides over the rest
+  const int64_t rows = (int64_t)a.BH * a.Nq;
+  const int64_t o_chunks = rows * a.d * (a.elem == kFP32 ? 4 : 2) / 16;
   const int64_t n = o_chunks > rows ? o_chunks : rows;
-  hipLaunchKernelGGL(fa2_fill_no_keys_kernel, dim3((unsigned)((n + kThreads - 1) / kThreads)),
-                     dim3(kThreads), 0, a.stream, (u32x4_t*)a.O, a.L, o_chunks, rows);
+  int64_t blocks = (n + kThreads - 1) / kThreads;
+  if (blocks > kMaxBlocks) blocks = kMaxBlocks;
+  hipLaunchKernelGGL(fa2_fill_no_keys_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, a.stream,
+                     (u32x4_t*)a.O, a.L, o_chunks, rows);
   return hipGetLastError();
 }
 

@@ -257,19 +257,39 @@ def test_eight_wavefronts_more_queries_than_keys():
     _cmp(o, lse, O, L, "bf16", "eight wavefronts, Nq > Nk")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 @pytest.mark.parametrize("causal", [False, True])
-def test_d256_two_wavefronts_per_simd_cross_lengths(causal):
+def test_d256_two_wavefronts_per_simd_cross_lengths(causal, dtype):
     """d = 256 on a grid of >= 2 items per CU (two wavefronts per SIMD, 256
-    VGPRs) with Nq != Nk and a ragged last block; sampled rows of four heads."""
+    VGPRs, the instantiation that spills a few registers) with Nq != Nk and a
+    ragged last block; sampled rows of four heads, bf16 and fp16."""
     B, H, Nq, Nk, d = 1, 32, 2100, 2500, 256
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     assert fa2_launch_shape(B, H, Nq, d)[2] >= 2 * cus  # 32 x 17 = 544 items
-    _say(f"d=256 two per SIMD B={B} H={H} Nq={Nq} Nk={Nk} causal={causal}")
-    q, k, v = make_random(B, H, Nq, d, seed=31 + causal, Nk=Nk)
+    _say(f"d=256 two per SIMD {dtype} B={B} H={H} Nq={Nq} Nk={Nk} causal={causal}")
+    q, k, v = make_random(B, H, Nq, d, seed=31 + causal, dtype=dtype, Nk=Nk)
     o, lse = _cross(q, k, v, causal=causal)
     rows = np.unique(np.concatenate([np.arange(0, 40), np.arange(1000, 1040),
                                      np.arange(Nq - 60, Nq)]))
     for h in (0, 7, 20, 31):
         O, L = attention_rows_fp64(q, k, v, 0, h, rows, causal=causal)
         idx = torch.as_tensor(rows)
-        _cmp(o[0, h][idx], lse[0, h][idx], O, L, "bf16", f"d=256 head {h}")
+        _cmp(o[0, h][idx], lse[0, h][idx], O, L, dtype, f"d=256 {dtype} head {h}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_no_keys_fill_grid_stride(dtype):
+    """Nk = 0 over more output than the fill kernel's capped grid covers in one
+    pass (2048 workgroups of 256 threads, 16 bytes each): the grid-stride loop
+    must still write O = 0 and L = -inf everywhere."""
+    B, H, Nq, d = 1, 3, 70000, 128
+    q = torch.randn((B, H, Nq, d)).to(torch.bfloat16 if dtype == "bf16" else torch.float32).cuda()
+    kv = torch.empty((B, H, 0, d), dtype=q.dtype, device="cuda")
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full((B, H, Nq), float("nan"), dtype=torch.float32, device="cuda")
+    assert o.numel() * o.element_size() // 16 > 2048 * 256
+    _say(f"no keys {dtype} B={B} H={H} Nq={Nq} d={d}")
+    fa2_fwd_cross(q, kv, kv, o, lse, causal=False)
+    torch.cuda.synchronize()
+    assert bool((o == 0).all()), "O != 0 with no keys"
+    assert bool(torch.isneginf(lse).all()), "L != -inf with no keys"
