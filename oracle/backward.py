@@ -42,12 +42,14 @@ def _f64(x) -> np.ndarray:
     return np.asarray(x, dtype=np.float64)
 
 
-def _probs(q, k, causal, scale):
-    """Row softmax of the masked logits; a row that sees no key has P = 0."""
-    Nq, Nk = q.shape[0], k.shape[0]
-    S = scale * (q @ k.T)
+def _probs(q_rows, k, rows, causal, scale, offset):
+    """Row softmax of the masked logits of the given query rows (absolute positions
+    `rows`; key j is hidden from row i when j > i + offset); a row that sees no key has
+    P = 0."""
+    Nk = k.shape[0]
+    S = scale * (q_rows @ k.T)
     if causal:
-        S = np.where(np.arange(Nk)[None, :] > np.arange(Nq)[:, None] + (Nk - Nq), -np.inf, S)
+        S = np.where(np.arange(Nk)[None, :] > np.asarray(rows)[:, None] + offset, -np.inf, S)
     P = np.zeros_like(S)
     if Nk == 0:
         return P
@@ -63,25 +65,31 @@ def delta_fp64(o, do):
     return (_f64(o) * _f64(do)).sum(axis=-1)
 
 
-def attention_bwd_fp64(q, k, v, do, causal: bool = False, scale: float | None = None):
+def attention_bwd_fp64(q, k, v, do, causal: bool = False, scale: float | None = None,
+                       row_chunk: int = 2048):
     """(dQ [B,H,Nq,d], dK, dV [B,H,Nk,d]) in float64, for O = attention(q, k, v) and upstream dO.
 
     q and do are [B, H, Nq, d], k and v [B, H, Nk, d]; the causal mask is aligned
     bottom-right as in the forward oracle, and rows that see no key (P = 0) add nothing.
+    Query rows are taken in chunks of at most `row_chunk` (each row's P, dP and dS depend on
+    that row alone; dK and dV are sums over rows), which bounds the memory at long lengths.
     """
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
-    B, H, N, d = q.shape
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     dQ, dK, dV = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
     for b in range(B):
         for h in range(H):
-            P = _probs(q[b, h], k[b, h], causal, scale)
-            O = P @ v[b, h]
-            dV[b, h] = P.T @ do[b, h]
-            dP = do[b, h] @ v[b, h].T
-            D = (do[b, h] * O).sum(axis=1, keepdims=True)
-            dS = P * (dP - D)
-            dQ[b, h] = scale * (dS @ k[b, h])
-            dK[b, h] = scale * (dS.T @ q[b, h])
+            for r0 in range(0, Nq, row_chunk):
+                r1 = min(Nq, r0 + row_chunk)
+                P = _probs(q[b, h, r0:r1], k[b, h], np.arange(r0, r1), causal, scale, Nk - Nq)
+                O = P @ v[b, h]
+                dV[b, h] += P.T @ do[b, h, r0:r1]
+                dP = do[b, h, r0:r1] @ v[b, h].T
+                D = (do[b, h, r0:r1] * O).sum(axis=1, keepdims=True)
+                dS = P * (dP - D)
+                dQ[b, h, r0:r1] = scale * (dS @ k[b, h])
+                dK[b, h] += scale * (dS.T @ q[b, h, r0:r1])
     return dQ, dK, dV

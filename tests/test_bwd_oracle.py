@@ -184,3 +184,25 @@ def test_excess_queries_get_zero_gradient(Nq, Nk):
     dQs, dKs, dVs = _autograd(q[:, :, e:], k, v, do[:, :, e:], True, 0.45)
     assert np.abs(dQ[:, :, e:] - dQs).max() < 1e-12
     assert np.abs(dK - dKs).max() < 1e-12 and np.abs(dV - dVs).max() < 1e-12
+
+
+# ---- row chunking (bounded memory at long lengths) ------------------------------------------
+@pytest.mark.parametrize("Nq,Nk,causal", [(23, 23, True), (23, 23, False), (17, 40, True),
+                                          (40, 17, True), (33, 9, False)])
+@pytest.mark.parametrize("chunk", [1, 5, 16])
+def test_row_chunks_are_the_same_computation(Nq, Nk, causal, chunk):
+    """Taking the query rows in chunks is the same computation (each row's P, dP and dS
+    depend on that row alone; dK, dV sum over rows): the chunked result equals the
+    one-chunk result (itself pinned by autograd above, and here for the square case), so
+    a mistake in the chunk offsets (the mask shifted by the chunk start, a dropped or
+    doubled chunk of dK / dV) fails here."""
+    g = np.random.default_rng(Nq * 3 + Nk + chunk)
+    q, do = g.standard_normal((2, 1, 2, Nq, 8))
+    k, v = g.standard_normal((2, 1, 2, Nk, 8))
+    got = attention_bwd_fp64(q, k, v, do, causal, 0.37, row_chunk=chunk)
+    whole = attention_bwd_fp64(q, k, v, do, causal, 0.37, row_chunk=1 << 30)
+    for a, b in zip(got, whole):
+        assert np.abs(a - b).max() < 1e-12
+    if Nq == Nk:
+        for a, r in zip(got, _autograd(q, k, v, do, causal, 0.37)):
+            assert np.abs(a - r).max() < 1e-11

@@ -181,3 +181,34 @@ def test_autograd_wrapper_cross_fp16():
     out.backward(do.cuda())
     torch.cuda.synchronize()
     _check((qd.grad, kd.grad, vd.grad), ref, "autograd cross fp16")
+
+
+# ------------------------------------------- the sizes the benchmark times, sampled heads
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("name", ["train", "long"])
+def test_bwd_benchmark_shapes_sampled_heads(name, causal):
+    """The backward pass at the sizes `bench.py --backward` times (16 x 16 x 2048 and
+    1 x 16 x 16384, d = 128, bf16), launched on the whole problem, compared with the
+    oracle on every element of dQ, dK and dV of four (batch, head) slices (the first, the
+    last and two drawn at random)."""
+    from exact_attention_62_amd.inputs import WORKLOADS, make
+
+    w = WORKLOADS[name]
+    B, H, N, d = w.B, w.H, w.N, w.d
+    _say(f"backward {name} B={B} H={H} N={N} d={d} causal={causal}")
+    q, k, v = make(w, 0)
+    do = make_upstream(B, H, N, d, 0)
+    qd, kd, vd, dod = (t.cuda() for t in (q, k, v, do))
+    o, lse = attention(qd, kd, vd, causal=causal, scale=w.scale)
+    dq, dk, dv = attention_backward(qd, kd, vd, o, lse, dod, causal=causal, scale=w.scale)
+    torch.cuda.synchronize()
+    dq, dk, dv = dq.cpu(), dk.cpu(), dv.cpu()
+    rng = np.random.default_rng(11 + causal)
+    heads = sorted({(0, 0), (B - 1, H - 1)} | {(int(rng.integers(B)), int(rng.integers(H)))
+                                                for _ in range(2)})
+    while len(heads) < 4:  # draw again on a collision
+        heads = sorted(set(heads) | {(int(rng.integers(B)), int(rng.integers(H)))})
+    for b, h in heads:
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        ref = attention_bwd_fp64(q[sl], k[sl], v[sl], do[sl], causal, w.scale, row_chunk=2048)
+        _check((dq[sl], dk[sl], dv[sl]), ref, f"{name} head ({b},{h}) causal={causal}")
