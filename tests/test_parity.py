@@ -121,7 +121,7 @@ def _sample_rows(N, rng, n_random=48):
 
 @pytest.mark.parametrize("name,causal,seed", [
     ("train", True, 0), ("train", True, 1), ("train", True, 2),
-    ("long", True, 0), ("long", False, 0), ("long", True, 1),
+    ("long", True, 0), ("long", False, 0), ("long", True, 1), ("long", False, 1),
     ("ragged", True, 0), ("ragged", True, 1), ("ragged", True, 2),
 ])
 def test_full_size_workload_sampled(name, causal, seed):
@@ -141,6 +141,72 @@ def test_full_size_workload_sampled(name, causal, seed):
         eo, el = _cmp(o[b, h, rows], lse[b, h, rows], O, L, "bf16", f"{name} head ({b},{h})")
         worst_o, worst_l = max(worst_o, eo), max(worst_l, el)
     _say(f"{name}: max |dO| = {worst_o:.3e}, max |dL| = {worst_l:.3e}")
+
+
+def test_train_workload_every_head_element_by_element():
+    """The training-shaped workload (16 x 16 x 2048 x 128, causal, seed 0) in the
+    benchmark's launch form, compared with the oracle on every element of O and L of all
+    256 (batch, head) slices: every work item of the persistent grid, including the
+    item hand-over of every workgroup, is covered."""
+    w = WORKLOADS["train"]
+    _say(f"workload train all {w.B * w.H} heads element by element")
+    q, k, v = make(w, 0)
+    assert fa2_launch_shape(w.B, w.H, w.N, w.d)[0] == 256
+    o, lse = _run(q, k, v, True, w.scale)
+    o, lse = o.cpu(), lse.cpu()
+    worst_o = worst_l = 0.0
+    for b in range(w.B):
+        for h in range(w.H):
+            O, L = attention_fp64(q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1],
+                                  causal=True, scale=w.scale)
+            eo, el = _cmp(o[b:b + 1, h:h + 1], lse[b:b + 1, h:h + 1], O, L, "bf16",
+                          f"train head ({b},{h})")
+            worst_o, worst_l = max(worst_o, eo), max(worst_l, el)
+    _say(f"train, all heads: max |dO| = {worst_o:.3e}, max |dL| = {worst_l:.3e}")
+
+
+def _ramp_inputs(n_blocks, d, step, dtype, seed):
+    """Keys whose logits rise by a fixed amount per 64-key block: key j has `step` in
+    dims 1 .. j // 64 (dim 0 is 0) and every query is 1 in those dims, so
+    q . k_j = step * (j // 64) exactly (integer multiples of one bf16/fp16 value summed
+    in fp32).  V is N(0, 1)."""
+    N = 64 * n_blocks
+    assert n_blocks <= d
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float16
+    j = torch.arange(N)
+    k = torch.zeros((1, 1, N, d))
+    for t in range(1, n_blocks):
+        k[0, 0, j // 64 >= t, t] = step
+    q = torch.zeros((1, 1, N, d))
+    q[..., 1:] = 1.0
+    gen = torch.Generator().manual_seed(seed)
+    v = torch.randn((1, 1, N, d), generator=gen)
+    return q.to(dt), k.to(dt), v.to(dt)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d,step", [(64, 43.75), (64, 44.5), (128, 62.0), (128, 63.0)])
+def test_lazy_rescale_edges(d, step, causal, dtype):
+    """The kernel moves its reference max only when a block's max exceeds it by more than
+    8 (log2 units), where the pages rescale at every block (page "Flash Attention
+    V2原理解读", commentary on the FWD inner loop).  Here every row's logits rise by just
+    under 8 per block (43.75 / 8 * log2(e) = 7.89 at d = 64; 62 / sqrt(128) * log2(e) = 7.91
+    at d = 128), so the reference lags by up to two blocks and P~ reaches 2^7.9 before it is
+    rounded to bf16 or fp16; and by just over 8 (8.02, 8.03), so it moves at every block.
+    The result must still match the oracle."""
+    n_blocks = d - 1 if d == 64 else 48
+    q, k, v = _ramp_inputs(n_blocks, d, step, dtype, seed=d + int(step * 4))
+    c = math.log2(math.e) / math.sqrt(d)
+    _say(f"lazy rescale d={d} step={step} ({step * c:.3f} log2 units per block) {dtype} "
+         f"causal={causal}")
+    o, lse = _run(q, k, v, causal)
+    O, L = attention_fp64(q, k, v, causal=causal)
+    otol, ltol = (2e-2, 1e-3) if dtype == "bf16" else (1e-2, 1e-3)
+    o64, l64 = o.double().cpu().numpy(), lse.double().cpu().numpy()
+    assert np.all(np.isfinite(o64)) and np.all(np.isfinite(l64))
+    eo, el = np.abs(o64 - O).max(), np.abs(l64 - L).max()
+    assert eo <= otol and el <= ltol, f"max |dO| = {eo:.3e}, max |dL| = {el:.3e}"
 
 
 def test_very_long_sequence_sampled():
