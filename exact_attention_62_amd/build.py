@@ -1,6 +1,10 @@
 """Build libfa2.so (the gfx950 kernels plus the C-ABI host code) in-tree with hipcc.
 
     python -m exact_attention_62_amd.build          # writes exact_attention_62_amd/libfa2.so
+    python -m exact_attention_62_amd.build --sanitize OUT.so
+        # host code built with AddressSanitizer and UndefinedBehaviorSanitizer
+        # (device code unchanged); load it with the ASan runtime preloaded
+        # (sanitizer_runtime() names it) and FA2_LIBRARY=OUT.so
 
 hipcc cross-compiles for gfx950 without a GPU present.  Packed fp32 VALU
 instructions are disabled for device code (``-packed-fp32-ops``); the host
@@ -40,9 +44,33 @@ def common_flags(extra=()):
             "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}", *extra]
 
 
-def build(verbose: bool = False, extra_flags=()) -> str:
-    """Compile every source and link libfa2.so; returns its path.  Raises on failure."""
+# Host-only sanitizer flags: each -fsanitize= sits directly after -Xarch_host, so
+# that the device pass is built exactly as in the normal library.
+SANITIZE_FLAGS = ["-Xarch_host", "-O1", "-Xarch_host", "-g",
+                  "-Xarch_host", "-fsanitize=address",
+                  "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-sanitize-recover=all",
+                  "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def sanitizer_runtime() -> str:
+    """The ASan runtime (which carries the UBSan handlers too) of hipcc's clang, to
+    preload into a process that loads a sanitized library."""
+    import glob
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    found = sorted(glob.glob(os.path.join(rocm, "llvm", "lib", "clang", "*", "lib", "linux",
+                                          "libclang_rt.asan-x86_64.so")))
+    if not found:
+        raise RuntimeError("no libclang_rt.asan-x86_64.so under " + rocm)
+    return found[-1]
+
+
+def build(verbose: bool = False, extra_flags=(), out: str = LIB, sanitize: bool = False) -> str:
+    """Compile every source and link the library (libfa2.so, or `out`); returns its path.
+    With sanitize, host code is instrumented with ASan + UBSan.  Raises on failure."""
     cc = hipcc()
+    if sanitize:
+        extra_flags = [*extra_flags, *SANITIZE_FLAGS]
     with tempfile.TemporaryDirectory(prefix="fa2_build_") as tmp:
         cmds, objs = [], []
         for src in SOURCES:
@@ -57,10 +85,12 @@ def build(verbose: bool = False, extra_flags=()) -> str:
             for f in [pool.submit(_run, cmd, verbose) for cmd in cmds]:
                 f.result()
         tmp_lib = os.path.join(tmp, "libfa2.so")
-        _run([cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp_lib], verbose)
-        shutil.copyfile(tmp_lib, LIB + ".tmp")
-        os.replace(LIB + ".tmp", LIB)
-    return LIB
+        link_san = ["-Xarch_host", "-fsanitize=address,undefined"] if sanitize else []
+        _run([cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *link_san, *objs, "-o", tmp_lib],
+             verbose)
+        shutil.copyfile(tmp_lib, out + ".tmp")
+        os.replace(out + ".tmp", out)
+    return out
 
 
 def _run(cmd, verbose):
@@ -76,4 +106,9 @@ def _run(cmd, verbose):
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv[1:]))
+    args = sys.argv[1:]
+    if "--sanitize" in args:
+        i = args.index("--sanitize")
+        print(build(verbose="-v" in args, out=os.path.abspath(args[i + 1]), sanitize=True))
+    else:
+        print(build(verbose="-v" in args))

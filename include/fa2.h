@@ -54,13 +54,19 @@ typedef enum {
   FA2_OK = 0,
   FA2_EINVAL = -1,  /* an argument is invalid: null/misaligned/overlapping pointer, bad size, ... */
   FA2_ENOTSUP = -2, /* a valid request this build does not implement (head dim, dtype)           */
-  FA2_EHIP = -3     /* the HIP runtime reported an error (no device, launch failure, ...)        */
+  FA2_EHIP = -3,    /* the HIP runtime reported an error (no device, launch failure, ...)        */
+  FA2_STATUS_MAX_ENUM = 0x7fffffff /* not a status: makes the type a full 32-bit int */
 } fa2_status_t;
 
 typedef enum {
   FA2_BF16 = 0, /* bfloat16 Q/K/V/O; QK^T and PV on bf16 MFMA with float32 accumulation      */
   FA2_FP32 = 1, /* float32 Q/K/V/O; every step in float32 (exact mode, meant for small sizes) */
-  FA2_FP16 = 2  /* float16 Q/K/V/O; QK^T and PV on fp16 MFMA with float32 accumulation       */
+  FA2_FP16 = 2, /* float16 Q/K/V/O; QK^T and PV on fp16 MFMA with float32 accumulation       */
+  /* Not dtypes: the two widen the enum to every 32-bit signed value, so that a caller
+   * passing any int (an unknown code included) hands over a valid value of the type,
+   * which the entry points then reject with FA2_ENOTSUP. */
+  FA2_DTYPE_INVALID = -1,
+  FA2_DTYPE_MAX_ENUM = 0x7fffffff
 } fa2_dtype_t;
 
 /*

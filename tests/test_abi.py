@@ -437,3 +437,13 @@ def test_bwd_cross_zero_size_sides_need_no_pointers():
     # still written, so the call then needs the device); likewise K, V, dK, dV without keys.
     assert _bwd_cross(q=None, o=None, do=None, L=None, dq=None, ws=None, ws_bytes=0, Nq=0) == F.FA2_EHIP
     assert _bwd_cross(k=None, v=None, dk=None, dv=None, Nk=0) == F.FA2_EHIP
+
+
+def test_enums_span_every_int32_value():
+    """fa2_dtype_t and fa2_status_t carry a 0x7fffffff member, so any 32-bit code a caller
+    passes is a valid value of the type (no undefined behaviour before the dtype check)."""
+    text = open(HEADER).read()
+    assert "FA2_DTYPE_INVALID = -1" in text and "FA2_DTYPE_MAX_ENUM = 0x7fffffff" in text
+    assert "FA2_STATUS_MAX_ENUM = 0x7fffffff" in text
+    for code in (3, 7, -1, -(1 << 31), 0x7fffffff):
+        assert _fwd(dtype=code) == F.FA2_ENOTSUP
