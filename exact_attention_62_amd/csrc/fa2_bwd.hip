@@ -215,16 +215,23 @@ __device__ __forceinline__ typename Vec16<T>::x8 tr_frag(const char* tile, const
 }
 
 // Compile-time proof of the layout for a [ROWS][D] tile: the direct loads of
-// stage_tile fill every element where toff puts it; row and transposing
-// fragment addresses equal toff of the (row, dims) the MFMA operand needs;
-// each 16-lane pass of a row read reaches 16 distinct 16-byte bank groups
-// (64 banks of 4 bytes) and each 16-lane group of a transposing read 16
+// stage_tile stay inside the tile (rows < ROWS, dims < D, 16-byte chunks) and
+// fill every (row, 8 dims) exactly once, where toff puts it; row and
+// transposing fragment reads are aligned (16 and 8 bytes), stay inside the
+// tile and their addresses equal toff of the (row, dims) the MFMA operand
+// needs; each 16-lane pass of a row read reaches 16 distinct 16-byte bank
+// groups (64 banks of 4 bytes) and each 16-lane group of a transposing read 16
 // distinct 8-byte slots of one 128-byte span.
 template <int D, int ROWS>
 __device__ __forceinline__ constexpr bool tile_layout_ok() {
-  for (int n = 0; n < ROWS * D * 2 / 1024; ++n)
+  constexpr int BYTES = ROWS * D * 2;
+  bool seen[ROWS * D / 8] = {};
+  for (int n = 0; n < BYTES / 1024; ++n)
     for (int L = 0; L < 64; ++L) {
       const int r = stage_row<D>(n, L), c = stage_col<D>(n, L);
+      if (r < 0 || r >= ROWS || c < 0 || c + 8 > D || c % 8 != 0) return false;
+      if (seen[(r * D + c) / 8]) return false;
+      seen[(r * D + c) / 8] = true;
       if (r - stage_row<D>(n, 0) != r % 4 + 4 * ((L / 8) / (D / 16))) return false;
       for (int k = 0; k < 8; ++k)
         if (toff<D>(r, c + k) != n * 1024 + 16 * L + 2 * k) return false;
@@ -235,6 +242,7 @@ __device__ __forceinline__ constexpr bool tile_layout_ok() {
         bool used[16] = {};
         for (int l = 16 * pass; l < 16 * pass + 16; ++l) {
           const int a = row_base<D>(l, ks & 1) + (row0 / 4) * (8 * D) + 256 * (ks >> 1);
+          if (a < 0 || a + 16 > BYTES || a % 16 != 0) return false;
           for (int k = 0; k < 8; ++k)
             if (toff<D>(row0 + (l & 31), 16 * ks + 8 * (l >> 5) + k) != a + 2 * k) return false;
           if (used[(a / 16) % 16]) return false;
@@ -250,6 +258,7 @@ __device__ __forceinline__ constexpr bool tile_layout_ok() {
           for (int l = 16 * grp; l < 16 * grp + 16; ++l) {
             const int a = tr_base<D>(l, e) + 32 * D * u + 256 * t;
             lo = a < lo ? a : lo;
+            if (a < 0 || a + 8 > BYTES || a % 8 != 0) return false;
           }
           for (int l = 16 * grp; l < 16 * grp + 16; ++l) {
             const int a = tr_base<D>(l, e) + 32 * D * u + 256 * t, i = l & 15;
@@ -387,6 +396,12 @@ fa2_bwd_dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict_
   // block's V rows (the B operand of dP), staged once.
   __shared__ __attribute__((aligned(1024))) char smem[2 * (2 * TILE + 512)];
   __shared__ __attribute__((aligned(1024))) char vtile[kRows * D * 2];
+  static_assert(tile_layout_ok<D, kQStep>() && tile_layout_ok<D, kRows>(), "staged tiles");
+  // L and D of a step: 64 floats each, 256 bytes after the two tiles; the reads
+  // take 4 floats at 8g + 4*half (g < 4), the last ending at float 32.
+  static_assert(4 * (8 * 3 + 4 + 4) <= 256, "L and D reads stay inside their 256 bytes");
+  static_assert(2 * (2 * (2 * TILE + 512) + kRows * D * 2) <= 160 * 1024,
+                "two resident workgroups' LDS fits a CU");
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -521,6 +536,8 @@ fa2_bwd_dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ 
   constexpr int KS = D / 16, DT = D / 32;
   constexpr int TILE = kStep * D * 2;
   __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * TILE];  // K, V tiles, two steps
+  static_assert(tile_layout_ok<D, kStep>(), "staged tiles");
+  static_assert(2 * (2 * 2 * TILE) <= 160 * 1024, "two resident workgroups' LDS fits a CU");
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);

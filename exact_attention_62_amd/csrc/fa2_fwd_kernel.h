@@ -176,6 +176,77 @@ template <int D> __host__ __device__ constexpr int v_row(int n, int l) {
 template <int D> __host__ __device__ constexpr int v_dim(int n, int l) {
   return 16 * ((8 * n + l / 8) % (D / 16)) + 8 * (l % 2);
 }
+template <int D> __host__ __device__ constexpr int v_off(int r, int d) {
+  return (r / 4) * (8 * D) + (d / 16) * 128 + 32 * (r % 4) + 2 * (d % 16);
+}
+// V^T fragment reads (the A operand of O^T += V^T P^T, PV k-step u of 16 keys,
+// head-dimension tile t of 32 dims) through ds_read_b64_tr_b16: lane l reads 8
+// bytes at v_read_base(l) + v_read_off(u, t, e), e = 0 for operand slots 0..3
+// and e = 1 for slots 4..7.  Within each 16-lane group the hardware hands lane
+// i element j (j = 0..3) of its result from element i % 4 of the 8 bytes that
+// lane 4j + i/4 of the group addressed.
+template <int D> __host__ __device__ __forceinline__ constexpr int v_read_base(int l) {
+  return ((l >> 4) >> 1) * 4 * (2 * D) + ((l >> 4) & 1) * 128 + 8 * (l & 15);
+}
+template <int D> __host__ __device__ __forceinline__ constexpr int v_read_off(int u, int t, int e) {
+  return u * 32 * D + e * 16 * D + t * 256;
+}
+// Compile-time proof of the V layout of a block of BN keys:
+//  - the direct loads (load n, lane l: 16 bytes at n*1024 + 16*l, key row
+//    v_row, dims v_dim .. +7) stay inside the block, land where v_off puts
+//    them and write every (row, 8 dims) exactly once; where the kernel splits
+//    the load address into a per-load and a per-lane part (8 blocks of a load
+//    and the 16-dim segments of a row nest), the parts add up to it;
+//  - every transposing read is 8-byte aligned and inside the block, each
+//    16-lane group reads one 128-byte span with 16 distinct 8-byte slots, and
+//    slot s of lane l's operand receives V[key][32t + l%32] for the key that
+//    slot s of the P~ operand holds: 16u + 8*(s/4) + 4*(l/32) + s%4 (P~ is
+//    packed from the S^T accumulators, whose register r of lane l is key
+//    8*(r/4) + 4*(l/32) + r%4 of its 32-key sub-block).
+template <int D, int BN> __host__ __device__ constexpr bool v_layout_ok() {
+  constexpr int TBV = BN * 2 * D, NSEG = D / 16;
+  constexpr bool SEP = 8 % NSEG == 0 || NSEG % 8 == 0;
+  bool seen[BN * D / 8] = {};
+  for (int n = 0; n < TBV / 1024; ++n)
+    for (int l = 0; l < 64; ++l) {
+      const int r = v_row<D>(n, l), d = v_dim<D>(n, l);
+      if (r < 0 || r >= BN || d < 0 || d + 8 > D || d % 8 != 0) return false;
+      for (int k = 0; k < 8; ++k)
+        if (v_off<D>(r, d + k) != n * 1024 + 16 * l + 2 * k) return false;
+      if (seen[(r * D + d) / 8]) return false;
+      seen[(r * D + d) / 8] = true;
+      if (SEP && v_row<D>(n, 0) * D + v_dim<D>(n, 0) + v_row<D>(0, l) * D + v_dim<D>(0, l) !=
+                     r * D + d)
+        return false;
+    }
+  for (int u = 0; u < BN / 16; ++u)
+    for (int t = 0; t < D / 32; ++t)
+      for (int e = 0; e < 2; ++e)
+        for (int grp = 0; grp < 4; ++grp) {
+          int lo = 1 << 30;
+          for (int l = 16 * grp; l < 16 * grp + 16; ++l) {
+            const int a = v_read_base<D>(l) + v_read_off<D>(u, t, e);
+            lo = a < lo ? a : lo;
+            if (a < 0 || a + 8 > TBV || a % 8 != 0) return false;
+          }
+          bool used[16] = {};
+          for (int l = 16 * grp; l < 16 * grp + 16; ++l) {
+            const int a = v_read_base<D>(l) + v_read_off<D>(u, t, e);
+            if (a - lo >= 128 || used[(a - lo) / 8]) return false;
+            used[(a - lo) / 8] = true;
+            const int i = l & 15;
+            for (int j = 0; j < 4; ++j) {
+              const int src = 16 * grp + 4 * j + i / 4;  // the lane whose address serves slot j
+              const int s = 4 * e + j;
+              const int key = 16 * u + 8 * (s / 4) + 4 * (l / 32) + s % 4;
+              const int dim = 32 * t + (l & 31);
+              if (v_read_base<D>(src) + v_read_off<D>(u, t, e) + 2 * (i % 4) != v_off<D>(key, dim))
+                return false;
+            }
+          }
+        }
+  return true;
+}
 
 template <typename T, int D, bool CAUSAL, bool SPLIT, int WAVES, int OCC>
 __global__ void __launch_bounds__(64 * WAVES, (groups_per_cu<WAVES, OCC>()))
@@ -213,6 +284,9 @@ fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
   static_assert(k_layout_ok<D, BN>(), "K LDS layout: rows, pieces and banks");
   static_assert(lds_off<D>(BN - 1) + ROWB <= TB, "K rows stay inside their buffer");
   static_assert(LOADS_V >= 1 && TBV % (1024 * kWaves) == 0, "V block must split evenly");
+  static_assert(v_layout_ok<D, BN>(), "V LDS layout: direct loads and transposing reads");
+  static_assert(groups_per_cu<WAVES, OCC>() * (2 * TBV + 2 * TB) <= 160 * 1024,
+                "the resident workgroups' LDS fits a CU");
   static_assert(TBV + 16 * ROWB * (U - 1) + 8 * ROWB + 256 * (DT - 1) < 65536 &&
                     2 * TBV + TB + KTSTEP * (KT - 1) + 32 * (KS - 1) < 65536,
                 "LDS offsets fit the 16-bit instruction offset");
@@ -442,8 +516,7 @@ fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
   // the keys 8*(r/4) + 4*half + r%4 that a lane's S^T accumulators hold.  With
   // the V layout, the 16 lanes of a group read one contiguous 128-byte block:
   // lane i at byte 8i of the block of rows kbase.. and dims d0..d0+15.
-  const uint32_t vaddr =
-      (uint32_t)(((lane >> 4) >> 1) * 4 * ROWB + ((lane >> 4) & 1) * 128 + 8 * (lane & 15));
+  const uint32_t vaddr = (uint32_t)v_read_base<D>(lane);
 
   // Issue priority: lowered by one each time another prio_step blocks of this
   // workgroup's sequence have started (set before the first item).
@@ -526,9 +599,9 @@ fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
 #pragma unroll
       for (int t = 0; t < DT; ++t) {
         const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4_ptr_t)(vb + u * 16 * ROWB + t * 256));
+            (lds_s16x4_ptr_t)(vb + v_read_off<D>(u, t, 0)));
         const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4_ptr_t)(vb + 8 * ROWB + u * 16 * ROWB + t * 256));
+            (lds_s16x4_ptr_t)(vb + v_read_off<D>(u, t, 1)));
         const t8_t a =
             __builtin_bit_cast(t8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         o[t] = mfma32x32x16(a, pb[u], o[t]);
