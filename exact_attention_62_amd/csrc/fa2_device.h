@@ -32,8 +32,27 @@ constexpr int kBufferFlags = 0x00020000;
 
 // Value of x combined with the one held 32 lanes away (the two lane halves of
 // a 32x32 MFMA tile hold different keys of the same query row).
-__device__ __forceinline__ float halves_max(float x) { return fmaxf(x, __shfl_xor(x, 32, 64)); }
-__device__ __forceinline__ float halves_sum(float x) { return x + __shfl_xor(x, 32, 64); }
+// v_permlane32_swap swaps the upper 32 lanes of its first operand with the
+// lower 32 lanes of its second; with x in both, lane l < 32 ends with (x[l],
+// x[l+32]) and lane l >= 32 with (x[l-32], x[l]), so every lane holds its own
+// value and its partner's, and max or sum of the two is the same in both
+// halves.  Inline assembly with both registers read and written: the compiler
+// builtin, given the same value twice, has its two results taken for one
+// register (r0 - r1 compiles to v - v).  The s_nop gives the two wait states a
+// VALU write needs before the swap reads its operands.
+__device__ __forceinline__ void swap_halves(uint32_t& a, uint32_t& b) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ float halves_max(float x) {
+  uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+  swap_halves(a, b);
+  return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+  swap_halves(a, b);
+  return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
+}
 
 // Direct global -> LDS loads of 16 bytes per lane (lane i fills LDS bytes
 // lds + 16i .. +16), and the waits and barriers that order them.  They are

@@ -524,7 +524,10 @@ fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
 
   f32x16_t o[DT];
   float m_ref = kNegInf;  // reference max of the (sign-adjusted) raw logits
+  float mc = 0.f;         // c * m_ref (0 while m_ref = -inf)
+  float m_lim = kNegInf;  // m_ref + kTau / c: a larger row max moves the reference
   float l_part = 0.f;     // running sum over this lane's half of the keys
+  const float tau_raw = kTau / c;
 
   auto compute_S = [&](const char* kb, f32x16_t (&S)[KT]) __attribute__((always_inline)) {
 #pragma unroll
@@ -569,15 +572,23 @@ fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[kt][r]);
     mx = halves_max(mx);
-    // The first block with a visible key always moves the reference (alpha =
-    // exp2(-inf) = 0 then: O and l are still zero).  A block can hold no key
-    // a row sees (mx = -inf: a split's range, or a row that sees no key at
-    // all): the reference then stays at -inf and the block adds nothing,
-    // without forming exp2(-inf + inf).
-    const bool move = m_ref == kNegInf ? mx != kNegInf : c * (mx - m_ref) > kTau;
-    const float alpha = move ? __builtin_amdgcn_exp2f(c * (m_ref - mx)) : 1.f;
-    m_ref = move ? mx : m_ref;
-    const float mc = m_ref == kNegInf ? 0.f : c * m_ref;
+    // The reference moves when the block's row max exceeds m_lim = m_ref +
+    // kTau / c.  The first block with a visible key always moves it (m_lim =
+    // -inf; alpha = exp2(-inf) = 0 then: O and l are still zero).  A block can
+    // hold no key a row sees (mx = -inf: a split's range, or a row that sees
+    // no key at all): the reference then stays at -inf and the block adds
+    // nothing, without forming exp2(-inf + inf).  Moves are rare, so the test
+    // is one compare and a branch that the whole wavefront takes together.
+    if (__builtin_amdgcn_ballot_w64(mx > m_lim)) {
+      const bool move = mx > m_lim;
+      const float alpha = move ? __builtin_amdgcn_exp2f(c * (m_ref - mx)) : 1.f;
+      m_ref = move ? mx : m_ref;
+      mc = move ? c * mx : mc;
+      m_lim = move ? mx + tau_raw : m_lim;
+      l_part *= alpha;
+#pragma unroll
+      for (int t = 0; t < DT; ++t) o[t] *= alpha;
+    }
     float ls = 0.f;
     t8_t pb[U];
 #pragma unroll
@@ -588,11 +599,7 @@ fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
         ls += p;
         pb[kt * 2 + r / 8][r % 8] = (T)p;  // round to nearest even
       }
-    l_part = alpha * l_part + ls;
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
-#pragma unroll
-      for (int t = 0; t < DT; ++t) o[t] *= alpha;
-    }
+    l_part += ls;
     const char* vb = Vb0 + ((gb + j) & 1) * TBV + vaddr;
 #pragma unroll
     for (int u = 0; u < U; ++u)
@@ -651,6 +658,8 @@ fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
 #pragma unroll
     for (int t = 0; t < DT; ++t) o[t] = f32x16_t{};
     m_ref = kNegInf;
+    mc = 0.f;
+    m_lim = kNegInf;
     l_part = 0.f;
     compute_S(Kb0 + (g0 & 1) * TB, S_cur);
   };
