@@ -12,8 +12,11 @@ sustained clocks), then W untimed warm-up steps, then exactly K timed steps
 bracketed by torch.cuda.synchronize().  An event recorded on the stream the
 kernels are enqueued on separates consecutive launches, so every launch is
 timed on its own: the roofline uses their mean, and the line gives their
-median, min and max.  The device's name, compute units and graphics clock
-(sampled through amdsmi during the timed steps) are reported beside it.
+median, min and max.  The device's name, compute units and graphics clock are
+reported beside it; the clock is sampled through amdsmi during the settle phase
+and over --clock-seconds of untimed steps right after the timed region, never
+during it (a sampling thread's driver calls can delay launches, and a delayed
+launch counts as idle time in the events and the wall clock).
 
 Prints one JSON line.  ``value`` is TFLOP/s by the metric's count
 (4*B*H*N^2*d, halved with the causal mask); ``roofline`` compares the same
@@ -82,6 +85,9 @@ def parse_args(argv=None):
                    help="with --ring: spread the partial-result launches over K streams")
     p.add_argument("--splits", type=int, default=None, metavar="S",
                    help="time the split-KV path (fa2_fwd_splitkv) with S splits; 0 = the pages' rule")
+    p.add_argument("--clock-seconds", type=float, default=0.5,
+                   help="untimed launches after the timed region while the shader clock is "
+                        "sampled (0: no clock sampling)")
     p.add_argument("--settle-seconds", type=float, default=1.0,
                    help="before the warm-up steps, run steps for this many seconds so the clocks "
                         "reach their sustained level (reported as 'settle'; 0 disables it)")
@@ -440,6 +446,9 @@ def main(argv=None) -> int:
             if time.perf_counter() - t_settle >= args.settle_seconds:
                 break
     settle_s = time.perf_counter() - t_settle
+    # No sampling while timed: a sampling thread's calls into the driver can delay
+    # the launch loop, and a delayed launch shows up as idle time in the events.
+    clock.stop()
 
     for _ in range(args.warmup):
         step()
@@ -457,7 +466,24 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     wall = t1 - t0
-    clock.stop()
+    # The timed step's outputs, kept for the parity check before the clock phase
+    # below overwrites them (with the same values: the kernels are deterministic).
+    o_timed, lse_timed = o.clone(), lse.clone()
+    # The clock the timed launches ran at: sampled over untimed launches of the
+    # same step right after the timed region.
+    after = ClockSampler(0).start() if args.clock_seconds > 0 else None
+    t_after = time.perf_counter()
+    after_launches = 0
+    while after is not None:
+        for _ in range(16):
+            step()
+        after_launches += 16
+        torch.cuda.synchronize()
+        if time.perf_counter() - t_after >= args.clock_seconds:
+            break
+    t_after_end = time.perf_counter()
+    if after is not None:
+        after.stop()
     launch_ms = [events[i].elapsed_time(events[i + 1]) for i in range(args.steps)]
     kernel_ms = sum(launch_ms) / len(launch_ms)  # average launch duration on the stream
     srt = sorted(launch_ms)
@@ -542,7 +568,11 @@ def main(argv=None) -> int:
         "roofline": roofline,
         "device": {"name": props.name, "arch": props.gcnArchName,
                    "compute_units": props.multi_processor_count,
-                   "gfx_clock_timed": clock.window(t0, t1),
+                   "gfx_clock_after_timed": (
+                       {**after.window(t_after, t_after_end), "launches": after_launches,
+                        "note": "amdsmi samples over untimed launches of the same step right "
+                                "after the timed region (nothing samples while timed)"}
+                       if after is not None else None),
                    "gfx_clock_settle": clock.window(t_settle, t_settle + settle_s)},
         "settle": {"seconds": round(settle_s, 3), "launches": settled,
                    "note": "untimed launches before the warm-up, so the clocks reach their "
@@ -550,7 +580,8 @@ def main(argv=None) -> int:
     }
     if args.cpu_seconds > 0 and not args.backward and not args.ring:
         out["cpu_baseline"], out["parity"] = cpu_baseline(
-            w, q_cpu, k_cpu, v_cpu, o.cpu(), lse.cpu(), causal, scale, args.cpu_seconds)
+            w, q_cpu, k_cpu, v_cpu, o_timed.cpu(), lse_timed.cpu(), causal, scale,
+            args.cpu_seconds)
     print(json.dumps(out), flush=True)
     return 0
 
