@@ -278,7 +278,7 @@ fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
   // 16-dim segments of a row and the 8 blocks of a load do not nest (D = 96).
   constexpr bool V_SEP = 8 % NSEG == 0 || NSEG % 8 == 0;
   constexpr int KTSTEP = lds_off<D>(32) - lds_off<D>(0); // 32 keys further in a K block
-  constexpr int NSTORE = DT * 4 + 1;         // O and L stores per wavefront per item
+  constexpr int NSTORE = DT * (SPLIT ? 4 : 2) + 1;  // O and L stores per wavefront per item
   static_assert(LOADS >= 1 && PIECES % kWaves == 0, "block must split evenly over wavefronts");
   static_assert(BN % 32 == 0 && BN % RPP == 0 && RPP * ROWB <= 1024, "piece geometry");
   static_assert(k_layout_ok<D, BN>(), "K LDS layout: rows, pieces and banks");
@@ -687,25 +687,42 @@ fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
     const float l_tot = halves_sum(l_part);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     const int lrow = rgrp * 32 + col;  // this lane's row in the query block
+    if constexpr (SPLIT) {
 #pragma unroll
-    for (int t = 0; t < DT; ++t)
+      for (int t = 0; t < DT; ++t)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int dim = t * 32 + 8 * g + 4 * half;
-        if constexpr (SPLIT) {
+        for (int g = 0; g < 4; ++g) {
+          const int dim = t * 32 + 8 * g + 4 * half;
           f32x4_t w;
 #pragma unroll
           for (int r = 0; r < 4; ++r) w[r] = o[t][g * 4 + r] * inv;
           __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, w), o_rsrc,
                                                  (lrow * D + dim) * 4, 0, 0);
-        } else {
-          t4_t w;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) w[r] = (T)(o[t][g * 4 + r] * inv);
-          __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, w), o_rsrc,
-                                                lrow * ROWB + dim * 2, 0, 0);
         }
-      }
+    } else {
+      // Lane half h holds dims 32t + 8g + 4h .. +3 of its row for g = 0..3.
+      // For each pair (2i, 2i+1), one swap across the halves leaves half h
+      // with all 8 dims 32t + 8(2i + h) .. +7: 16-byte stores, half as many.
+#pragma unroll
+      for (int t = 0; t < DT; ++t)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          t4_t w0, w1;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            w0[r] = (T)(o[t][(2 * i) * 4 + r] * inv);
+            w1[r] = (T)(o[t][(2 * i + 1) * 4 + r] * inv);
+          }
+          u32x2_t a = __builtin_bit_cast(u32x2_t, w0), b = __builtin_bit_cast(u32x2_t, w1);
+          uint32_t a0 = a[0], a1 = a[1], b0 = b[0], b1 = b[1];
+          swap_halves(a0, b0);
+          swap_halves(a1, b1);
+          const u32x4_t v = {a0, a1, b0, b1};
+          __builtin_amdgcn_raw_buffer_store_b128(v, o_rsrc,
+                                                 lrow * ROWB + (t * 32 + 8 * (2 * i + half)) * 2,
+                                                 0, 0);
+        }
+    }
     // Both halves of a row hold the same l and m: they store the same L.
     __builtin_amdgcn_raw_buffer_store_b32(
         __builtin_bit_cast(uint32_t,
