@@ -583,8 +583,6 @@ fa2_status_t fa2_bwd_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d, 
   int64_t bm = 0;
   fa2_status_t s = check_shape(B, H, N, N, d, FA2_BF16, &bm);
   if (s != FA2_OK) return s;
-  if (d != 64 && d != 128)
-    return fail(FA2_ENOTSUP, "the backward pass supports d = 64 and 128 (d=%lld)", (long long)d);
   if (!bytes) return fail(FA2_EINVAL, "bytes is NULL");
   // -D = -rowsum(dO * O) and L * log2(e), float32 per row, rows padded per head
   *bytes = static_cast<size_t>(B * H * fa2::bwd_rows(N) * 8);
@@ -609,8 +607,6 @@ fa2_status_t bwd_common(const void* Q, const void* K, const void* V, const void*
   int64_t bm = 0;
   fa2_status_t s = check_shape(B, H, Nq, Nk, d, dtype, &bm);
   if (s != FA2_OK) return s;
-  if (d != 64 && d != 128)
-    return fail(FA2_ENOTSUP, "the backward pass supports d = 64 and 128 (d=%lld)", (long long)d);
   if (causal != 0 && causal != 1) return fail(FA2_EINVAL, "causal=%d must be 0 or 1", causal);
   if (!std::isfinite(scale)) return fail(FA2_EINVAL, "scale must be finite");
   if (B * H * (Nq + Nk) == 0) return FA2_OK;  // no element of dQ, dK or dV

@@ -75,8 +75,7 @@ __device__ __forceinline__ constexpr int toff(int r, int c) {
 // chunk n of the tile: its lane L writes the 16 bytes at slot L%8 of 128-byte
 // block bk = 8n + L/8, which is segment position bk % NSEG of row group
 // g = bk / NSEG: row 4g + L%4, dims 16*((bk % NSEG) ^ (g%2)) + 8*((L%8)/4 ^ (g/2)%2).
-// As 8n is a multiple of NSEG, the row is stage_row(n, 0) (uniform) plus a
-// part that depends on L only.
+// The row is stage_row(n, 0) (uniform) plus a non-negative per-lane part.
 template <int D>
 __device__ __forceinline__ constexpr int stage_row(int n, int L) {
   return 4 * ((8 * n + L / 8) / (D / 16)) + L % 4;
@@ -88,20 +87,36 @@ __device__ __forceinline__ constexpr int stage_col(int n, int L) {
   return 16 * ((bk % NSEG) ^ (g & 1)) + 8 * (((L % 8) / 4) ^ ((g >> 1) & 1));
 }
 
+// The direct loads of a [ROWS][D] tile: NL loads of 1 KB.  When they split
+// evenly over the wavefronts, wavefront w issues loads w*PER .. w*PER + PER-1;
+// otherwise (d = 32 and 96) load i*kWaves + w for i < PER while it exists, a
+// wave-uniform test.
+template <int D, int ROWS>
+struct TileLoads {
+  static constexpr int NL = ROWS * D * 2 / 1024;
+  static constexpr bool EVEN = NL % kWaves == 0;
+  static constexpr int PER = (NL + kWaves - 1) / kWaves;
+  static_assert(ROWS * D * 2 % 1024 == 0 && NL >= 1, "the tile is whole 1 KB loads");
+  __device__ static constexpr int load(int wave, int i) {
+    return EVEN ? wave * PER + i : i * kWaves + wave;
+  }
+  __device__ static constexpr bool issued(int wave, int i) { return EVEN || i * kWaves + wave < NL; }
+};
+
 // Stage rows [r0, r0 + ROWS) of a [N][D] 16-bit slice into LDS in the tile
-// layout; load i of this thread is direct load n = wave*LOADS + i.  With CLAMP,
-// rows past N are clamped to row N - 1 (callers mask them); without, every row
-// must exist, and each load is a scalar base (the row stage_row(n, 0)) plus a
-// per-lane byte offset.
+// layout (this wavefront's loads, TileLoads).  With CLAMP, rows past N are
+// clamped to row N - 1 (callers mask them); without, every row must exist, and
+// each load is a scalar base (the row stage_row(n, 0)) plus a per-lane byte
+// offset.
 template <int D, int ROWS, bool CLAMP>
 __device__ __forceinline__ void stage_tile(const uint16_t* head, int r0, int N, char* buf,
                                            int wave) {
-  constexpr int LOADS = ROWS * D * 2 / 1024 / kWaves;
-  static_assert(LOADS >= 1 && ROWS * D * 2 % (1024 * kWaves) == 0, "tile splits over the waves");
+  typedef TileLoads<D, ROWS> TL;
   const int lane = fresh_lane();  // recomputed here: not kept in registers across the loop
 #pragma unroll
-  for (int i = 0; i < LOADS; ++i) {
-    const int n = wave * LOADS + i;
+  for (int i = 0; i < TL::PER; ++i) {
+    if (!TL::issued(wave, i)) continue;
+    const int n = TL::load(wave, i);
     if constexpr (CLAMP) {
       const int r = min(r0 + stage_row<D>(n, lane), N - 1);
       lds_dma(head + (size_t)r * D + stage_col<D>(n, lane), lds_addr(buf + n * 1024));
@@ -117,18 +132,22 @@ __device__ __forceinline__ void stage_tile(const uint16_t* head, int r0, int N, 
 // kernel that keeps them in registers across its loop.
 template <int D, int ROWS>
 struct StageOffsets {
-  static constexpr int LOADS = ROWS * D * 2 / 1024 / kWaves;
+  static constexpr int LOADS = TileLoads<D, ROWS>::PER;
   uint32_t tile[LOADS];
   uint32_t vec;  // 4 * lane, for stage_vec
 };
 template <int D, int ROWS>
 __device__ __forceinline__ StageOffsets<D, ROWS> stage_offsets(int wave) {
+  typedef TileLoads<D, ROWS> TL;
   StageOffsets<D, ROWS> o;
   const int lane = fresh_lane();
 #pragma unroll
   for (int i = 0; i < o.LOADS; ++i) {
-    const int n = wave * o.LOADS + i;
-    o.tile[i] = (uint32_t)(((stage_row<D>(n, lane) - stage_row<D>(n, 0)) * D + stage_col<D>(n, lane)) * 2);
+    const int n = TL::load(wave, i);
+    o.tile[i] = TL::issued(wave, i)
+                    ? (uint32_t)(((stage_row<D>(n, lane) - stage_row<D>(n, 0)) * D +
+                                  stage_col<D>(n, lane)) * 2)
+                    : 0u;
   }
   o.vec = (uint32_t)(4 * lane);
   return o;
@@ -136,9 +155,11 @@ __device__ __forceinline__ StageOffsets<D, ROWS> stage_offsets(int wave) {
 template <int D, int ROWS>
 __device__ __forceinline__ void stage_tile_at(const uint16_t* head, int r0, char* buf, int wave,
                                               const StageOffsets<D, ROWS>& o) {
+  typedef TileLoads<D, ROWS> TL;
 #pragma unroll
   for (int i = 0; i < o.LOADS; ++i) {
-    const int n = wave * o.LOADS + i;
+    if (!TL::issued(wave, i)) continue;
+    const int n = TL::load(wave, i);
     lds_dma(head + (size_t)(r0 + stage_row<D>(n, 0)) * D, o.tile[i], lds_addr(buf + n * 1024));
   }
 }
@@ -232,7 +253,7 @@ __device__ __forceinline__ constexpr bool tile_layout_ok() {
       if (r < 0 || r >= ROWS || c < 0 || c + 8 > D || c % 8 != 0) return false;
       if (seen[(r * D + c) / 8]) return false;
       seen[(r * D + c) / 8] = true;
-      if (r - stage_row<D>(n, 0) != r % 4 + 4 * ((L / 8) / (D / 16))) return false;
+      if (r < stage_row<D>(n, 0)) return false;  // the per-lane part of the address is >= 0
       for (int k = 0; k < 8; ++k)
         if (toff<D>(r, c + k) != n * 1024 + 16 * L + 2 * k) return false;
     }
@@ -272,9 +293,18 @@ __device__ __forceinline__ constexpr bool tile_layout_ok() {
         }
   return true;
 }
-static_assert(tile_layout_ok<64, 32>() && tile_layout_ok<64, 64>(), "tile layout, d = 64");
-static_assert(tile_layout_ok<128, 32>() && tile_layout_ok<128, 64>(), "tile layout, d = 128");
-static_assert(tile_layout_ok<64, 128>() && tile_layout_ok<128, 128>(), "tile layout, 128 rows");
+static_assert(tile_layout_ok<32, 32>() && tile_layout_ok<32, 64>() && tile_layout_ok<32, 128>(),
+              "tile layout, d = 32");
+static_assert(tile_layout_ok<64, 32>() && tile_layout_ok<64, 64>() && tile_layout_ok<64, 128>(),
+              "tile layout, d = 64");
+static_assert(tile_layout_ok<96, 32>() && tile_layout_ok<96, 64>() && tile_layout_ok<96, 128>(),
+              "tile layout, d = 96");
+static_assert(tile_layout_ok<128, 32>() && tile_layout_ok<128, 64>() &&
+                  tile_layout_ok<128, 128>(),
+              "tile layout, d = 128");
+static_assert(tile_layout_ok<256, 32>() && tile_layout_ok<256, 64>() &&
+                  tile_layout_ok<256, 128>(),
+              "tile layout, d = 256");
 
 // B operand fragments of a [N][D] 16-bit slice held in registers: for k-step ks,
 // lane l holds row r0 + l%32, dims 16*ks + 8*(l/32) .. +8 (zero past N).
@@ -349,20 +379,26 @@ using sched::xcd_block;
 // kernel's query step): padded rows get D = 0 and L*log2(e) = +inf, so
 // exp2(c*S - L*log2(e)) is 0 there and the dK/dV kernel needs no test for
 // queries past Nq.
+// Threads per row of the prep kernel: one per 8 dims, rounded up to a power of
+// two for the butterfly sum (d = 96: 16, of which 12 load).
+template <int D>
+constexpr int prep_tpr() {
+  return D == 96 ? 16 : D / 8;
+}
 template <typename T, int D>
 __global__ void __launch_bounds__(kThreads)
 fa2_bwd_prep_kernel(const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO,
                     const float* __restrict__ L, float* __restrict__ Dv, float* __restrict__ L2v,
                     int Nq, int Npad, int rows) {
   typedef typename Vec16<T>::x8 t8_t;
-  constexpr int TPR = D / 8;  // threads per row, 8 dims each
+  constexpr int TPR = prep_tpr<D>();  // threads per row, 8 dims each (the last idle for d = 96)
   const int row = blockIdx.x * (kThreads / TPR) + threadIdx.x / TPR;
   const int t = threadIdx.x % TPR;
   const int bh = row / Npad, q = row - bh * Npad;
   const bool valid = row < rows && q < Nq;
   const size_t src = (size_t)bh * Nq + q;
   float acc = 0.f;
-  if (valid) {
+  if (valid && t < D / 8) {
     const t8_t o = *(const t8_t*)(O + src * D + 8 * t);
     const t8_t g = *(const t8_t*)(dO + src * D + 8 * t);
 #pragma unroll
@@ -382,8 +418,10 @@ fa2_bwd_prep_kernel(const uint16_t* __restrict__ O, const uint16_t* __restrict__
 // tile) within 256 so that two wavefronts share each SIMD.
 constexpr int kQStep = 32;
 
-template <typename T, int D, bool CAUSAL>
-__global__ void __launch_bounds__(kThreads, 2)
+// OCC: workgroups per CU (two, or one for d = 256, whose dK and dV
+// accumulators alone take 256 registers).
+template <typename T, int D, bool CAUSAL, int OCC>
+__global__ void __launch_bounds__(kThreads, OCC)
 fa2_bwd_dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
                     const uint16_t* __restrict__ Vg, const uint16_t* __restrict__ dOg,
                     const float* __restrict__ L2g, const float* __restrict__ Dg,
@@ -400,8 +438,8 @@ fa2_bwd_dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict_
   // L and D of a step: 64 floats each, 256 bytes after the two tiles; the reads
   // take 4 floats at 8g + 4*half (g < 4), the last ending at float 32.
   static_assert(4 * (8 * 3 + 4 + 4) <= 256, "L and D reads stay inside their 256 bytes");
-  static_assert(2 * (2 * (2 * TILE + 512) + kRows * D * 2) <= 160 * 1024,
-                "two resident workgroups' LDS fits a CU");
+  static_assert(OCC * (2 * (2 * TILE + 512) + kRows * D * 2) <= 160 * 1024,
+                "the resident workgroups' LDS fits a CU");
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -525,8 +563,8 @@ fa2_bwd_dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict_
 }
 
 // ---------------------------------------------------------------- dQ
-template <typename T, int D, bool CAUSAL>
-__global__ void __launch_bounds__(kThreads, 2)
+template <typename T, int D, bool CAUSAL, int OCC>
+__global__ void __launch_bounds__(kThreads, OCC)
 fa2_bwd_dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
                   const uint16_t* __restrict__ Vg, const uint16_t* __restrict__ dOg,
                   const float* __restrict__ L2g, const float* __restrict__ Dg,
@@ -537,7 +575,7 @@ fa2_bwd_dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ 
   constexpr int TILE = kStep * D * 2;
   __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * TILE];  // K, V tiles, two steps
   static_assert(tile_layout_ok<D, kStep>(), "staged tiles");
-  static_assert(2 * (2 * 2 * TILE) <= 160 * 1024, "two resident workgroups' LDS fits a CU");
+  static_assert(OCC * (2 * 2 * TILE) <= 160 * 1024, "the resident workgroups' LDS fits a CU");
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -635,11 +673,12 @@ fa2_bwd_dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ 
 
 template <typename T, int D, bool CAUSAL>
 hipError_t launch(const BwdArgs& a) {
+  constexpr int OCC = D == 256 ? 1 : 2;
   const float c = a.scale * kLog2e;
   const int Npad = (int)bwd_rows(a.Nq);
   const int qrows = a.BH * Npad;
   float* L2v = a.Dvec + (size_t)qrows;
-  constexpr int RPB = kThreads / (D / 8);
+  constexpr int RPB = kThreads / prep_tpr<D>();
   // Kernels with nothing to do are not launched: no queries leaves dK = dV = 0
   // (written by the dK/dV kernel, which then walks no query step); no keys
   // leaves dQ = 0 (written by the dQ kernel, which then walks no key block).
@@ -649,13 +688,13 @@ hipError_t launch(const BwdArgs& a) {
                        a.Nq, Npad, qrows);
   const int nkb = (a.Nk + kRows - 1) / kRows;
   if (nkb * a.BH > 0)
-    hipLaunchKernelGGL((fa2_bwd_dkdv_kernel<T, D, CAUSAL>), dim3(nkb * a.BH), dim3(kThreads), 0,
+    hipLaunchKernelGGL((fa2_bwd_dkdv_kernel<T, D, CAUSAL, OCC>), dim3(nkb * a.BH), dim3(kThreads), 0,
                        a.stream, (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V,
                        (const uint16_t*)a.dO, L2v, a.Dvec, (uint16_t*)a.dK, (uint16_t*)a.dV, a.Nq,
                        a.Nk, Npad, nkb, c, a.scale);
   const int nmb = (a.Nq + kRows - 1) / kRows;
   if (nmb * a.BH > 0)
-    hipLaunchKernelGGL((fa2_bwd_dq_kernel<T, D, CAUSAL>), dim3(nmb * a.BH), dim3(kThreads), 0,
+    hipLaunchKernelGGL((fa2_bwd_dq_kernel<T, D, CAUSAL, OCC>), dim3(nmb * a.BH), dim3(kThreads), 0,
                        a.stream, (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V,
                        (const uint16_t*)a.dO, L2v, a.Dvec, (uint16_t*)a.dQ, a.Nq, a.Nk, Npad, nmb,
                        c, a.scale);
@@ -665,10 +704,16 @@ hipError_t launch(const BwdArgs& a) {
 template <typename T>
 hipError_t dispatch(const BwdArgs& a) {
   switch (a.d * 2 + a.causal) {
+    case 32 * 2 + 0: return launch<T, 32, false>(a);
+    case 32 * 2 + 1: return launch<T, 32, true>(a);
     case 64 * 2 + 0: return launch<T, 64, false>(a);
     case 64 * 2 + 1: return launch<T, 64, true>(a);
+    case 96 * 2 + 0: return launch<T, 96, false>(a);
+    case 96 * 2 + 1: return launch<T, 96, true>(a);
     case 128 * 2 + 0: return launch<T, 128, false>(a);
     case 128 * 2 + 1: return launch<T, 128, true>(a);
+    case 256 * 2 + 0: return launch<T, 256, false>(a);
+    case 256 * 2 + 1: return launch<T, 256, true>(a);
   }
   return hipErrorInvalidValue;
 }

@@ -413,7 +413,7 @@ def attention_backward(q, k, v, o, lse, do, causal: bool = False, scale: float |
 
 class FlashAttention(torch.autograd.Function):
     """Autograd wrapper: forward through fa2_fwd / fa2_fwd_cross, backward through fa2_bwd /
-    fa2_bwd_cross (bfloat16 or float16; d = 64 or 128 for the backward)."""
+    fa2_bwd_cross (bfloat16 or float16; every head dimension of the forward)."""
 
     @staticmethod
     def forward(ctx, q, k, v, causal=False, scale=None):

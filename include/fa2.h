@@ -330,7 +330,8 @@ const char* fa2_strerror(fa2_status_t status);
  *   dQ, dK, dV       [B][H][N][d] outputs of type dtype, device memory, 16-byte aligned.
  *   B, H, N, causal, scale, stream: as for fa2_fwd (the same values as the
  *                    forward call).  B*H*N == 0 does nothing and returns FA2_OK.
- *   d                64 or 128 (others: FA2_ENOTSUP).
+ *   d                32, 64, 96, 128 or 256 (others: FA2_ENOTSUP); d = 256 runs one
+ *                    workgroup per CU (its dK and dV accumulators take 256 registers).
  *   dtype            FA2_BF16 or FA2_FP16 (FA2_FP32: FA2_ENOTSUP).
  *   workspace        device memory owned by the caller, 4-byte aligned, at least
  *                    fa2_bwd_workspace_size() bytes (it receives -D and L*log2(e));

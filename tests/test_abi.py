@@ -313,15 +313,18 @@ def test_bwd_workspace_size_formula():
     assert F.fa2_bwd_workspace_size(2, 4, 1000, 64) == 2 * 4 * 1024 * 8
     assert F.fa2_bwd_workspace_size(1, 3, 33, 128) == 3 * 64 * 8
     assert F.fa2_bwd_workspace_size(1, 1, 0, 128) == 0
+    # every forward head dimension has a backward; others are refused
+    for d in (32, 64, 96, 128, 256):
+        assert F.fa2_bwd_workspace_size(1, 1, 16, d) == 32 * 8
     with pytest.raises(F.FA2Error) as e:
-        F.fa2_bwd_workspace_size(1, 1, 16, 256)
+        F.fa2_bwd_workspace_size(1, 1, 16, 80)
     assert e.value.status == F.FA2_ENOTSUP
 
 
 @pytest.mark.parametrize("kw,status,needle", [
     (dict(dtype=F.FA2_FP32), F.FA2_ENOTSUP, "FA2_BF16 and FA2_FP16 only"),
-    (dict(d=256), F.FA2_ENOTSUP, "d=256"),
-    (dict(d=96), F.FA2_ENOTSUP, "d=96"),
+    (dict(d=80), F.FA2_ENOTSUP, "d=80"),
+    (dict(d=48), F.FA2_ENOTSUP, "d=48"),
     (dict(do=None), F.FA2_EINVAL, "dO is NULL"),
     (dict(ws=None), F.FA2_EINVAL, "workspace is NULL"),
     (dict(dk=FAKE + 0x700008), F.FA2_EINVAL, "dK="),
@@ -418,7 +421,7 @@ def _bwd_cross(dtype=F.FA2_BF16, ws_bytes=1 << 16, **kw):
     (dict(dk=None), F.FA2_EINVAL, "dK is NULL"),
     # dK holds 48 rows of 128 bytes: dV placed 4 KB after its start overlaps it
     (dict(dv=FAKE + 0x700000 + 4096), F.FA2_EINVAL, "overlaps"),
-    (dict(d=96), F.FA2_ENOTSUP, "d=96"),
+    (dict(d=80), F.FA2_ENOTSUP, "d=80"),
 ])
 def test_bwd_cross_invalid_arguments_before_any_hip_call(kw, status, needle):
     assert _bwd_cross(**kw) == status

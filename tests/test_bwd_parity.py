@@ -58,7 +58,12 @@ def _check(got, ref, what):
 
 
 SHAPES = [(1, 1, 1, 64), (1, 1, 7, 128), (1, 2, 64, 64), (2, 1, 127, 128), (1, 3, 129, 64),
-          (1, 2, 200, 128), (2, 2, 300, 64), (1, 1, 513, 128), (1, 2, 1024, 128)]
+          (1, 2, 200, 128), (2, 2, 300, 64), (1, 1, 513, 128), (1, 2, 1024, 128),
+          # the other head dimensions: d = 32 and 96 stage their 32-query tiles in fewer 1 KB
+          # loads than (or not a multiple of) the four wavefronts; d = 256 runs one workgroup
+          # per CU
+          (1, 1, 1, 32), (1, 2, 100, 32), (2, 1, 300, 32), (1, 1, 7, 96), (1, 2, 129, 96),
+          (2, 1, 400, 96), (1, 1, 1, 256), (1, 2, 127, 256), (1, 1, 300, 256)]
 
 
 @pytest.mark.parametrize("causal", [False, True])
@@ -123,7 +128,8 @@ def _run_bwd(q, k, v, do, causal, scale=None):
 
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("shape", [(1, 2, 64, 64), (2, 1, 127, 128), (1, 2, 300, 64),
-                                   (1, 1, 513, 128)], ids=lambda s: "x".join(map(str, s)))
+                                   (1, 1, 513, 128), (1, 2, 200, 32), (1, 1, 129, 96),
+                                   (1, 1, 130, 256)], ids=lambda s: "x".join(map(str, s)))
 def test_bwd_fp16(shape, causal):
     B, H, N, d = shape
     _say(f"fp16 B={B} H={H} N={N} d={d} causal={causal}")
@@ -138,6 +144,7 @@ CROSS = [
     # (the first Nq - Nk rows see no key under the causal mask), ragged both ways, one key
     (1, 2, 5, 300, 64), (2, 1, 64, 200, 128), (1, 2, 1, 513, 128), (1, 2, 200, 64, 64),
     (1, 1, 300, 129, 128), (1, 2, 129, 1, 64), (2, 2, 100, 1000, 64),
+    (1, 2, 70, 300, 32), (1, 1, 300, 129, 96), (1, 2, 50, 400, 256),
 ]
 
 
