@@ -293,13 +293,19 @@ class ClockSampler:
             self._thread.start()
         return self
 
-    def stop(self):
+    def halt(self):
+        """Stop sampling (the thread ends after its current reading)."""
         self._stop.set()
         if self._thread is not None:
             self._thread.join()
+            self._thread = None
+
+    def stop(self):
+        self.halt()
         try:
             if self._handle is not None:
                 self._amdsmi.amdsmi_shut_down()
+                self._handle = None
         except Exception:  # noqa: BLE001
             pass
 
@@ -434,21 +440,29 @@ def main(argv=None) -> int:
     clock = ClockSampler(0).start()
     t_settle = time.perf_counter()
     settled = 0
+    t_sampled = t_settle
     if args.settle_seconds > 0:
         # Untimed, reported: enough launches for the clocks to reach their sustained
         # level (a fresh GPU starts from idle clocks).  Synchronised every 16 launches
-        # so that the queue stays short.
+        # so that the queue stays short.  The clock is sampled over the first 70% of
+        # the phase only: no sampling while timed (a sampling thread's calls into the
+        # driver can delay launches, and a delayed launch shows up as idle time in the
+        # events), and the launches go on while the sampler stops, because even a
+        # short idle gap drops the clock again (after 3 s idle the next 20 launches
+        # took 20% longer).
         while True:
             for _ in range(16):
                 step()
             settled += 16
             torch.cuda.synchronize()
-            if time.perf_counter() - t_settle >= args.settle_seconds:
+            elapsed = time.perf_counter() - t_settle
+            if t_sampled == t_settle and elapsed >= 0.7 * args.settle_seconds:
+                clock.halt()
+                t_sampled = time.perf_counter()
+            if elapsed >= args.settle_seconds:
                 break
     settle_s = time.perf_counter() - t_settle
-    # No sampling while timed: a sampling thread's calls into the driver can delay
-    # the launch loop, and a delayed launch shows up as idle time in the events.
-    clock.stop()
+    clock.halt()
 
     for _ in range(args.warmup):
         step()
@@ -484,6 +498,7 @@ def main(argv=None) -> int:
     t_after_end = time.perf_counter()
     if after is not None:
         after.stop()
+    clock.stop()
     launch_ms = [events[i].elapsed_time(events[i + 1]) for i in range(args.steps)]
     kernel_ms = sum(launch_ms) / len(launch_ms)  # average launch duration on the stream
     srt = sorted(launch_ms)
@@ -573,10 +588,10 @@ def main(argv=None) -> int:
                         "note": "amdsmi samples over untimed launches of the same step right "
                                 "after the timed region (nothing samples while timed)"}
                        if after is not None else None),
-                   "gfx_clock_settle": clock.window(t_settle, t_settle + settle_s)},
+                   "gfx_clock_settle": clock.window(t_settle, t_sampled)},
         "settle": {"seconds": round(settle_s, 3), "launches": settled,
                    "note": "untimed launches before the warm-up, so the clocks reach their "
-                           "sustained level"},
+                           "sustained level; the clock is sampled over its first 70% only"},
     }
     if args.cpu_seconds > 0 and not args.backward and not args.ring:
         out["cpu_baseline"], out["parity"] = cpu_baseline(
