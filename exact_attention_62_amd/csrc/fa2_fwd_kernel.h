@@ -72,10 +72,11 @@
 // are dropped by the hardware, and every wavefront issues the same number of
 // stores, which the next item's first wait counts past.
 //
-// Overlap.  The MFMAs of block j+1's S = K Q^T are issued in the same basic
-// block as block j's softmax (vector ALU: exp2, row max/sum, 16-bit packing),
-// so the matrix cores and the vector ALUs work concurrently; the PV MFMAs of
-// block j follow.
+// Overlap.  Block j's row max is formed while block j-1 is finished, so that
+// the one branch of a step (the rescale test) comes first; after it, block
+// j+1's S = K Q^T MFMAs, block j's exp2, row sum and 16-bit packing, block
+// j's PV MFMAs and block j+1's row max all sit in one basic block, where the
+// compiler interleaves the vector ALU work with both MFMA streams.
 //
 // Rescaling.  The running reference max m only moves when a block's row max
 // exceeds it by more than kTau (in log2 units); otherwise O and l keep their
@@ -528,6 +529,9 @@ fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
   float m_lim = kNegInf;  // m_ref + kTau / c: a larger row max moves the reference
   float l_part = 0.f;     // running sum over this lane's half of the keys
   const float tau_raw = kTau / c;
+  // Row max of the block about to be consumed, formed while the block before
+  // it was finished (over the unmasked logits; a masked block forms it again).
+  float mx_c = kNegInf;
 
   auto compute_S = [&](const char* kb, f32x16_t (&S)[KT]) __attribute__((always_inline)) {
 #pragma unroll
@@ -541,11 +545,25 @@ fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
     }
   };
 
+  // Row max over the lane's keys and the lane 32 positions away.
+  auto row_max = [&](const f32x16_t(&S)[KT]) __attribute__((always_inline)) -> float {
+    float mx = kNegInf;
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[kt][r]);
+    return halves_max(mx);
+  };
+
   // Block j's step of the online softmax (new running max, rescaled running
-  // sum, unnormalised probabilities) and the rescaled O update;
-  // `during` issues independent MFMA work (the next block's S) alongside.
-  auto consume = [&](auto masked_tag, int j, f32x16_t(&S)[KT],
-                     auto&& during) __attribute__((always_inline)) {
+  // sum, unnormalised probabilities) and the rescaled O update.  `during`
+  // issues independent MFMA work (the next block's S) after the rescale test,
+  // where it can overlap this block's exps; `after` forms the next block's
+  // row max while the PV product runs.  The row max of block j (mx_c) was
+  // formed by the previous step's `after` (or the item's prologue); a masked
+  // block forms it again after masking.
+  auto consume = [&](auto masked_tag, int j, f32x16_t(&S)[KT], auto&& during,
+                     auto&& after) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked_tag)::value;
     const int k0 = j * BN;
     if constexpr (MASKED) {
@@ -564,14 +582,9 @@ fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
           const int cr = kt * 32 + 8 * (r / 4) + (r % 4);
           S[kt][r] = cr > th ? kNegInf : S[kt][r];
         }
+      mx_c = row_max(S);
     }
-    during();
-    float mx = kNegInf;
-#pragma unroll
-    for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[kt][r]);
-    mx = halves_max(mx);
+    const float mx = mx_c;
     // The reference moves when the block's row max exceeds m_lim = m_ref +
     // kTau / c.  The first block with a visible key always moves it (m_lim =
     // -inf; alpha = exp2(-inf) = 0 then: O and l are still zero).  A block can
@@ -589,17 +602,18 @@ fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
 #pragma unroll
       for (int t = 0; t < DT; ++t) o[t] *= alpha;
     }
-    float ls = 0.f;
+    during();
+    float ls[2] = {0.f, 0.f};  // two chains: shorter dependency, same sum in every form
     t8_t pb[U];
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kt][r], c, -mc));
-        ls += p;
+        ls[r / 8] += p;
         pb[kt * 2 + r / 8][r % 8] = (T)p;  // round to nearest even
       }
-    l_part += ls;
+    l_part += ls[0] + ls[1];
     const char* vb = Vb0 + ((gb + j) & 1) * TBV + vaddr;
 #pragma unroll
     for (int u = 0; u < U; ++u)
@@ -613,6 +627,11 @@ fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
             __builtin_bit_cast(t8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         o[t] = mfma32x32x16(a, pb[u], o[t]);
       }
+    after();
+    // The row sum and the next row max are due before the next block's
+    // barrier: formed here they overlap the PV product (left to itself, the
+    // compiler moves both past the barrier, where nothing overlaps them).
+    asm volatile("" : "+v"(l_part), "+v"(mx_c));
   };
 
   // One barrier per block: block j's V and block j+1's K have landed in LDS,
@@ -662,6 +681,7 @@ fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
     m_lim = kNegInf;
     l_part = 0.f;
     compute_S(Kb0 + (g0 & 1) * TB, S_cur);
+    mx_c = row_max(S_cur);
   };
   // The item after the current one, and its key range.
   int next = -1, nbh = 0, nm = 0, nsp = 0, nbeg = 0, nend = 0;
@@ -784,15 +804,18 @@ fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
     for (; j + 2 <= j_unmasked; j += 2) {
       advance(j);
       consume(std::false_type{}, j, S_cur,
-              [&]() { compute_S(Kb0 + ((gb + j + 1) & 1) * TB, SB); });
+              [&]() { compute_S(Kb0 + ((gb + j + 1) & 1) * TB, SB); },
+              [&]() { mx_c = row_max(SB); });
       advance(j + 1);
       consume(std::false_type{}, j + 1, SB,
-              [&]() { compute_S(Kb0 + ((gb + j) & 1) * TB, S_cur); });
+              [&]() { compute_S(Kb0 + ((gb + j) & 1) * TB, S_cur); },
+              [&]() { mx_c = row_max(S_cur); });
     }
     if (j < j_unmasked) {
       advance(j);
       consume(std::false_type{}, j, S_cur,
-              [&]() { compute_S(Kb0 + ((gb + j + 1) & 1) * TB, SB); });
+              [&]() { compute_S(Kb0 + ((gb + j + 1) & 1) * TB, SB); },
+              [&]() { mx_c = row_max(SB); });
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt) S_cur[kt] = SB[kt];
       ++j;
@@ -800,15 +823,15 @@ fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
     for (; j + 2 < j_cend; j += 2) {
       advance(j);
       consume(std::true_type{}, j, S_cur,
-              [&]() { compute_S(Kb0 + ((gb + j + 1) & 1) * TB, SB); });
+              [&]() { compute_S(Kb0 + ((gb + j + 1) & 1) * TB, SB); }, [] {});
       advance(j + 1);
       consume(std::true_type{}, j + 1, SB,
-              [&]() { compute_S(Kb0 + ((gb + j) & 1) * TB, S_cur); });
+              [&]() { compute_S(Kb0 + ((gb + j) & 1) * TB, S_cur); }, [] {});
     }
     if (j + 1 < j_cend) {
       advance(j);
       consume(std::true_type{}, j, S_cur,
-              [&]() { compute_S(Kb0 + ((gb + j + 1) & 1) * TB, SB); });
+              [&]() { compute_S(Kb0 + ((gb + j + 1) & 1) * TB, SB); }, [] {});
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt) S_cur[kt] = SB[kt];
       ++j;
@@ -821,7 +844,7 @@ fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
     if (j + 1 == j_end) prefetch_next();
     // Always the masked form: one copy of the code, and for an unmasked block
     // the threshold test hides nothing.
-    consume(std::true_type{}, j, S_cur, [] {});
+    consume(std::true_type{}, j, S_cur, [] {}, [] {});
     // Blocks hidden from all of this wavefront's rows: loads and barriers.
     for (++j; j < j_end; ++j) {
       advance(j);
