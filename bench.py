@@ -6,9 +6,11 @@
 A step is one fa2_fwd call (the whole hot path: one kernel launch) over the
 workload's inputs (with --splits: one fa2_fwd_splitkv call, the split kernel and
 the merge kernel), which are generated with the seeded recipe and copied to
-HBM before timing starts.  First a settle phase (--settle-seconds of untimed
-steps, reported in the line as "settle", so that a GPU that was idle reaches its
-sustained clocks), then W untimed warm-up steps, then exactly K timed steps
+HBM before timing starts.  First a settle phase (untimed steps for at least
+--settle-seconds and until the launch rate of two consecutive quarter seconds
+agrees within 2%, at most --settle-max-seconds; reported in the line as
+"settle"), so that a GPU that was idle reaches its sustained clocks (a box's
+first run can take a few seconds), then W untimed warm-up steps, then exactly K timed steps
 bracketed by torch.cuda.synchronize().  An event recorded on the stream the
 kernels are enqueued on separates consecutive launches, so every launch is
 timed on its own: the roofline uses their mean, and the line gives their
@@ -89,8 +91,11 @@ def parse_args(argv=None):
                    help="untimed launches after the timed region while the shader clock is "
                         "sampled (0: no clock sampling)")
     p.add_argument("--settle-seconds", type=float, default=1.0,
-                   help="before the warm-up steps, run steps for this many seconds so the clocks "
-                        "reach their sustained level (reported as 'settle'; 0 disables it)")
+                   help="before the warm-up steps, run steps for at least this many seconds, and "
+                        "on until the launch rate is steady, so the clocks reach their sustained "
+                        "level (reported as 'settle'; 0 disables it)")
+    p.add_argument("--settle-max-seconds", type=float, default=8.0,
+                   help="upper bound of the settle phase")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target duration of the CPU-oracle baseline sample (0 disables it)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -437,10 +442,17 @@ def main(argv=None) -> int:
             fa2_fwd(q, k, v, o, lse, causal=causal, scale=scale)
 
     props = torch.cuda.get_device_properties(dev)
+    # One event between consecutive timed launches, all on the stream the kernels
+    # are enqueued on: launch i runs between events i and i+1.  Created before
+    # the settle phase: creating them between the warm-up and the timed region
+    # left the GPU idle long enough, on a box's first run, for the next launches
+    # to run up to a third slower for some 30 ms.
+    events = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     clock = ClockSampler(0).start()
     t_settle = time.perf_counter()
     settled = 0
     t_sampled = t_settle
+    steady, rate_prev, rate_last = False, None, None
     if args.settle_seconds > 0:
         # Untimed, reported: enough launches for the clocks to reach their sustained
         # level (a fresh GPU starts from idle clocks).  Synchronised every 16 launches
@@ -450,27 +462,32 @@ def main(argv=None) -> int:
         # events), and the launches go on while the sampler stops, because even a
         # short idle gap drops the clock again (after 3 s idle the next 20 launches
         # took 20% longer).
+        # After the minimum, the phase goes on until two consecutive quarter-second
+        # windows run launches at rates within 2% of each other (a box's first run
+        # has taken seconds to reach its clocks).
+        t_win, n_win = t_settle, 0
         while True:
             for _ in range(16):
                 step()
             settled += 16
+            n_win += 16
             torch.cuda.synchronize()
-            elapsed = time.perf_counter() - t_settle
+            now = time.perf_counter()
+            elapsed = now - t_settle
             if t_sampled == t_settle and elapsed >= 0.7 * args.settle_seconds:
                 clock.halt()
                 t_sampled = time.perf_counter()
-            if elapsed >= args.settle_seconds:
+            if now - t_win >= 0.25:
+                rate_prev, rate_last = rate_last, (now - t_win) / n_win
+                t_win, n_win = now, 0
+                steady = rate_prev is not None and abs(rate_last - rate_prev) <= 0.02 * rate_prev
+            if elapsed >= args.settle_seconds and (steady or elapsed >= args.settle_max_seconds):
                 break
     settle_s = time.perf_counter() - t_settle
     clock.halt()
 
     for _ in range(args.warmup):
         step()
-    torch.cuda.synchronize()
-
-    # One event between consecutive launches, all on the stream the kernels are
-    # enqueued on: launch i runs between events i and i+1.
-    events = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     events[0].record(stream)
@@ -589,9 +606,14 @@ def main(argv=None) -> int:
                                 "after the timed region (nothing samples while timed)"}
                        if after is not None else None),
                    "gfx_clock_settle": clock.window(t_settle, t_sampled)},
-        "settle": {"seconds": round(settle_s, 3), "launches": settled,
-                   "note": "untimed launches before the warm-up, so the clocks reach their "
-                           "sustained level; the clock is sampled over its first 70% only"},
+        "settle": {"seconds": round(settle_s, 3), "launches": settled, "steady": steady,
+                   "ms_per_launch_last_windows": (
+                       [round(1e3 * x, 5) for x in (rate_prev, rate_last) if x is not None]),
+                   "note": "untimed launches before the warm-up, at least --settle-seconds and "
+                           "until two consecutive quarter-second windows agree within 2% on "
+                           "the launch rate (wall clock, 16 launches per synchronisation), "
+                           "so the clocks reach their sustained level; the clock is sampled "
+                           "over the first 70% of the minimum only"},
     }
     if args.cpu_seconds > 0 and not args.backward and not args.ring:
         out["cpu_baseline"], out["parity"] = cpu_baseline(
