@@ -28,12 +28,14 @@
 // and light causal blocks balance.  While the last K/V block of an item is
 // processed, the next item's Q rows and first K/V blocks are already loading.
 //
-// Issue priority.  Where two workgroups share a CU, the SIMDs' arbitration
-// favours the older one: with the same number of blocks each, the younger
-// finished up to 15% later and then ran alone on its CU.  Each wavefront
-// therefore lowers its priority (s_setprio 3, 2, 1, 0) as its workgroup
-// passes each quarter of its blocks, so that the partner that is behind wins
-// the arbitration until it reaches the same quarter.
+// Issue priority.  Where two workgroups share a CU (four wavefronts each), the
+// SIMDs' arbitration favours the older one: with the same number of blocks
+// each, the younger finished up to 15% later and then ran alone on its CU.
+// Each wavefront therefore lowers its priority (s_setprio 3, 2, 1, 0) as its
+// workgroup passes each quarter of its blocks, so that the partner that is
+// behind wins the arbitration until it reaches the same quarter.  The
+// eight-wavefront form has its CU to itself and keeps the default priority
+// (the test and branch per block cost it 1-2%).
 //
 // Wavefront layout (the pages' split-Q warp scheme, re-derived for 64-wide
 // wavefronts and 32x32 MFMA tiles): each wavefront owns 32 query rows against
@@ -643,7 +645,7 @@ fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
     if (j == j_beg && k_item > 0) wait_vmcnt<NSTORE>();
     else wait_vmcnt<0>();
     lds_barrier();
-    if (g0 + (j - j_beg) >= prio_next) {  // a quarter of the blocks passed
+    if (kWaves == 4 && g0 + (j - j_beg) >= prio_next) {  // a quarter of the blocks passed
       prio_next += prio_step;
       --prio_level;
       if (prio_level == 2) __builtin_amdgcn_s_setprio(2);
@@ -783,7 +785,7 @@ fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
     }
     prio_step = max(1, (blocks + 3) / 4);
     prio_next = prio_step;
-    __builtin_amdgcn_s_setprio(3);
+    if constexpr (kWaves == 4) __builtin_amdgcn_s_setprio(3);
   }
   set_item(logical);
   if (!finish_empty_items()) return;
