@@ -288,13 +288,22 @@ fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
   static_assert(lds_off<D>(BN - 1) + ROWB <= TB, "K rows stay inside their buffer");
   static_assert(LOADS_V >= 1 && TBV % (1024 * kWaves) == 0, "V block must split evenly");
   static_assert(v_layout_ok<D, BN>(), "V LDS layout: direct loads and transposing reads");
-  static_assert(groups_per_cu<WAVES, OCC>() * (2 * TBV + 2 * TB) <= 160 * 1024,
+  // Eight-wavefront form: the next item's Q rows are loaded whole (lane l of
+  // load n: row 4n + l/16 of the wavefront's 32, 16-byte chunk l%16), into
+  // the Q registers, and rearranged into the MFMA operand layout through
+  // QB bytes of LDS in the prologue.  (Loaded in that layout straight from
+  // memory, each lane reads its own row: 32 rows per load instruction, which
+  // held the last block of every item up by thousands of cycles.)
+  constexpr bool QT = WAVES == 8;
+  constexpr int QB = QT ? kBM * ROWB : 0;
+  static_assert(!QT || D == 128, "Q rearrangement: 16 chunks of 16 bytes per row");
+  static_assert(groups_per_cu<WAVES, OCC>() * (2 * TBV + 2 * TB + QB) <= 160 * 1024,
                 "the resident workgroups' LDS fits a CU");
   static_assert(TBV + 16 * ROWB * (U - 1) + 8 * ROWB + 256 * (DT - 1) < 65536 &&
                     2 * TBV + TB + KTSTEP * (KT - 1) + 32 * (KS - 1) < 65536,
                 "LDS offsets fit the 16-bit instruction offset");
 
-  __shared__ __attribute__((aligned(1024))) char smem[2 * TBV + 2 * TB];  // V0 V1 K0 K1
+  __shared__ __attribute__((aligned(1024))) char smem[2 * TBV + 2 * TB + QB];  // V0 V1 K0 K1 Q
   char* const Vb0 = smem;
   char* const Kb0 = smem + 2 * TBV;
 
@@ -410,6 +419,40 @@ fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
       qf[ks] = __builtin_bit_cast(t8_t, t);
     }
   };
+  // Whole-row loads (eight-wavefront form): qf[n] of lane l = row 4n + l/16
+  // of the wavefront's 32 (rows past Nq read as zero), chunk l%16.
+  auto load_q_rows = [&](const uint16_t* qh, int row0) __attribute__((always_inline)) {
+    const int ql = fresh_lane();
+#pragma unroll
+    for (int n = 0; n < KS; ++n) {
+      const int row = row0 + 4 * n + (ql >> 4);
+      u32x4_t t = {0u, 0u, 0u, 0u};
+      if (row < Nq) t = *(const u32x4_t*)(qh + (size_t)row * D + (ql & 15) * 8);
+      qf[n] = __builtin_bit_cast(t8_t, t);
+    }
+  };
+  // ... and into the operand layout through this wavefront's 8 KB of LDS: row
+  // r's chunk c sits at slot c ^ (r % 16) of the row, so that the writes (16
+  // chunks of one row per 16 lanes) and the reads (one chunk index of 16 rows)
+  // meet 16 different bank groups.  Only this wavefront touches its area.
+  auto arrange_q = [&]() __attribute__((always_inline)) {
+    if constexpr (QT) {
+      char* const qs = smem + 2 * TBV + 2 * TB + wave * 32 * ROWB;
+      const int ql = fresh_lane();
+#pragma unroll
+      for (int n = 0; n < KS; ++n) {
+        const int r = 4 * n + (ql >> 4);
+        *(t8_t*)(qs + r * ROWB + (((ql & 15) ^ (r & 15)) * 16)) = qf[n];
+      }
+      // Other lanes' writes are read below: the wavefront's LDS accesses run in
+      // order, and this keeps the compiler from moving a read above a write.
+      asm volatile("" ::: "memory");
+      const int qc = ql & 31, qhf = ql >> 5;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        qf[ks] = *(const t8_t*)(qs + qc * ROWB + (((2 * ks + qhf) ^ (qc & 15)) * 16));
+    }
+  };
   // After the sign/zero fix, the fragments pass through an empty asm
   // statement: the compiler waits for the Q loads there, once per item, and
   // from then on sees register values with no load pending (it cannot see the
@@ -500,9 +543,10 @@ fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
   // The first blocks of an item (blocks beg, beg+1, ... of its range): Q rows,
   // K_beg and V_beg, and K_beg+1 if the range has it.  g is the running block
   // count of this workgroup: block g of the sequence uses buffers g & 1.
-  auto issue_item_start = [&](const uint16_t* qh, const uint16_t* kh, const uint16_t* vh, int row,
+  auto issue_item_start = [&](const uint16_t* qh, const uint16_t* kh, const uint16_t* vh, int row0,
                               int beg, int blocks, int g) __attribute__((always_inline)) {
-    load_q(qh, row);
+    if constexpr (QT) load_q_rows(qh, row0);
+    else load_q(qh, row0 + col);
     issue_k(kh, beg * BN, Kb0 + (g & 1) * TB);
     issue_v(vh, beg * BN, Vb0 + (g & 1) * TBV);
     if (blocks > 1) issue_k(kh, (beg + 1) * BN, Kb0 + ((g + 1) & 1) * TB);
@@ -666,6 +710,7 @@ fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
   // everything.
   f32x16_t S_cur[KT];
   auto prologue = [&](auto later_tag) __attribute__((always_inline)) {
+    arrange_q();
     fix_q();
     const bool two = j_end - j_beg > 1;
     if constexpr (decltype(later_tag)::value) {
@@ -699,7 +744,7 @@ fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
   auto prefetch_next = [&]() __attribute__((always_inline)) {
     if (next >= 0 && nend > nbeg) {
       const size_t nqs = (size_t)nbh * (size_t)Nq * D, nks = (size_t)nbh * (size_t)Nk * D;
-      issue_item_start(Qg + nqs, Kg + nks, Vg + nks, nm * kBM + rgrp * 32 + col, nbeg,
+      issue_item_start(Qg + nqs, Kg + nks, Vg + nks, nm * kBM + rgrp * 32, nbeg,
                        nend - nbeg, g0 + (j_end - j_beg));
     }
   };
@@ -790,7 +835,7 @@ fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
   set_item(logical);
   if (!finish_empty_items()) return;
   if (k_item == 0) {
-    issue_item_start(Qh, Kh, Vh, qrow, j_beg, j_end - j_beg, g0);
+    issue_item_start(Qh, Kh, Vh, q0, j_beg, j_end - j_beg, g0);
     prologue(std::false_type{});
   } else {
     prologue(std::true_type{});  // prefetched by the last empty item, stores after it
