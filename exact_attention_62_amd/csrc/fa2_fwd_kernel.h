@@ -685,8 +685,10 @@ fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
   // for blocks j+2 (K) and j+1 (V) issued right after reuse.
   auto advance = [&](int j) __attribute__((always_inline)) {
     // At an item's first block the previous item's O and L stores, issued
-    // last, need not have completed.
-    if (j == j_beg && k_item > 0) wait_vmcnt<NSTORE>();
+    // last, need not have completed.  (The eight-wavefront form waits for
+    // them too: by then they have had the item edge to complete, and the
+    // block loop without the test runs 0-1% faster.)
+    if (kWaves == 4 && j == j_beg && k_item > 0) wait_vmcnt<NSTORE>();
     else wait_vmcnt<0>();
     lds_barrier();
     if (kWaves == 4 && g0 + (j - j_beg) >= prio_next) {  // a quarter of the blocks passed
