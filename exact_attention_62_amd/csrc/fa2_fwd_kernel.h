@@ -683,7 +683,9 @@ fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
   // One barrier per block: block j's V and block j+1's K have landed in LDS,
   // and every wavefront is done with the buffers of block j-1, which the loads
   // for blocks j+2 (K) and j+1 (V) issued right after reuse.
-  auto advance = [&](int j) __attribute__((always_inline)) {
+  // k_known / v_known: the caller knows that block j+2 (K) / j+1 (V) exists
+  // (the loops of block pairs below), so the test is left out of the loop.
+  auto advance = [&](int j, auto k_known, auto v_known) __attribute__((always_inline)) {
     // At an item's first block the previous item's O and L stores, issued
     // last, need not have completed.  (The eight-wavefront form waits for
     // them too: by then they have had the item edge to complete, and the
@@ -698,8 +700,8 @@ fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
       else if (prio_level == 1) __builtin_amdgcn_s_setprio(1);
       else __builtin_amdgcn_s_setprio(0);
     }
-    if (j + 2 < j_end) issue_k(Kh, (j + 2) * BN, Kb0 + ((gb + j) & 1) * TB);
-    if (j + 1 < j_end) issue_v(Vh, (j + 1) * BN, Vb0 + ((gb + j + 1) & 1) * TBV);
+    if (decltype(k_known)::value || j + 2 < j_end) issue_k(Kh, (j + 2) * BN, Kb0 + ((gb + j) & 1) * TB);
+    if (decltype(v_known)::value || j + 1 < j_end) issue_v(Vh, (j + 1) * BN, Vb0 + ((gb + j + 1) & 1) * TBV);
   };
 
   // ---- item prologue: wait for Q and K_beg, then S for the first block.
@@ -851,17 +853,17 @@ fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
     // Unrolled by two so that the S registers alternate between S_cur and SB
     // instead of being copied every block.
     for (; j + 2 <= j_unmasked; j += 2) {
-      advance(j);
+      advance(j, std::true_type{}, std::true_type{});
       consume(std::false_type{}, j, S_cur,
               [&]() { compute_S(Kb0 + ((gb + j + 1) & 1) * TB, SB); },
               [&]() { mx_c = row_max(SB); });
-      advance(j + 1);
+      advance(j + 1, std::false_type{}, std::true_type{});
       consume(std::false_type{}, j + 1, SB,
               [&]() { compute_S(Kb0 + ((gb + j) & 1) * TB, S_cur); },
               [&]() { mx_c = row_max(S_cur); });
     }
     if (j < j_unmasked) {
-      advance(j);
+      advance(j, std::false_type{}, std::false_type{});
       consume(std::false_type{}, j, S_cur,
               [&]() { compute_S(Kb0 + ((gb + j + 1) & 1) * TB, SB); },
               [&]() { mx_c = row_max(SB); });
@@ -870,15 +872,15 @@ fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
       ++j;
     }
     for (; j + 2 < j_cend; j += 2) {
-      advance(j);
+      advance(j, std::true_type{}, std::true_type{});
       consume(std::true_type{}, j, S_cur,
               [&]() { compute_S(Kb0 + ((gb + j + 1) & 1) * TB, SB); }, [] {});
-      advance(j + 1);
+      advance(j + 1, std::false_type{}, std::true_type{});
       consume(std::true_type{}, j + 1, SB,
               [&]() { compute_S(Kb0 + ((gb + j) & 1) * TB, S_cur); }, [] {});
     }
     if (j + 1 < j_cend) {
-      advance(j);
+      advance(j, std::false_type{}, std::false_type{});
       consume(std::true_type{}, j, S_cur,
               [&]() { compute_S(Kb0 + ((gb + j + 1) & 1) * TB, SB); }, [] {});
 #pragma unroll
@@ -889,14 +891,14 @@ fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
     // K buffers and the other V buffer are free, and so are the Q registers:
     // the next item's Q, K_beg, V_beg, K_beg+1 go out there and overlap that
     // block's softmax, its PV product and the O stores.
-    advance(j);
+    advance(j, std::false_type{}, std::false_type{});
     if (j + 1 == j_end) prefetch_next();
     // Always the masked form: one copy of the code, and for an unmasked block
     // the threshold test hides nothing.
     consume(std::true_type{}, j, S_cur, [] {}, [] {});
     // Blocks hidden from all of this wavefront's rows: loads and barriers.
     for (++j; j < j_end; ++j) {
-      advance(j);
+      advance(j, std::false_type{}, std::false_type{});
       if (j + 1 == j_end) prefetch_next();
     }
     store_result();
