@@ -543,13 +543,20 @@ fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
   // The first blocks of an item (blocks beg, beg+1, ... of its range): Q rows,
   // K_beg and V_beg, and K_beg+1 if the range has it.  g is the running block
   // count of this workgroup: block g of the sequence uses buffers g & 1.
-  auto issue_item_start = [&](const uint16_t* qh, const uint16_t* kh, const uint16_t* vh, int row0,
-                              int beg, int blocks, int g) __attribute__((always_inline)) {
+  auto issue_item_q = [&](const uint16_t* qh, int row0) __attribute__((always_inline)) {
     if constexpr (QT) load_q_rows(qh, row0);
     else load_q(qh, row0 + col);
+  };
+  auto issue_item_kv = [&](const uint16_t* kh, const uint16_t* vh, int beg, int blocks,
+                           int g) __attribute__((always_inline)) {
     issue_k(kh, beg * BN, Kb0 + (g & 1) * TB);
     issue_v(vh, beg * BN, Vb0 + (g & 1) * TBV);
     if (blocks > 1) issue_k(kh, (beg + 1) * BN, Kb0 + ((g + 1) & 1) * TB);
+  };
+  auto issue_item_start = [&](const uint16_t* qh, const uint16_t* kh, const uint16_t* vh, int row0,
+                              int beg, int blocks, int g) __attribute__((always_inline)) {
+    issue_item_q(qh, row0);
+    issue_item_kv(kh, vh, beg, blocks, g);
   };
 
   // ---- LDS fragment addresses (bytes within a block buffer).
@@ -752,6 +759,20 @@ fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
                        nend - nbeg, g0 + (j_end - j_beg));
     }
   };
+  // The same in two parts, for a wavefront whose rows see none of the item's
+  // last blocks: its Q registers are free from its last computed block on, so
+  // its share of the next item's Q goes out then, and the next item's first
+  // K/V blocks (whose buffers free up only at the item's last block) later.
+  auto prefetch_next_q = [&]() __attribute__((always_inline)) {
+    if (next >= 0 && nend > nbeg)
+      issue_item_q(Qg + (size_t)nbh * (size_t)Nq * D, nm * kBM + rgrp * 32);
+  };
+  auto prefetch_next_kv = [&]() __attribute__((always_inline)) {
+    if (next >= 0 && nend > nbeg) {
+      const size_t nks = (size_t)nbh * (size_t)Nk * D;
+      issue_item_kv(Kg + nks, Vg + nks, nbeg, nend - nbeg, g0 + (j_end - j_beg));
+    }
+  };
   // ---- item epilogue, after the KV loop: O = O / l once, L = m + ln(l).
   // (A row that saw no key has l = 0: O = 0 and L = -inf.)
   auto store_result = [&]() __attribute__((always_inline)) {
@@ -897,9 +918,16 @@ fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
     // the threshold test hides nothing.
     consume(std::true_type{}, j, S_cur, [] {}, [] {});
     // Blocks hidden from all of this wavefront's rows: loads and barriers.
-    for (++j; j < j_end; ++j) {
+    // Its next Q rows go out after the first of them (its Q registers are
+    // free; the item's last block then issues less at once).
+    if (++j < j_end) {
       advance(j, std::false_type{}, std::false_type{});
-      if (j + 1 == j_end) prefetch_next();
+      prefetch_next_q();
+      if (j + 1 == j_end) prefetch_next_kv();
+      for (++j; j < j_end; ++j) {
+        advance(j, std::false_type{}, std::false_type{});
+        if (j + 1 == j_end) prefetch_next_kv();
+      }
     }
     store_result();
     if (next < 0) break;
