@@ -288,15 +288,16 @@ fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
   static_assert(lds_off<D>(BN - 1) + ROWB <= TB, "K rows stay inside their buffer");
   static_assert(LOADS_V >= 1 && TBV % (1024 * kWaves) == 0, "V block must split evenly");
   static_assert(v_layout_ok<D, BN>(), "V LDS layout: direct loads and transposing reads");
-  // Eight-wavefront form: the next item's Q rows are loaded whole (lane l of
-  // load n: row 4n + l/16 of the wavefront's 32, 16-byte chunk l%16), into
-  // the Q registers, and rearranged into the MFMA operand layout through
-  // QB bytes of LDS in the prologue.  (Loaded in that layout straight from
-  // memory, each lane reads its own row: 32 rows per load instruction, which
-  // held the last block of every item up by thousands of cycles.)
+  // Eight-wavefront form: the next item's Q rows go by direct loads of whole
+  // rows into QB bytes of LDS (8 KB per wavefront), and the prologue reads
+  // them from there in the MFMA operand layout.  (Loaded in that layout
+  // straight from memory, each lane reads its own row: 32 rows per load
+  // instruction, which held the last block of every item up by thousands of
+  // cycles.)
   constexpr bool QT = WAVES == 8;
   constexpr int QB = QT ? kBM * ROWB : 0;
-  static_assert(!QT || D == 128, "Q rearrangement: 16 chunks of 16 bytes per row");
+  constexpr int QLOADS = 32 * ROWB / 1024;  // direct loads of a wavefront's 32 Q rows
+  static_assert(!QT || D == 128, "Q rows through LDS: 16 chunks of 16 bytes per row");
   static_assert(groups_per_cu<WAVES, OCC>() * (2 * TBV + 2 * TB + QB) <= 160 * 1024,
                 "the resident workgroups' LDS fits a CU");
   static_assert(TBV + 16 * ROWB * (U - 1) + 8 * ROWB + 256 * (DT - 1) < 65536 &&
@@ -419,38 +420,40 @@ fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
       qf[ks] = __builtin_bit_cast(t8_t, t);
     }
   };
-  // Whole-row loads (eight-wavefront form): qf[n] of lane l = row 4n + l/16
-  // of the wavefront's 32 (rows past Nq read as zero), chunk l%16.
-  auto load_q_rows = [&](const uint16_t* qh, int row0) __attribute__((always_inline)) {
+  // Whole-row direct loads (eight-wavefront form) into this wavefront's 8 KB
+  // of LDS: load n fills rows 4n .. 4n+3 of the wavefront's 32, lane l the
+  // 16-byte slot l%16 of row r = 4n + l/16.  Row r's chunk c sits at slot
+  // c ^ (r % 16), so lane l fetches chunk (l%16) ^ (r%16); the operand reads
+  // below (one chunk index of 16 rows per 16 lanes) then meet 16 different
+  // bank groups.  Rows past Nq are clamped to row Nq-1: their results are
+  // never stored.  Only this wavefront touches its area.
+  char* const q_area = smem + 2 * TBV + 2 * TB + wave * 32 * ROWB;
+  auto load_q_lds = [&](const uint16_t* qh, int row0) __attribute__((always_inline)) {
     const int ql = fresh_lane();
+    const int rl = ql >> 4, sl = ql & 15;
+    if (row0 + 32 <= Nq) {
 #pragma unroll
-    for (int n = 0; n < KS; ++n) {
-      const int row = row0 + 4 * n + (ql >> 4);
-      u32x4_t t = {0u, 0u, 0u, 0u};
-      if (row < Nq) t = *(const u32x4_t*)(qh + (size_t)row * D + (ql & 15) * 8);
-      qf[n] = __builtin_bit_cast(t8_t, t);
+      for (int n = 0; n < QLOADS; ++n) {
+        const uint32_t voff = (uint32_t)(rl * D + (sl ^ ((4 * n + rl) & 15)) * 8) * 2;
+        lds_dma(qh + (size_t)(row0 + 4 * n) * D, voff, lds_addr(q_area + n * 1024));
+      }
+    } else {
+#pragma unroll
+      for (int n = 0; n < QLOADS; ++n) {
+        const int r = 4 * n + rl;
+        lds_dma(qh + (size_t)min(row0 + r, Nq - 1) * D + (sl ^ (r & 15)) * 8,
+                lds_addr(q_area + n * 1024));
+      }
     }
   };
-  // ... and into the operand layout through this wavefront's 8 KB of LDS: row
-  // r's chunk c sits at slot c ^ (r % 16) of the row, so that the writes (16
-  // chunks of one row per 16 lanes) and the reads (one chunk index of 16 rows)
-  // meet 16 different bank groups.  Only this wavefront touches its area.
-  auto arrange_q = [&]() __attribute__((always_inline)) {
+  // ... read in the operand layout once they have landed (prologue).
+  auto read_q = [&]() __attribute__((always_inline)) {
     if constexpr (QT) {
-      char* const qs = smem + 2 * TBV + 2 * TB + wave * 32 * ROWB;
       const int ql = fresh_lane();
-#pragma unroll
-      for (int n = 0; n < KS; ++n) {
-        const int r = 4 * n + (ql >> 4);
-        *(t8_t*)(qs + r * ROWB + (((ql & 15) ^ (r & 15)) * 16)) = qf[n];
-      }
-      // Other lanes' writes are read below: the wavefront's LDS accesses run in
-      // order, and this keeps the compiler from moving a read above a write.
-      asm volatile("" ::: "memory");
       const int qc = ql & 31, qhf = ql >> 5;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        qf[ks] = *(const t8_t*)(qs + qc * ROWB + (((2 * ks + qhf) ^ (qc & 15)) * 16));
+        qf[ks] = *(const t8_t*)(q_area + qc * ROWB + (((2 * ks + qhf) ^ (qc & 15)) * 16));
     }
   };
   // After the sign/zero fix, the fragments pass through an empty asm
@@ -544,7 +547,7 @@ fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
   // K_beg and V_beg, and K_beg+1 if the range has it.  g is the running block
   // count of this workgroup: block g of the sequence uses buffers g & 1.
   auto issue_item_q = [&](const uint16_t* qh, int row0) __attribute__((always_inline)) {
-    if constexpr (QT) load_q_rows(qh, row0);
+    if constexpr (QT) load_q_lds(qh, row0);
     else load_q(qh, row0 + col);
   };
   auto issue_item_kv = [&](const uint16_t* kh, const uint16_t* vh, int beg, int blocks,
@@ -721,9 +724,20 @@ fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
   // everything.
   f32x16_t S_cur[KT];
   auto prologue = [&](auto later_tag) __attribute__((always_inline)) {
-    arrange_q();
-    fix_q();
     const bool two = j_end - j_beg > 1;
+    if constexpr (QT) {
+      // The Q rows (the oldest loads in flight) have landed; K, V and the
+      // stores may still be in flight.
+      if constexpr (decltype(later_tag)::value) {
+        if (two) wait_vmcnt<LOADS_V + 2 * LOADS + NSTORE>();
+        else wait_vmcnt<LOADS_V + LOADS + NSTORE>();
+      } else {
+        if (two) wait_vmcnt<LOADS_V + 2 * LOADS>();
+        else wait_vmcnt<LOADS_V + LOADS>();
+      }
+      read_q();
+    }
+    fix_q();
     if constexpr (decltype(later_tag)::value) {
       if (two) wait_vmcnt<LOADS_V + LOADS + NSTORE>();
       else wait_vmcnt<LOADS_V + NSTORE>();
@@ -760,9 +774,10 @@ fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
     }
   };
   // The same in two parts, for a wavefront whose rows see none of the item's
-  // last blocks: its Q registers are free from its last computed block on, so
-  // its share of the next item's Q goes out then, and the next item's first
-  // K/V blocks (whose buffers free up only at the item's last block) later.
+  // last blocks: its Q registers (with eight wavefronts, its Q area of LDS,
+  // read in the prologue) are free from its last computed block on, so its
+  // share of the next item's Q goes out then, and the next item's first K/V
+  // blocks (whose buffers free up only at the item's last block) later.
   auto prefetch_next_q = [&]() __attribute__((always_inline)) {
     if (next >= 0 && nend > nbeg)
       issue_item_q(Qg + (size_t)nbh * (size_t)Nq * D, nm * kBM + rgrp * 32);
@@ -909,17 +924,17 @@ fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
       ++j;
     }
     // Last block that this wavefront computes.  At the item's last block both
-    // K buffers and the other V buffer are free, and so are the Q registers:
-    // the next item's Q, K_beg, V_beg, K_beg+1 go out there and overlap that
-    // block's softmax, its PV product and the O stores.
+    // K buffers and the other V buffer are free, and so are the Q registers
+    // (or Q area): the next item's Q, K_beg, V_beg, K_beg+1 go out there and
+    // overlap that block's softmax, its PV product and the O stores.
     advance(j, std::false_type{}, std::false_type{});
     if (j + 1 == j_end) prefetch_next();
     // Always the masked form: one copy of the code, and for an unmasked block
     // the threshold test hides nothing.
     consume(std::true_type{}, j, S_cur, [] {}, [] {});
     // Blocks hidden from all of this wavefront's rows: loads and barriers.
-    // Its next Q rows go out after the first of them (its Q registers are
-    // free; the item's last block then issues less at once).
+    // Its next Q rows go out after the first of them (its Q registers or Q
+    // area are free; the item's last block then issues less at once).
     if (++j < j_end) {
       advance(j, std::false_type{}, std::false_type{});
       prefetch_next_q();

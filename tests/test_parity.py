@@ -244,8 +244,9 @@ def test_ragged_sigma2_reading():
 def test_wide_workgroups_ragged(causal, dtype):
     # 64 heads x ceil(1000 / 256) = 256 items: the 256-row, eight-wavefront
     # kernel, with a ragged last block, query rows past the end inside the last
-    # item (loaded as zero by the whole-row Q loads) and (causal) blocks hidden
-    # from the first wavefronts' rows, whose next Q rows go out early.
+    # item (the direct Q loads clamp them to the last row; they are never
+    # stored) and (causal) blocks hidden from the first wavefronts' rows, whose
+    # next Q rows go out early.
     assert fa2_launch_shape(1, 64, 1000, 128)[0] == 256
     _say(f"wide {dtype} B=1 H=64 N=1000 d=128 causal={causal}")
     q, k, v = make_random(1, 64, 1000, 128, seed=91 + causal, dtype=dtype)
