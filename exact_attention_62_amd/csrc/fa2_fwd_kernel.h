@@ -250,6 +250,40 @@ template <int D, int BN> __host__ __device__ constexpr bool v_layout_ok() {
         }
   return true;
 }
+// Q rows staged in LDS (a wavefront's 32 rows of 2D bytes, QC = D/8 chunks of
+// 16 bytes each): chunk c of row r sits at slot c ^ q_swz(r) of the row.
+template <int D> __host__ __device__ constexpr int q_swz(int r) {
+  return (r * (D / 8) / 16) & (D / 8 - 1);
+}
+// Compile-time proof of that layout: direct load n, lane l (16 bytes at
+// n*1024 + 16*l) fills slot l % QC of row QRPL*n + l / QC with the chunk that
+// belongs there, every (row, chunk) exactly once; the operand read of k-step
+// ks (lane l: chunk 2*ks + l/32 of row l%32) finds that chunk; and each
+// 16-lane group of a read meets 16 different 16-byte bank groups.
+template <int D> __host__ __device__ constexpr bool q_layout_ok() {
+  constexpr int ROWB = 2 * D, QC = D / 8, QRPL = 1024 / ROWB;
+  if (QC < 4 || QC > 16 || (QC & (QC - 1)) != 0 || QRPL * QC != 64) return false;
+  int where[32 * 16] = {};
+  for (int i = 0; i < 32 * QC; ++i) where[i] = -1;
+  for (int n = 0; n < 32 * ROWB / 1024; ++n)
+    for (int l = 0; l < 64; ++l) {
+      const int r = QRPL * n + l / QC, c = (l % QC) ^ q_swz<D>(r), off = n * 1024 + 16 * l;
+      if (off != r * ROWB + (l % QC) * 16 || where[r * QC + c] != -1) return false;
+      where[r * QC + c] = off;
+    }
+  for (int ks = 0; ks < D / 16; ++ks)
+    for (int grp = 0; grp < 4; ++grp) {
+      bool used[16] = {};
+      for (int l = 16 * grp; l < 16 * grp + 16; ++l) {
+        const int qc = l & 31, c = 2 * ks + (l >> 5);
+        const int off = qc * ROWB + ((c ^ q_swz<D>(qc)) * 16);
+        if (where[qc * QC + c] != off || used[(off / 16) % 16]) return false;
+        used[(off / 16) % 16] = true;
+      }
+    }
+  return true;
+}
+static_assert(q_layout_ok<128>(), "Q LDS layout");
 
 template <typename T, int D, bool CAUSAL, bool SPLIT, int WAVES, int OCC>
 __global__ void __launch_bounds__(64 * WAVES, (groups_per_cu<WAVES, OCC>()))
@@ -288,16 +322,19 @@ fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
   static_assert(lds_off<D>(BN - 1) + ROWB <= TB, "K rows stay inside their buffer");
   static_assert(LOADS_V >= 1 && TBV % (1024 * kWaves) == 0, "V block must split evenly");
   static_assert(v_layout_ok<D, BN>(), "V LDS layout: direct loads and transposing reads");
-  // Eight-wavefront form: the next item's Q rows go by direct loads of whole
-  // rows into QB bytes of LDS (8 KB per wavefront), and the prologue reads
-  // them from there in the MFMA operand layout.  (Loaded in that layout
+  // Eight-wavefront form (d = 128): the next item's Q rows go by direct loads
+  // of whole rows into QB bytes of LDS (8 KB per wavefront), and the prologue
+  // reads them from there in the MFMA operand layout.  (Loaded in that layout
   // straight from memory, each lane reads its own row: 32 rows per load
   // instruction, which held the last block of every item up by thousands of
-  // cycles.)
+  // cycles.)  The four-wavefront forms, whose two or three workgroups per CU
+  // cover each other's item edges, keep the per-lane loads.
   constexpr bool QT = WAVES == 8;
   constexpr int QB = QT ? kBM * ROWB : 0;
+  constexpr int QC = ROWB / 16;             // 16-byte chunks per Q row
+  constexpr int QRPL = 1024 / ROWB;         // Q rows per direct load
   constexpr int QLOADS = 32 * ROWB / 1024;  // direct loads of a wavefront's 32 Q rows
-  static_assert(!QT || D == 128, "Q rows through LDS: 16 chunks of 16 bytes per row");
+  static_assert(!QT || q_layout_ok<D>(), "Q LDS layout: direct loads and operand reads");
   static_assert(groups_per_cu<WAVES, OCC>() * (2 * TBV + 2 * TB + QB) <= 160 * 1024,
                 "the resident workgroups' LDS fits a CU");
   static_assert(TBV + 16 * ROWB * (U - 1) + 8 * ROWB + 256 * (DT - 1) < 65536 &&
@@ -420,28 +457,31 @@ fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
       qf[ks] = __builtin_bit_cast(t8_t, t);
     }
   };
-  // Whole-row direct loads (eight-wavefront form) into this wavefront's 8 KB
-  // of LDS: load n fills rows 4n .. 4n+3 of the wavefront's 32, lane l the
-  // 16-byte slot l%16 of row r = 4n + l/16.  Row r's chunk c sits at slot
-  // c ^ (r % 16), so lane l fetches chunk (l%16) ^ (r%16); the operand reads
-  // below (one chunk index of 16 rows per 16 lanes) then meet 16 different
-  // bank groups.  Rows past Nq are clamped to row Nq-1: their results are
-  // never stored.  Only this wavefront touches its area.
+  // Whole-row direct loads into this wavefront's 32 * ROWB bytes of LDS:
+  // load n fills rows QRPL*n .. QRPL*n + QRPL-1 of the wavefront's 32, lane l
+  // the 16-byte slot l % QC of row r = QRPL*n + l / QC.  Row r's chunk c sits
+  // at slot c ^ q_swz(r), so lane l fetches chunk (l % QC) ^ q_swz(r).  The
+  // operand reads below take one chunk index of 16 consecutive rows per 16
+  // lanes; those rows span 16 * ROWB bytes, and q_swz gives the rows that
+  // fall on the same 16-byte bank group of a 256-byte line distinct slots, so
+  // the 16 lanes meet 16 different bank groups.  Rows past Nq are clamped to
+  // row Nq-1: their results are never stored.  Only this wavefront touches
+  // its area.
   char* const q_area = smem + 2 * TBV + 2 * TB + wave * 32 * ROWB;
   auto load_q_lds = [&](const uint16_t* qh, int row0) __attribute__((always_inline)) {
     const int ql = fresh_lane();
-    const int rl = ql >> 4, sl = ql & 15;
+    const int rl = ql / QC, sl = ql % QC;
     if (row0 + 32 <= Nq) {
 #pragma unroll
       for (int n = 0; n < QLOADS; ++n) {
-        const uint32_t voff = (uint32_t)(rl * D + (sl ^ ((4 * n + rl) & 15)) * 8) * 2;
-        lds_dma(qh + (size_t)(row0 + 4 * n) * D, voff, lds_addr(q_area + n * 1024));
+        const uint32_t voff = (uint32_t)(rl * D + (sl ^ q_swz<D>(QRPL * n + rl)) * 8) * 2;
+        lds_dma(qh + (size_t)(row0 + QRPL * n) * D, voff, lds_addr(q_area + n * 1024));
       }
     } else {
 #pragma unroll
       for (int n = 0; n < QLOADS; ++n) {
-        const int r = 4 * n + rl;
-        lds_dma(qh + (size_t)min(row0 + r, Nq - 1) * D + (sl ^ (r & 15)) * 8,
+        const int r = QRPL * n + rl;
+        lds_dma(qh + (size_t)min(row0 + r, Nq - 1) * D + (sl ^ q_swz<D>(r)) * 8,
                 lds_addr(q_area + n * 1024));
       }
     }
@@ -453,7 +493,7 @@ fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
       const int qc = ql & 31, qhf = ql >> 5;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        qf[ks] = *(const t8_t*)(q_area + qc * ROWB + (((2 * ks + qhf) ^ (qc & 15)) * 16));
+        qf[ks] = *(const t8_t*)(q_area + qc * ROWB + (((2 * ks + qhf) ^ q_swz<D>(qc)) * 16));
     }
   };
   // After the sign/zero fix, the fragments pass through an empty asm
