@@ -65,9 +65,12 @@
 // touch every LDS bank once.  V: 128-byte blocks of 4 key rows x 16 dims, so
 // that each 16-lane group of a transposing read (ds_read_b64_tr_b16) reads
 // one contiguous block, the pattern the LDS serves fastest.  Every fragment
-// address is one per-lane base plus a compile-time offset.  The direct loads,
-// and the waits and barriers that order them, are inline assembly, so the
-// compiler does not serialise them against the LDS reads in between.
+// address is one per-lane base plus a compile-time offset.  With eight
+// wavefronts the next item's Q rows take the same route, into 8 KB of LDS per
+// wavefront, and the item's prologue reads them in the operand layout.  The
+// direct loads, and the waits and barriers that order them, are inline
+// assembly, so the compiler does not serialise them against the LDS reads in
+// between.
 //
 // Epilogue.  O and L go straight from registers to global memory through
 // buffer stores whose resource covers only the rows < Nq: rows past the end
