@@ -255,6 +255,20 @@ def test_wide_workgroups_ragged(causal, dtype):
     _cmp(o, lse, O, L, dtype, f"wide {dtype} causal={causal}")
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_wide_workgroups_last_item_mostly_past_the_end(causal):
+    # 64 heads x ceil(770 / 256) = 256 items: in each head's last item only
+    # rows 768 and 769 exist, so seven of its eight wavefronts have no row
+    # inside the sequence (their Q rows are clamped to the last row and their
+    # results dropped by the bounded stores).
+    assert fa2_launch_shape(1, 64, 770, 128)[0] == 256
+    _say(f"wide bf16 B=1 H=64 N=770 d=128 causal={causal}")
+    q, k, v = make_random(1, 64, 770, 128, seed=77 + causal)
+    O, L = attention_fp64(q, k, v, causal=causal)
+    o, lse = _run(q, k, v, causal)
+    _cmp(o, lse, O, L, "bf16", f"wide N=770 causal={causal}")
+
+
 def test_wide_workgroups_cross_lengths():
     # 96 heads x ceil(700 / 256) = 288 items; Nk > Nq with the causal mask
     # aligned bottom-right.
