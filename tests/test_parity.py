@@ -269,6 +269,25 @@ def test_wide_workgroups_last_item_mostly_past_the_end(causal):
     _cmp(o, lse, O, L, "bf16", f"wide N=770 causal={causal}")
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("Nq", [2, 33])
+def test_wide_workgroups_few_queries_many_heads(Nq, causal):
+    # 256 heads of a few queries over 300 keys: 256 items of one query block
+    # each, so the eight-wavefront kernel runs with at most two wavefronts'
+    # rows inside the sequence in any item.
+    B, H, Nk, d = 1, 256, 300, 128
+    assert fa2_launch_shape(B, H, Nq, d)[0] == 256
+    _say(f"wide bf16 few queries B={B} H={H} Nq={Nq} Nk={Nk} causal={causal}")
+    q, k, v = make_random(B, H, Nq, d, seed=5 + Nq + causal, Nk=Nk)
+    O, L = attention_fp64(q, k, v, causal=causal)
+    qd, kd, vd = (t.cuda() for t in (q, k, v))
+    o = torch.empty_like(qd)
+    lse = torch.empty(B, H, Nq, device="cuda")
+    fa2_fwd_cross(qd, kd, vd, o, lse, causal=causal)
+    torch.cuda.synchronize()
+    _cmp(o, lse, O, L, "bf16", f"wide few queries Nq={Nq} causal={causal}")
+
+
 def test_wide_workgroups_cross_lengths():
     # 96 heads x ceil(700 / 256) = 288 items; Nk > Nq with the causal mask
     # aligned bottom-right.
