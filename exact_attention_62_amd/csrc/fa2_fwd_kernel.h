@@ -67,7 +67,9 @@
 // one contiguous block, the pattern the LDS serves fastest.  Every fragment
 // address is one per-lane base plus a compile-time offset.  With eight
 // wavefronts the next item's Q rows take the same route, into 8 KB of LDS per
-// wavefront, and the item's prologue reads them in the operand layout.  The
+// wavefront: they go out in the current item's prologue, once its own rows
+// have been read from there, and the next item's prologue reads them in the
+// operand layout.  The
 // direct loads, and the waits and barriers that order them, are inline
 // assembly, so the compiler does not serialise them against the LDS reads in
 // between.
@@ -738,13 +740,23 @@ fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
   // for blocks j+2 (K) and j+1 (V) issued right after reuse.
   // k_known / v_known: the caller knows that block j+2 (K) / j+1 (V) exists
   // (the loops of block pairs below), so the test is left out of the loop.
+  // Eight-wavefront form: the next item's Q rows go out in the current
+  // item's prologue (the Q area is free once it has been read), so that an
+  // item's last block issues only K/V loads; the first block's wait then
+  // leaves those rows in flight.
+  bool q_early = false;
   auto advance = [&](int j, auto k_known, auto v_known) __attribute__((always_inline)) {
     // At an item's first block the previous item's O and L stores, issued
     // last, need not have completed.  (The eight-wavefront form waits for
     // them too: by then they have had the item edge to complete, and the
     // block loop without the test runs 0-1% faster.)
-    if (kWaves == 4 && j == j_beg && k_item > 0) wait_vmcnt<NSTORE>();
-    else wait_vmcnt<0>();
+    if constexpr (QT) {
+      if (j == j_beg && q_early) wait_vmcnt<QLOADS>();
+      else wait_vmcnt<0>();
+    } else {
+      if (kWaves == 4 && j == j_beg && k_item > 0) wait_vmcnt<NSTORE>();
+      else wait_vmcnt<0>();
+    }
     lds_barrier();
     if (kWaves == 4 && g0 + (j - j_beg) >= prio_next) {  // a quarter of the blocks passed
       prio_next += prio_step;
@@ -757,6 +769,15 @@ fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
     if (decltype(v_known)::value || j + 1 < j_end) issue_v(Vh, (j + 1) * BN, Vb0 + ((gb + j + 1) & 1) * TBV);
   };
 
+  // The item after the current one, and its key range.
+  int next = -1, nbh = 0, nm = 0, nsp = 0, nbeg = 0, nend = 0;
+  auto look_ahead = [&]() __attribute__((always_inline)) {
+    next = logical_of(k_item + 1);
+    if (next >= 0) {
+      decode(next, nbh, nm, nsp);
+      range_of(nm, nsp, nbeg, nend);
+    }
+  };
   // ---- item prologue: wait for Q and K_beg, then S for the first block.
   // Vector memory operations complete in issue order, and V_beg and K_beg+1
   // (and, after the first item, the previous item's O and L stores) were
@@ -789,6 +810,11 @@ fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
       else wait_vmcnt<LOADS_V>();
     }
     lds_barrier();
+    if constexpr (QT) {
+      look_ahead();
+      q_early = next >= 0 && nend > nbeg;
+      if (q_early) issue_item_q(Qg + (size_t)nbh * (size_t)Nq * D, nm * kBM + rgrp * 32);
+    }
 #pragma unroll
     for (int t = 0; t < DT; ++t) o[t] = f32x16_t{};
     m_ref = kNegInf;
@@ -798,32 +824,29 @@ fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
     compute_S(Kb0 + (g0 & 1) * TB, S_cur);
     mx_c = row_max(S_cur);
   };
-  // The item after the current one, and its key range.
-  int next = -1, nbh = 0, nm = 0, nsp = 0, nbeg = 0, nend = 0;
-  auto look_ahead = [&]() __attribute__((always_inline)) {
-    next = logical_of(k_item + 1);
-    if (next >= 0) {
-      decode(next, nbh, nm, nsp);
-      range_of(nm, nsp, nbeg, nend);
-    }
-  };
-  // The next item's Q and first K/V blocks; issued while this item's last
+  // The next item's Q (with eight wavefronts, only its K/V: the Q rows went
+  // out in the prologue) and first K/V blocks; issued while this item's last
   // block is processed (or at once, for an empty item).
   auto prefetch_next = [&]() __attribute__((always_inline)) {
     if (next >= 0 && nend > nbeg) {
       const size_t nqs = (size_t)nbh * (size_t)Nq * D, nks = (size_t)nbh * (size_t)Nk * D;
-      issue_item_start(Qg + nqs, Kg + nks, Vg + nks, nm * kBM + rgrp * 32, nbeg,
-                       nend - nbeg, g0 + (j_end - j_beg));
+      if constexpr (QT)
+        issue_item_kv(Kg + nks, Vg + nks, nbeg, nend - nbeg, g0 + (j_end - j_beg));
+      else
+        issue_item_start(Qg + nqs, Kg + nks, Vg + nks, nm * kBM + rgrp * 32, nbeg,
+                         nend - nbeg, g0 + (j_end - j_beg));
     }
   };
   // The same in two parts, for a wavefront whose rows see none of the item's
-  // last blocks: its Q registers (with eight wavefronts, its Q area of LDS,
-  // read in the prologue) are free from its last computed block on, so its
-  // share of the next item's Q goes out then, and the next item's first K/V
-  // blocks (whose buffers free up only at the item's last block) later.
+  // last blocks: its Q registers are free from its last computed block on, so
+  // its share of the next item's Q goes out then (with eight wavefronts it
+  // went out in the prologue), and the next item's first K/V blocks (whose
+  // buffers free up only at the item's last block) later.
   auto prefetch_next_q = [&]() __attribute__((always_inline)) {
-    if (next >= 0 && nend > nbeg)
-      issue_item_q(Qg + (size_t)nbh * (size_t)Nq * D, nm * kBM + rgrp * 32);
+    if constexpr (!QT) {
+      if (next >= 0 && nend > nbeg)
+        issue_item_q(Qg + (size_t)nbh * (size_t)Nq * D, nm * kBM + rgrp * 32);
+    }
   };
   auto prefetch_next_kv = [&]() __attribute__((always_inline)) {
     if (next >= 0 && nend > nbeg) {
@@ -925,7 +948,7 @@ fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
   }
 
   for (;;) {
-    look_ahead();
+    if constexpr (!QT) look_ahead();
     const int j_unmasked = min(j_mask, j_cend - 1);  // unmasked blocks that have a successor
     f32x16_t SB[KT];
     int j = j_beg;
@@ -967,17 +990,18 @@ fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
       ++j;
     }
     // Last block that this wavefront computes.  At the item's last block both
-    // K buffers and the other V buffer are free, and so are the Q registers
-    // (or Q area): the next item's Q, K_beg, V_beg, K_beg+1 go out there and
-    // overlap that block's softmax, its PV product and the O stores.
+    // K buffers and the other V buffer are free, and so are the Q registers:
+    // the next item's Q (unless it went out in the prologue), K_beg, V_beg and
+    // K_beg+1 go out there and overlap that block's softmax, its PV product
+    // and the O stores.
     advance(j, std::false_type{}, std::false_type{});
     if (j + 1 == j_end) prefetch_next();
     // Always the masked form: one copy of the code, and for an unmasked block
     // the threshold test hides nothing.
     consume(std::true_type{}, j, S_cur, [] {}, [] {});
     // Blocks hidden from all of this wavefront's rows: loads and barriers.
-    // Its next Q rows go out after the first of them (its Q registers or Q
-    // area are free; the item's last block then issues less at once).
+    // Its next Q rows go out after the first of them (its Q registers are
+    // free; the item's last block then issues less at once).
     if (++j < j_end) {
       advance(j, std::false_type{}, std::false_type{});
       prefetch_next_q();
