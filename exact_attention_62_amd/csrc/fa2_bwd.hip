@@ -618,7 +618,7 @@ fa2_bwd_dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ 
   auto buf = [&](int j) { return smem + (j & 1) * (2 * TILE); };
   // Blocks wholly before Nk are staged with scalar bases; only a ragged last
   // block needs clamped per-lane addresses.
-  auto stage = [&](int j) {
+  auto stage = [&](int j) __attribute__((always_inline)) {
     if ((j + 1) * kStep <= Nk) {
       stage_tile<D, kStep, false>(Kh, j * kStep, Nk, buf(j), wave);
       stage_tile<D, kStep, false>(Vh, j * kStep, Nk, buf(j) + TILE, wave);
@@ -627,14 +627,20 @@ fa2_bwd_dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ 
       stage_tile<D, kStep, true>(Vh, j * kStep, Nk, buf(j) + TILE, wave);
     }
   };
-  if (j_end > 0) stage(0);
-  for (int j = 0; j < j_end; ++j) {
+  // Blocks before j_clean need no mask for this wavefront: all their keys
+  // precede Nk and every query of the wavefront sees them.  Walking up, they
+  // come first, and a loop of their own runs them without any test, so that
+  // each of their steps is one basic block.
+  const int seen = q0 + off + 1;  // keys the wavefront's first query sees
+  const int j_clean =
+      min(j_end, min(Nk / kStep, CAUSAL ? (seen <= 0 ? 0 : seen / kStep) : Nk / kStep));
+  auto step = [&](int j, auto masked_tag) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
     wait_vmcnt<0>();
     lds_barrier();
     if (j + 1 < j_end) stage(j + 1);
     const char* kt_ = buf(j);
     const char* vt = buf(j) + TILE;
-    const bool clean = (j + 1) * kStep <= Nk && (!CAUSAL || (j + 1) * kStep - 1 <= q0 + off);
     t8_t sb[4];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
@@ -644,18 +650,16 @@ fa2_bwd_dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ 
         S = mfma32x32x16(row_frag<T, D>(kt_, lb, 32 * kt, ks), qf[ks], S);
         dP = mfma32x32x16(row_frag<T, D>(vt, lb, 32 * kt, ks), df[ks], dP);
       }
-      // This lane's query is qrow; accumulator r holds key
-      // j*64 + 32*kt + cr + 4*half with cr = 8*(r/4) + r%4 (a constant),
-      // visible when cr <= th (key <= query + off, key < Nk).  Blocks whose keys
-      // every query of the wavefront sees, before Nk, skip the test (a branch
-      // that is uniform for the wavefront); a query that sees no key
-      // (L = -inf) has every entry masked.
-      const int kb0 = j * kStep + 32 * kt + 4 * half;
-      int th = Nk - 1 - kb0;
-      if (CAUSAL) th = min(th, qrow + off - kb0);
 #pragma unroll
       for (int r = 0; r < 16; ++r) S[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], c, -l2));
-      if (!clean) {
+      if constexpr (MASKED) {
+        // This lane's query is qrow; accumulator r holds key
+        // j*64 + 32*kt + cr + 4*half with cr = 8*(r/4) + r%4 (a constant),
+        // visible when cr <= th (key <= query + off, key < Nk); a query that
+        // sees no key (L = -inf) has every entry masked.
+        const int kb0 = j * kStep + 32 * kt + 4 * half;
+        int th = Nk - 1 - kb0;
+        if (CAUSAL) th = min(th, qrow + off - kb0);
 #pragma unroll
         for (int r = 0; r < 16; ++r) S[r] = 8 * (r / 4) + (r % 4) > th ? 0.f : S[r];
       }
@@ -667,7 +671,11 @@ fa2_bwd_dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ 
 #pragma unroll
       for (int t = 0; t < DT; ++t)
         dq[t] = mfma32x32x16(tr_frag<T, D>(kt_, lb, u, t), sb[u], dq[t]);
-  }
+  };
+  if (j_end > 0) stage(0);
+  int j = 0;
+  for (; j < j_clean; ++j) step(j, std::false_type{});
+  for (; j < j_end; ++j) step(j, std::true_type{});
   store_rows<T, D>(dq, scale, dQg + qslice, q0, Nq, lane);
 }
 
