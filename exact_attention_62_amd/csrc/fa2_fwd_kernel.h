@@ -1062,8 +1062,12 @@ hipError_t dispatch_fwd_mfma(const FwdArgs& a) {
     // d = 32 fits 168 VGPRs: three wavefronts per SIMD.
     FA2_CASE(32, 0, 3)
     FA2_CASE(32, 1, 3)
-    FA2_CASE(64, 0, 2)
-    FA2_CASE(64, 1, 2)
+    // d = 64 without splits: 153-155 VGPRs, so three wavefronts per SIMD too;
+    // the split form needs more and keeps two.
+  case (64 * 2 + 0) * 2 + 0: return launch<T, 64, false, false, 4, 3>(a);
+  case (64 * 2 + 0) * 2 + 1: return launch<T, 64, false, true, 4, 2>(a);
+  case (64 * 2 + 1) * 2 + 0: return launch<T, 64, true, false, 4, 3>(a);
+  case (64 * 2 + 1) * 2 + 1: return launch<T, 64, true, true, 4, 2>(a);
     FA2_CASE(96, 0, 2)
     FA2_CASE(96, 1, 2)
 #undef FA2_CASE
