@@ -543,11 +543,15 @@ def main(argv=None) -> int:
         waves = 4 if splits is not None else block_m // 32
         cus = torch.cuda.get_device_properties(0).multi_processor_count
         items = B * H * ((Nq + block_m - 1) // block_m)
-        # The same rule as the library's dispatch: three per SIMD for d = 32 and,
-        # without splits, d = 64 (168 VGPRs), one for d = 256 with splits or on
-        # small grids, two otherwise.
-        occ = (3 if d == 32 or (d == 64 and splits is None)
-               else (1 if d == 256 and (splits is not None or items < 2 * cus) else 2))
+        # The same rule as the library's dispatch: without splits four per SIMD
+        # for d = 32 (128 VGPRs) and three for d = 64 (168); with splits three
+        # for d = 32; one for d = 256 with splits or on small grids; two otherwise.
+        if d == 32:
+            occ = 4 if splits is None else 3
+        elif d == 64 and splits is None:
+            occ = 3
+        else:
+            occ = 1 if d == 256 and (splits is not None or items < 2 * cus) else 2
         kname = (f"fa2_fwd_kernel<{KERNEL_TYPE[dtype]}, {d}, {c}, "
                  f"{'true' if splits is not None else 'false'}, {waves}, {occ}>")
     if splits is not None:

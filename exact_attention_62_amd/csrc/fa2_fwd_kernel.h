@@ -1022,7 +1022,7 @@ fa2_fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
 }
 
 // OCC: wavefronts per SIMD that the kernel's registers allow (1: up to 512
-// VGPRs, 2: up to 256, 3: up to 168).
+// VGPRs, 2: up to 256, 3: up to 168, 4: up to 128).
 template <typename T, int D, bool CAUSAL, bool SPLIT, int WAVES, int OCC>
 hipError_t launch(const FwdArgs& a) {
   if (a.block_m != 32 * WAVES) return hipErrorInvalidValue;  // num_m_block counts other blocks
@@ -1059,9 +1059,12 @@ hipError_t dispatch_fwd_mfma(const FwdArgs& a) {
 #define FA2_CASE(D, C, OCC)                                                  \
   case (D * 2 + C) * 2 + 0: return launch<T, D, (bool)C, false, 4, OCC>(a); \
   case (D * 2 + C) * 2 + 1: return launch<T, D, (bool)C, true, 4, OCC>(a);
-    // d = 32 fits 168 VGPRs: three wavefronts per SIMD.
-    FA2_CASE(32, 0, 3)
-    FA2_CASE(32, 1, 3)
+    // d = 32 fits 128 VGPRs without splits (four wavefronts per SIMD) and
+    // 168 with them (three).
+  case (32 * 2 + 0) * 2 + 0: return launch<T, 32, false, false, 4, 4>(a);
+  case (32 * 2 + 0) * 2 + 1: return launch<T, 32, false, true, 4, 3>(a);
+  case (32 * 2 + 1) * 2 + 0: return launch<T, 32, true, false, 4, 4>(a);
+  case (32 * 2 + 1) * 2 + 1: return launch<T, 32, true, true, 4, 3>(a);
     // d = 64 without splits: 153-155 VGPRs, so three wavefronts per SIMD too;
     // the split form needs more and keeps two.
   case (64 * 2 + 0) * 2 + 0: return launch<T, 64, false, false, 4, 3>(a);
